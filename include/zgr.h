@@ -1,0 +1,231 @@
+/*
+ * zgr — filter-first constrained beam search over semantic IDs on MI355X.
+ *
+ * C ABI of the library.  The operations follow the ZeroGR description
+ * ("ZeroGR: Filtering-First Constrained Decoding for Generative
+ * Recommendation", paper-daily page):
+ *   - "overall pipeline": an offline filter index, an online per-step engine
+ *     and a rebuild on every catalog/model update; each step takes every
+ *     beam's hidden vector, reads its legal tokens from the index, scores
+ *     them, applies log-softmax over the legal tokens only, adds the result
+ *     to the beam's cumulative log-prob and picks the next beams.
+ *   - "why slice the index per step": one table per step; a row is a prefix
+ *     of length t-1 and records its legal next tokens and their rows in the
+ *     next table; dense tables for steps with many legal tokens (columns in
+ *     full-projection order), sparse tables for late steps where an entry's
+ *     position is its next row and the last step stores no item ids.
+ *   - "why fewer scores is not faster": fixed padded candidate slots per beam
+ *     (the per-step maximum legal count; a dense step uses the whole
+ *     codebook), empty slots at minus infinity, weight rows read in place;
+ *     per step, full or selective projection is chosen by timing both on
+ *     warm-up traffic before serving and then frozen.
+ *
+ * Conventions
+ *   - Every call returns a status (ZGR_OK = 0); no error crosses the ABI any
+ *     other way.  zgr_last_error() gives a detail string for the calling
+ *     thread's last failure.
+ *   - Argument checks run before any HIP call, so bad arguments are reported
+ *     without touching the device.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HBM
+ *     allocations of the current HIP device (for example torch CUDA tensors).
+ *     The caller owns every pointer it passes and keeps it alive for the
+ *     call (for asynchronous calls, until the stream has passed the work).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Step work is enqueued asynchronously on it.
+ *   - The library owns zgr_index and zgr_plan objects and their HBM; only
+ *     zgr_index_free / zgr_plan_free release them.  An index is immutable
+ *     after upload and may be read by several plans; a plan owns scratch
+ *     buffers and must be used from one stream at a time.
+ *   - Tokens are int32 in [0, V); rows are int32 (-1 = dead beam); scores are
+ *     float32 (-inf = no candidate).
+ */
+#ifndef ZGR_H
+#define ZGR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------------------------- */
+#define ZGR_OK 0
+#define ZGR_E_ARG 1          /* null pointer, out-of-range scalar argument */
+#define ZGR_E_DUP_SID 2      /* two catalog rows share one SID */
+#define ZGR_E_TOKEN_RANGE 3  /* a catalog token outside [0, V) */
+#define ZGR_E_SHAPE 4        /* unsupported size combination (d, K, L*bits, ...) */
+#define ZGR_E_NOMEM 5        /* host or device allocation failed */
+#define ZGR_E_HIP 6          /* a HIP runtime call failed */
+#define ZGR_E_STATE 7        /* object used out of order, or a stale plan */
+#define ZGR_E_CALLBACK 8     /* the hidden-vector callback returned non-zero */
+#define ZGR_E_DEVICE 9       /* a kernel saw an invalid beam row (reported at sync) */
+
+/* ---- enums ----------------------------------------------------------------------------- */
+#define ZGR_F32 0   /* float32 weights and hidden vectors */
+#define ZGR_BF16 1  /* bfloat16 storage, float32 accumulation and log-softmax */
+#define ZGR_F16 2   /* IEEE half storage, float32 accumulation and log-softmax */
+
+#define ZGR_FMT_AUTO 0    /* smaller of the two encodings */
+#define ZGR_FMT_DENSE 1   /* bitmap per row over the codebook, slot = token */
+#define ZGR_FMT_SPARSE 2  /* sorted legal tokens per row, slot = position */
+
+#define ZGR_PROJ_AUTO 0       /* decided by warm-up timing (or a cost model without warm-up) */
+#define ZGR_PROJ_FULL 1       /* MFMA projection over the whole codebook, then legal columns */
+#define ZGR_PROJ_SELECTIVE 2  /* score only the legal tokens, weight rows read in place */
+
+typedef struct zgr_index zgr_index;
+typedef struct zgr_plan zgr_plan;
+
+/* Static description of one step's table. */
+typedef struct {
+  int64_t rows;    /* R_t: distinct prefixes of length t-1 */
+  int64_t nnz;     /* legal (row, token) pairs = rows of table t+1 (N at t = L) */
+  int32_t fmt;     /* ZGR_FMT_DENSE or ZGR_FMT_SPARSE */
+  int32_t stride;  /* S_t: slots per beam (max legal count of a row; V when dense) */
+  int64_t bytes;   /* device bytes of this table */
+  int32_t max_legal;  /* largest legal count of any row */
+  int32_t reserved;
+} zgr_step_stats;
+
+/* Text of a status code (static storage). */
+const char* zgr_status_str(int32_t status);
+
+/* Copy the calling thread's last error detail into buf (NUL-terminated,
+ * truncated to n bytes).  Returns the status of that failure. */
+int32_t zgr_last_error(char* buf, size_t n);
+
+/* ---- index ---------------------------------------------------------------------------- */
+
+/*
+ * Build the per-step filter index of a catalog on the host (no HIP call).
+ *   sids  host int32 [N][L], row i = SID of catalog row i, tokens in [0, V).
+ *   fmt   host int32 [L] per-step ZGR_FMT_* or NULL (all AUTO).
+ *   rank_of_input  host int64 [N] or NULL: receives the item id of each
+ *         catalog row.  An item id is the lexicographic rank of the SID among
+ *         all catalog SIDs, i.e. its position in the last table (the last
+ *         step stores no ids: the position is the id).
+ * Rows of table t are the distinct length-(t-1) prefixes in lexicographic
+ * order; a legal (row, token) entry's next row is its lexicographic rank among
+ * distinct length-t prefixes.  1 <= L <= 8, 2 <= V <= 65536, N < 2^31,
+ * ceil(log2 V) * L <= 64.
+ * Errors: ZGR_E_ARG, ZGR_E_TOKEN_RANGE, ZGR_E_DUP_SID, ZGR_E_SHAPE, ZGR_E_NOMEM.
+ */
+int32_t zgr_index_build_host(const int32_t* sids, int64_t N, int32_t L, int32_t V,
+                             const int32_t* fmt, int64_t* rank_of_input, zgr_index** out);
+
+/* Copy a host-built index to HBM of the current device (synchronous on
+ * return).  Errors: ZGR_E_ARG, ZGR_E_STATE (already on device), ZGR_E_NOMEM,
+ * ZGR_E_HIP. */
+int32_t zgr_index_to_device(zgr_index* idx, void* stream);
+
+/* zgr_index_build_host followed by zgr_index_to_device. */
+int32_t zgr_index_upload(const int32_t* sids, int64_t N, int32_t L, int32_t V, const int32_t* fmt,
+                         void* stream, zgr_index** out, int64_t* rank_of_input);
+
+/* Per-step statistics, t in 1..L.  Errors: ZGR_E_ARG. */
+int32_t zgr_index_stats(const zgr_index* idx, int32_t t, zgr_step_stats* out);
+
+/* Host copies of table t (valid while idx lives): row_ptr int32 [rows+1]
+ * (CSR offsets; also the dense table's base), tok uint16 [nnz] sorted per
+ * row, bits uint32 [rows][ceil(V/32)] (NULL for sparse tables).  Any output
+ * pointer may be NULL.  Errors: ZGR_E_ARG. */
+int32_t zgr_index_host_table(const zgr_index* idx, int32_t t, const int32_t** row_ptr,
+                             const uint16_t** tok, const uint32_t** bits);
+
+/* Index shape: L, V, N (any output may be NULL). */
+int32_t zgr_index_shape(const zgr_index* idx, int32_t* L, int32_t* V, int64_t* N);
+
+void zgr_index_free(zgr_index* idx);
+
+/* ---- plan ----------------------------------------------------------------------------- */
+
+/*
+ * Hidden-vector source (the model; its time is not part of a step).  Called
+ * once per decode step with the B*k_in beams in flight: prefix_dev is device
+ * int32 [B*k_in][prefix_ld] holding each beam's t-1 tokens so far (beam
+ * b = request * k_in + rank), hidden_dev is device [B*k_in][d] of the plan's
+ * dtype to be filled.  Work must be enqueued on `stream` (or completed before
+ * returning).  Non-zero return aborts the decode with ZGR_E_CALLBACK.
+ */
+typedef int32_t (*zgr_hidden_fn)(void* user, int32_t t, int32_t B, int32_t k_in,
+                                 const int32_t* prefix_dev, int32_t prefix_ld, void* hidden_dev,
+                                 void* stream);
+
+/*
+ * Create a plan for batches of B requests, beam width K, hidden size d and
+ * the given weights, and freeze each step's projection ("why fewer scores is
+ * not faster": timed on warm-up traffic before serving, kept until the next
+ * update).
+ *   W_dev   L device pointers, W_t row-major [V][d] of dtype (kept, not copied;
+ *           must outlive the plan).
+ *   force   host int32 [L] of ZGR_PROJ_* or NULL (all AUTO).
+ *   n_warmup  warm-up decodes; for every AUTO step both projections are timed
+ *           with HIP events on each, and the one with the lower median wins
+ *           (an exact tie picks selective).  With n_warmup = 0 or no callback,
+ *           AUTO steps use a bandwidth/MFMA cost model instead.
+ *   hidden_fn, user  source of warm-up hidden vectors (may be NULL if no timing).
+ * Limits: d % 64 == 0, d <= 4096; 1 <= K <= 1024; B >= 1; B*K < 2^31.
+ * Errors: ZGR_E_ARG, ZGR_E_SHAPE, ZGR_E_STATE (index not on device), ZGR_E_NOMEM,
+ * ZGR_E_HIP, ZGR_E_CALLBACK.
+ */
+int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t dtype, int32_t d,
+                        int32_t B, int32_t K, zgr_hidden_fn hidden_fn, void* user,
+                        int32_t n_warmup, const int32_t* force, void* stream, zgr_plan** out);
+
+/* The frozen choice of step t and the warm-up medians in microseconds
+ * (negative when that option was not timed).  Errors: ZGR_E_ARG. */
+int32_t zgr_plan_choice(const zgr_plan* plan, int32_t t, int32_t* proj, float* us_full,
+                        float* us_sel);
+
+/* Re-freeze step t's projection (ZGR_PROJ_FULL or ZGR_PROJ_SELECTIVE), e.g. to
+ * resume a plan exported by zgr_plan_choice without a new warm-up. */
+int32_t zgr_plan_set_choice(zgr_plan* plan, int32_t t, int32_t proj);
+
+void zgr_plan_free(zgr_plan* plan);
+
+/*
+ * One decode step t (1..L) for the plan's B requests, asynchronous on stream.
+ *   hidden_dev  device [B*k_in][d] (plan dtype): beam b = request*k_in + rank.
+ *   row_in      device int32 [B*k_in]: the beam's row in table t (-1 = dead).
+ *   cum_in      device float [B*k_in]: cumulative log-prob (ignored when dead).
+ *   k_in        beams per request coming in (1 at t = 1, usually K after).
+ * Outputs, device, [B*K], per request sorted best first:
+ *   parent_out  int32: input beam index b of the chosen candidate (-1 = none)
+ *   token_out   int32: the chosen token (-1 = none)
+ *   row_out     int32: its row in table t+1; at t = L the item id (-1 = none)
+ *   cum_out     float: cum_in[parent] + log-softmax of the token over the
+ *               parent's legal tokens (-inf = none)
+ *   slot_dbg    NULL or device float [B*k_in][S_t]: every slot's log-prob,
+ *               -inf for empty slots and dead beams (S_t from zgr_index_stats).
+ * Ranking: cum_out descending, then parent ascending, then token ascending.
+ * Fewer than K candidates in a request: the tail is filled with "none".
+ * An out-of-range row sets a device flag reported by zgr_plan_status.
+ * Errors (before any work is enqueued): ZGR_E_ARG, ZGR_E_SHAPE, ZGR_E_HIP.
+ */
+int32_t zgr_step(zgr_plan* plan, int32_t t, const void* hidden_dev, const int32_t* row_in,
+                 const float* cum_in, int32_t k_in, int32_t* parent_out, int32_t* token_out,
+                 int32_t* row_out, float* cum_out, float* slot_dbg, void* stream);
+
+/*
+ * Full decode of the plan's B requests: L steps, each preceded by one
+ * hidden_fn call, starting from one empty-prefix beam per request with
+ * cumulative log-prob 0.  Outputs (device), per request best first:
+ *   item_out  int64 [B][top_k] item ids (-1 = none)
+ *   sid_out   int32 [B][top_k][L] or NULL
+ *   score_out float [B][top_k] or NULL
+ * 1 <= top_k <= K.  Synchronises the stream before returning and reports
+ * device-side flags.  Errors: ZGR_E_ARG, ZGR_E_CALLBACK, ZGR_E_HIP, ZGR_E_DEVICE.
+ */
+int32_t zgr_decode(zgr_plan* plan, zgr_hidden_fn hidden_fn, void* user, int32_t top_k,
+                   int64_t* item_out, int32_t* sid_out, float* score_out, void* stream);
+
+/* Synchronise stream and report (then clear) the plan's device-side error
+ * flag: ZGR_OK or ZGR_E_DEVICE; ZGR_E_HIP if the sync fails. */
+int32_t zgr_plan_status(zgr_plan* plan, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZGR_H */

@@ -1,0 +1,386 @@
+"""Python binding of libzgr (filter-first constrained beam search on MI355X).
+
+Argument marshalling only: every step of the search runs in the HIP kernels
+of ``libzgr.so`` behind the C ABI declared in ``include/zgr.h``.  Device
+buffers are passed as torch tensors on the current HIP device (their
+``data_ptr()``), host buffers as numpy arrays, streams as torch streams (or
+raw ``hipStream_t`` integers).  There is no fallback: if the library is
+missing, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Callable, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzgr.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "zgr.h")
+
+ZGR_OK, ZGR_E_ARG, ZGR_E_DUP_SID, ZGR_E_TOKEN_RANGE, ZGR_E_SHAPE = 0, 1, 2, 3, 4
+ZGR_E_NOMEM, ZGR_E_HIP, ZGR_E_STATE, ZGR_E_CALLBACK, ZGR_E_DEVICE = 5, 6, 7, 8, 9
+ZGR_F32, ZGR_BF16, ZGR_F16 = 0, 1, 2
+ZGR_FMT_AUTO, ZGR_FMT_DENSE, ZGR_FMT_SPARSE = 0, 1, 2
+ZGR_PROJ_AUTO, ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE = 0, 1, 2
+
+DTYPE_CODES = {"f32": ZGR_F32, "bf16": ZGR_BF16, "f16": ZGR_F16}
+FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR_FMT_SPARSE}
+PROJ_CODES = {None: ZGR_PROJ_AUTO, "auto": ZGR_PROJ_AUTO, "full": ZGR_PROJ_FULL,
+              "selective": ZGR_PROJ_SELECTIVE}
+
+_P = ctypes.c_void_p
+_I32, _I64 = ctypes.c_int32, ctypes.c_int64
+
+HIDDEN_FN = ctypes.CFUNCTYPE(ctypes.c_int32, _P, _I32, _I32, _I32, _P, _I32, _P, _P)
+
+
+class StepStats(ctypes.Structure):
+    _fields_ = [("rows", _I64), ("nnz", _I64), ("fmt", _I32), ("stride", _I32), ("bytes", _I64),
+                ("max_legal", _I32), ("reserved", _I32)]
+
+
+class ZgrError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{status_str(status)} ({status}): {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libzgr.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc, gfx950); there is no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "zgr_status_str": (ctypes.c_char_p, [_I32]),
+            "zgr_last_error": (_I32, [ctypes.c_char_p, ctypes.c_size_t]),
+            "zgr_index_build_host": (_I32, [_P, _I64, _I32, _I32, _P, _P, ctypes.POINTER(_P)]),
+            "zgr_index_to_device": (_I32, [_P, _P]),
+            "zgr_index_upload": (_I32, [_P, _I64, _I32, _I32, _P, _P, ctypes.POINTER(_P), _P]),
+            "zgr_index_stats": (_I32, [_P, _I32, ctypes.POINTER(StepStats)]),
+            "zgr_index_host_table": (_I32, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                            ctypes.POINTER(_P)]),
+            "zgr_index_shape": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                       ctypes.POINTER(_I64)]),
+            "zgr_index_free": (None, [_P]),
+            "zgr_plan_warmup": (_I32, [_P, _P, _I32, _I32, _I32, _I32, HIDDEN_FN, _P, _I32, _P, _P,
+                                       ctypes.POINTER(_P)]),
+            "zgr_plan_choice": (_I32, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_float),
+                                       ctypes.POINTER(ctypes.c_float)]),
+            "zgr_plan_set_choice": (_I32, [_P, _I32, _I32]),
+            "zgr_plan_free": (None, [_P]),
+            "zgr_step": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P]),
+            "zgr_decode": (_I32, [_P, HIDDEN_FN, _P, _I32, _P, _P, _P, _P]),
+            "zgr_plan_status": (_I32, [_P, _P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> List[str]:
+    """Names of the functions that include/zgr.h declares."""
+    import re
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(zgr_[a-z0-9_]+)\s*\(", text)) - {"zgr_hidden_fn"})
+
+
+def status_str(status: int) -> str:
+    return lib().zgr_status_str(status).decode()
+
+
+def last_error() -> str:
+    buf = ctypes.create_string_buffer(1024)
+    lib().zgr_last_error(buf, len(buf))
+    return buf.value.decode()
+
+
+def _check(status: int):
+    if status != ZGR_OK:
+        raise ZgrError(status, last_error())
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+# --------------------------------------------------------------------------- index
+
+class Index:
+    """Owner of a zgr_index handle."""
+
+    def __init__(self, handle: ctypes.c_void_p):
+        self._h = handle
+
+    @property
+    def handle(self):
+        return self._h
+
+    def free(self):
+        if self._h is not None and self._h.value:
+            lib().zgr_index_free(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def shape(self):
+        return zgr_index_shape(self)
+
+    def stats(self, t: int) -> dict:
+        return zgr_index_stats(self, t)
+
+    def host_table(self, t: int):
+        return zgr_index_host_table(self, t)
+
+
+def _fmt_array(fmt, L):
+    if fmt is None:
+        return None
+    a = np.asarray([FMT_CODES[f] if not isinstance(f, (int, np.integer)) else int(f) for f in fmt],
+                   dtype=np.int32)
+    if a.shape != (L,):
+        raise ValueError("fmt must have L entries")
+    return a
+
+
+def zgr_index_build_host(sids: np.ndarray, V: int, fmt=None, want_rank: bool = True):
+    """Host-only build.  Returns (Index, rank_of_input int64 [N] or None)."""
+    sids = np.ascontiguousarray(sids, dtype=np.int32)
+    N, L = sids.shape
+    f = _fmt_array(fmt, L)
+    rank = np.empty(N, dtype=np.int64) if want_rank else None
+    h = ctypes.c_void_p()
+    _check(lib().zgr_index_build_host(sids.ctypes.data, N, L, V,
+                                      None if f is None else f.ctypes.data,
+                                      None if rank is None else rank.ctypes.data, ctypes.byref(h)))
+    return Index(h), rank
+
+
+def zgr_index_to_device(index: Index, stream=None):
+    _check(lib().zgr_index_to_device(index.handle, _stream_ptr(stream)))
+
+
+def zgr_index_upload(sids: np.ndarray, V: int, fmt=None, stream=None, want_rank: bool = True):
+    """Build on the host and copy to HBM.  Returns (Index, rank_of_input)."""
+    sids = np.ascontiguousarray(sids, dtype=np.int32)
+    N, L = sids.shape
+    f = _fmt_array(fmt, L)
+    rank = np.empty(N, dtype=np.int64) if want_rank else None
+    h = ctypes.c_void_p()
+    _check(lib().zgr_index_upload(sids.ctypes.data, N, L, V, None if f is None else f.ctypes.data,
+                                  _stream_ptr(stream), ctypes.byref(h),
+                                  None if rank is None else rank.ctypes.data))
+    return Index(h), rank
+
+
+def zgr_index_stats(index: Index, t: int) -> dict:
+    st = StepStats()
+    _check(lib().zgr_index_stats(index.handle, t, ctypes.byref(st)))
+    return {k: getattr(st, k) for k, _ in StepStats._fields_ if k != "reserved"}
+
+
+def zgr_index_shape(index: Index):
+    L, V, N = _I32(), _I32(), _I64()
+    _check(lib().zgr_index_shape(index.handle, ctypes.byref(L), ctypes.byref(V), ctypes.byref(N)))
+    return L.value, V.value, N.value
+
+
+def zgr_index_host_table(index: Index, t: int):
+    """Copies of table t: (row_ptr int32 [rows+1], tok uint16 [nnz], bits uint32 [rows, words] or None)."""
+    rp, tk, bt = _P(), _P(), _P()
+    _check(lib().zgr_index_host_table(index.handle, t, ctypes.byref(rp), ctypes.byref(tk),
+                                      ctypes.byref(bt)))
+    st = zgr_index_stats(index, t)
+    _, V, _ = zgr_index_shape(index)
+    rows, nnz = st["rows"], st["nnz"]
+    row_ptr = np.ctypeslib.as_array(ctypes.cast(rp, ctypes.POINTER(ctypes.c_int32)), (rows + 1,)).copy()
+    tok = (np.ctypeslib.as_array(ctypes.cast(tk, ctypes.POINTER(ctypes.c_uint16)), (nnz,)).copy()
+           if nnz else np.zeros(0, np.uint16))
+    bits = None
+    if bt.value:
+        words = (V + 31) // 32
+        bits = np.ctypeslib.as_array(ctypes.cast(bt, ctypes.POINTER(ctypes.c_uint32)),
+                                     (rows, words)).copy()
+    return row_ptr, tok, bits
+
+
+def zgr_index_free(index: Index):
+    index.free()
+
+
+# --------------------------------------------------------------------------- plan
+
+HiddenCallable = Callable[[int, int, int, int, int, int, int], int]
+
+
+def make_hidden_fn(fn: HiddenCallable):
+    """Wrap fn(t, B, k_in, prefix_ptr, prefix_ld, hidden_ptr, stream_ptr) -> int
+    as a C callback.  Keep the returned object alive while it may be called."""
+    def tramp(user, t, B, k_in, prefix_ptr, prefix_ld, hidden_ptr, stream_ptr):
+        try:
+            return int(fn(t, B, k_in, prefix_ptr or 0, prefix_ld, hidden_ptr or 0, stream_ptr or 0))
+        except Exception:  # noqa: BLE001 - report as a callback failure
+            import traceback
+            traceback.print_exc()
+            return 1
+    return HIDDEN_FN(tramp)
+
+
+class Plan:
+    """Owner of a zgr_plan handle (keeps the weights and callback alive)."""
+
+    def __init__(self, handle, index: Index, W, L: int):
+        self._h = handle
+        self.index = index
+        self.W = W
+        self.L = L
+        self._keep = []
+
+    @property
+    def handle(self):
+        return self._h
+
+    def free(self):
+        if self._h is not None and self._h.value:
+            lib().zgr_plan_free(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:  # noqa: BLE001
+            pass
+
+    def choice(self, t: int):
+        return zgr_plan_choice(self, t)
+
+
+def zgr_plan_warmup(index: Index, W: Sequence, dtype: str, d: int, B: int, K: int,
+                    hidden_fn: Optional[HiddenCallable] = None, n_warmup: int = 0, force=None,
+                    stream=None) -> Plan:
+    """W: L device tensors [V, d] of dtype (kept alive by the plan).
+    force: None or L entries of 'auto' / 'full' / 'selective' (or ZGR_PROJ_* ints)."""
+    L = len(W)
+    ptrs = (ctypes.c_void_p * L)(*[w.data_ptr() for w in W])
+    f = None
+    if force is not None:
+        f = np.asarray([PROJ_CODES[x] if not isinstance(x, (int, np.integer)) else int(x)
+                        for x in force], dtype=np.int32)
+    cb = make_hidden_fn(hidden_fn) if hidden_fn is not None else HIDDEN_FN()
+    h = ctypes.c_void_p()
+    _check(lib().zgr_plan_warmup(index.handle, ctypes.cast(ptrs, _P), DTYPE_CODES.get(dtype, dtype),
+                                 d, B, K, cb, None, n_warmup, None if f is None else f.ctypes.data,
+                                 _stream_ptr(stream), ctypes.byref(h)))
+    p = Plan(h, index, list(W), L)
+    p._keep.append(cb)
+    return p
+
+
+def zgr_plan_choice(plan: Plan, t: int):
+    proj, uf, us = _I32(), ctypes.c_float(), ctypes.c_float()
+    _check(lib().zgr_plan_choice(plan.handle, t, ctypes.byref(proj), ctypes.byref(uf), ctypes.byref(us)))
+    return proj.value, uf.value, us.value
+
+
+def zgr_plan_set_choice(plan: Plan, t: int, proj):
+    code = PROJ_CODES[proj] if isinstance(proj, str) else int(proj)
+    _check(lib().zgr_plan_set_choice(plan.handle, t, code))
+
+
+def zgr_plan_free(plan: Plan):
+    plan.free()
+
+
+def zgr_step(plan: Plan, t: int, hidden, row_in, cum_in, k_in: int, parent_out, token_out,
+             row_out, cum_out, slot_dbg=None, stream=None):
+    """Enqueue one step (all buffers are device tensors; see include/zgr.h)."""
+    _check(lib().zgr_step(plan.handle, t, _dptr(hidden), _dptr(row_in), _dptr(cum_in), k_in,
+                          _dptr(parent_out), _dptr(token_out), _dptr(row_out), _dptr(cum_out),
+                          _dptr(slot_dbg), _stream_ptr(stream)))
+
+
+def zgr_decode(plan: Plan, hidden_fn: HiddenCallable, top_k: int, item_out, sid_out=None,
+               score_out=None, stream=None):
+    cb = make_hidden_fn(hidden_fn)
+    _check(lib().zgr_decode(plan.handle, cb, None, top_k, _dptr(item_out), _dptr(sid_out),
+                            _dptr(score_out), _stream_ptr(stream)))
+
+
+def zgr_plan_status(plan: Plan, stream=None):
+    _check(lib().zgr_plan_status(plan.handle, _stream_ptr(stream)))
+
+
+# --------------------------------------------------------------------------- HIP memcpy helper
+
+_hip = None
+
+
+def hip_runtime() -> ctypes.CDLL:
+    """libamdhip64 for raw-pointer copies inside hidden-vector callbacks."""
+    global _hip
+    if _hip is None:
+        for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                h = ctypes.CDLL(name)
+                break
+            except OSError:
+                h = None
+        if h is None:
+            raise ImportError("libamdhip64.so not found")
+        h.hipMemcpyAsync.restype = ctypes.c_int
+        h.hipMemcpyAsync.argtypes = [_P, _P, ctypes.c_size_t, ctypes.c_int, _P]
+        h.hipStreamSynchronize.restype = ctypes.c_int
+        h.hipStreamSynchronize.argtypes = [_P]
+        _hip = h
+    return _hip
+
+
+HIP_H2D, HIP_D2H, HIP_D2D = 1, 2, 3
+
+
+def copy_to_device(dst_ptr: int, src: np.ndarray, stream_ptr: int):
+    src = np.ascontiguousarray(src)
+    h = hip_runtime()
+    if h.hipMemcpyAsync(dst_ptr, src.ctypes.data, src.nbytes, HIP_H2D, stream_ptr) != 0:
+        raise RuntimeError("hipMemcpyAsync H2D failed")
+    if h.hipStreamSynchronize(stream_ptr) != 0:
+        raise RuntimeError("hipStreamSynchronize failed")
+
+
+def copy_to_host(dst: np.ndarray, src_ptr: int, stream_ptr: int):
+    h = hip_runtime()
+    if h.hipStreamSynchronize(stream_ptr) != 0:
+        raise RuntimeError("hipStreamSynchronize failed")
+    if h.hipMemcpyAsync(dst.ctypes.data, src_ptr, dst.nbytes, HIP_D2H, stream_ptr) != 0:
+        raise RuntimeError("hipMemcpyAsync D2H failed")
+    if h.hipStreamSynchronize(stream_ptr) != 0:
+        raise RuntimeError("hipStreamSynchronize failed")
+
+
+def copy_device(dst_ptr: int, src_ptr: int, nbytes: int, stream_ptr: int):
+    if hip_runtime().hipMemcpyAsync(dst_ptr, src_ptr, nbytes, HIP_D2D, stream_ptr) != 0:
+        raise RuntimeError("hipMemcpyAsync D2D failed")

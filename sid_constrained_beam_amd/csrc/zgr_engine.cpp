@@ -1,0 +1,460 @@
+// Step engine, decode loop, warm-up planner and error reporting.
+//
+// ZeroGR description, "why fewer scores is not faster": before a model
+// version takes traffic, every step's projection options are timed on
+// warm-up requests, the fastest is kept and frozen until the next update;
+// there is no per-request decision, so the choice follows the GPU, the
+// precision and the batch size.  Here a plan is made for one (index, weights,
+// dtype, d, B, K) and owns the HBM scratch of a step; zgr_step enqueues one
+// step on a stream without any host round trip.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "zgr_internal.h"
+
+namespace zgr {
+
+bool supported_hidden_size(int d);
+
+namespace {
+thread_local std::string g_err;
+thread_local int32_t g_err_status = ZGR_OK;
+}  // namespace
+
+int32_t fail(int32_t status, const std::string& msg) {
+  g_err = msg;
+  g_err_status = status;
+  return status;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(ZGR_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace zgr
+
+struct zgr_plan {
+  const zgr_index* idx = nullptr;
+  uint64_t idx_generation = 0;
+  int device = -1;
+  int32_t L = 0, V = 0, d = 0, B = 0, K = 0, dtype = 0;
+  std::vector<const void*> W;
+  int32_t choice[zgr::kMaxL] = {0};
+  float us_full[zgr::kMaxL], us_sel[zgr::kMaxL];
+  int n_cu = 256;
+  // HBM scratch
+  std::vector<void*> allocations;
+  float* z = nullptr;
+  int64_t z_elems = 0;
+  int32_t* nlegal = nullptr;
+  int32_t* unit_start = nullptr;
+  uint64_t* bkeys = nullptr;
+  int32_t* bcount = nullptr;
+  int32_t* err = nullptr;
+  // decode state: double-buffered beams and prefixes, hidden vectors, outputs
+  void* hidden = nullptr;
+  int32_t *row[2] = {nullptr, nullptr}, *prefix[2] = {nullptr, nullptr};
+  float* cum[2] = {nullptr, nullptr};
+  int32_t *parent = nullptr, *token = nullptr;
+};
+
+namespace {
+
+using namespace zgr;
+
+int64_t elem_size(int32_t dtype) { return dtype == ZGR_F32 ? 4 : 2; }
+
+int32_t beams_in(const zgr_plan* p, int32_t t) { return t == 1 ? 1 : p->K; }
+
+int32_t plan_alloc(zgr_plan* p, void** dst, size_t bytes) {
+  hipError_t e = hipMalloc(dst, std::max<size_t>(bytes, 256));
+  if (e != hipSuccess) {
+    *dst = nullptr;
+    (void)hipGetLastError();
+    return fail(ZGR_E_NOMEM, "zgr_plan: hipMalloc of " + std::to_string(bytes) + " bytes");
+  }
+  p->allocations.push_back(*dst);
+  return ZGR_OK;
+}
+
+// Cost model used for AUTO steps when nothing was timed: the selective path
+// moves one weight row per legal candidate (HBM bound), the full path does a
+// dense [M x d] x [d x V] product (MFMA bound) and writes M x V scores.
+int32_t model_choice(const zgr_plan* p, int32_t t) {
+  const HostTable& h = p->idx->host[t - 1];
+  const double M = (double)p->B * beams_in(p, t);
+  const double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
+  const double es = (double)elem_size(p->dtype);
+  const double sel_bytes = M * std::min((double)p->V, mean_n) * p->d * es;
+  const double sel_s = sel_bytes / 4.0e12;
+  const double peak = (p->dtype == ZGR_F32) ? 157.3e12 : 2.5e15;
+  const double full_s = 2.0 * M * p->V * p->d / (0.5 * peak) + M * p->V * 8.0 / 4.0e12;
+  return full_s < sel_s ? ZGR_PROJ_FULL : ZGR_PROJ_SELECTIVE;
+}
+
+int32_t check_args_step(const zgr_plan* p, int32_t t, const void* hidden, const int32_t* row_in,
+                        const float* cum_in, int32_t k_in, const int32_t* parent_out,
+                        const int32_t* token_out, const int32_t* row_out, const float* cum_out) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_step: null plan");
+  if (t < 1 || t > p->L) return fail(ZGR_E_ARG, "zgr_step: t out of range");
+  if (!hidden || !row_in || !cum_in || !parent_out || !token_out || !row_out || !cum_out)
+    return fail(ZGR_E_ARG, "zgr_step: null buffer");
+  if (k_in < 1 || k_in > p->K) return fail(ZGR_E_ARG, "zgr_step: k_in must be in [1, K]");
+  if (!index_alive(p->idx, p->idx_generation))
+    return fail(ZGR_E_STATE, "zgr_step: plan is stale (its index was freed)");
+  return ZGR_OK;
+}
+
+StepArgs make_args(zgr_plan* p, int32_t t, const void* hidden, const int32_t* row_in,
+                   const float* cum_in, int32_t k_in, int32_t* parent_out, int32_t* token_out,
+                   int32_t* row_out, float* cum_out, float* slot_dbg, const int32_t* prefix_in,
+                   int32_t* prefix_out) {
+  StepArgs a{};
+  a.tab = p->idx->dev[t - 1];
+  a.t = t;
+  a.L = p->L;
+  a.B = p->B;
+  a.K = p->K;
+  a.k_in = k_in;
+  a.M = p->B * k_in;
+  a.d = p->d;
+  a.dtype = p->dtype;
+  a.hidden = hidden;
+  a.W = p->W[t - 1];
+  a.row_in = row_in;
+  a.cum_in = cum_in;
+  a.parent_out = parent_out;
+  a.token_out = token_out;
+  a.row_out = row_out;
+  a.cum_out = cum_out;
+  a.slot_dbg = slot_dbg;
+  a.prefix_in = prefix_in;
+  a.prefix_out = prefix_out;
+  a.z = p->z;
+  a.nlegal = p->nlegal;
+  a.unit_start = p->unit_start;
+  a.bkeys = p->bkeys;
+  a.bcount = p->bcount;
+  a.err = p->err;
+  a.n_cu = p->n_cu;
+  return a;
+}
+
+// Enqueue one step with the given projection.
+int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
+  const bool dense = a.tab.fmt == ZGR_FMT_DENSE;
+  hipError_t e;
+  if (proj == ZGR_PROJ_FULL) {
+    a.ldz = p->V;
+    e = launch_full_projection(a, s);
+    if (e != hipSuccess) return hip_fail(e, "full projection launch");
+    e = launch_beam_reduce(a, true, s);
+  } else {
+    a.ldz = a.tab.stride;
+    e = launch_selective_score(a, s);
+    if (e != hipSuccess) return hip_fail(e, "selective score launch");
+    e = launch_beam_reduce(a, dense, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "beam reduce launch");
+  e = launch_request_select(a, s);
+  if (e != hipSuccess) return hip_fail(e, "request select launch");
+  return ZGR_OK;
+}
+
+int32_t read_device_flag(zgr_plan* p, hipStream_t s) {
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  int32_t flag = 0;
+  e = hipMemcpy(&flag, p->err, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy error flag");
+  if (flag) {
+    const int32_t zero = 0;
+    e = hipMemcpy(p->err, &zero, sizeof(int32_t), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpy error flag reset");
+    return fail(ZGR_E_DEVICE, "a beam row was outside its step table (beam treated as dead)");
+  }
+  return ZGR_OK;
+}
+
+// One decode (all L steps).  When time_opts is set, every AUTO step is run
+// with both projections, each timed with HIP events; the later run's outputs
+// carry the decode forward.
+int32_t decode_impl(zgr_plan* p, zgr_hidden_fn fn, void* user, hipStream_t s, bool time_opts,
+                    std::vector<float>* t_full, std::vector<float>* t_sel, int* final_buf) {
+  hipError_t e = launch_decode_init(p->row[0], p->cum[0], p->B, p->K, s);
+  if (e != hipSuccess) return hip_fail(e, "decode init launch");
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  if (time_opts)
+    for (auto& x : ev) {
+      e = hipEventCreate(&x);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+  int cur = 0;
+  int32_t rc = ZGR_OK;
+  for (int32_t t = 1; t <= p->L && rc == ZGR_OK; ++t) {
+    const int32_t k_in = beams_in(p, t);
+    if (fn(user, t, p->B, k_in, p->prefix[cur], p->L, p->hidden, (void*)s) != 0) {
+      rc = fail(ZGR_E_CALLBACK, "hidden-vector callback returned non-zero at step " + std::to_string(t));
+      break;
+    }
+    StepArgs a = make_args(p, t, p->hidden, p->row[cur], p->cum[cur], k_in, p->parent, p->token,
+                           p->row[1 - cur], p->cum[1 - cur], nullptr, p->prefix[cur],
+                           p->prefix[1 - cur]);
+    if (time_opts && p->choice[t - 1] == ZGR_PROJ_AUTO) {
+      float ms_full = 0.f, ms_sel = 0.f;
+      (void)hipEventRecord(ev[0], s);
+      rc = run_step(p, a, ZGR_PROJ_FULL, s);
+      (void)hipEventRecord(ev[1], s);
+      if (rc == ZGR_OK) rc = run_step(p, a, ZGR_PROJ_SELECTIVE, s);
+      (void)hipEventRecord(ev[2], s);
+      if (rc != ZGR_OK) break;
+      e = hipEventSynchronize(ev[2]);
+      if (e != hipSuccess) {
+        rc = hip_fail(e, "hipEventSynchronize");
+        break;
+      }
+      (void)hipEventElapsedTime(&ms_full, ev[0], ev[1]);
+      (void)hipEventElapsedTime(&ms_sel, ev[1], ev[2]);
+      t_full[t - 1].push_back(ms_full * 1000.f);
+      t_sel[t - 1].push_back(ms_sel * 1000.f);
+    } else {
+      int32_t proj = p->choice[t - 1];
+      if (proj == ZGR_PROJ_AUTO) proj = model_choice(p, t);
+      rc = run_step(p, a, proj, s);
+    }
+    cur = 1 - cur;
+  }
+  if (time_opts)
+    for (auto& x : ev)
+      if (x) (void)hipEventDestroy(x);
+  if (rc != ZGR_OK) {
+    (void)hipStreamSynchronize(s);
+    return rc;
+  }
+  *final_buf = cur;  // index of the buffers holding the final beams
+  return ZGR_OK;
+}
+
+float median(std::vector<float> v) {
+  if (v.empty()) return -1.f;
+  std::sort(v.begin(), v.end());
+  const size_t n = v.size();
+  return (n & 1) ? v[n / 2] : 0.5f * (v[n / 2 - 1] + v[n / 2]);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zgr_status_str(int32_t status) {
+  switch (status) {
+    case ZGR_OK: return "ok";
+    case ZGR_E_ARG: return "invalid argument";
+    case ZGR_E_DUP_SID: return "duplicate SID in catalog";
+    case ZGR_E_TOKEN_RANGE: return "catalog token outside [0, V)";
+    case ZGR_E_SHAPE: return "unsupported shape";
+    case ZGR_E_NOMEM: return "out of memory";
+    case ZGR_E_HIP: return "HIP runtime error";
+    case ZGR_E_STATE: return "invalid state";
+    case ZGR_E_CALLBACK: return "hidden-vector callback failed";
+    case ZGR_E_DEVICE: return "device-side invalid input";
+    default: return "unknown status";
+  }
+}
+
+int32_t zgr_last_error(char* buf, size_t n) {
+  if (buf && n > 0) {
+    const size_t k = std::min(n - 1, zgr::g_err.size());
+    std::memcpy(buf, zgr::g_err.data(), k);
+    buf[k] = '\0';
+  }
+  return zgr::g_err_status;
+}
+
+int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t dtype, int32_t d,
+                        int32_t B, int32_t K, zgr_hidden_fn hidden_fn, void* user,
+                        int32_t n_warmup, const int32_t* force, void* stream, zgr_plan** out) {
+  if (!idx || !W_dev || !out) return fail(ZGR_E_ARG, "zgr_plan_warmup: null argument");
+  *out = nullptr;
+  if (dtype < ZGR_F32 || dtype > ZGR_F16) return fail(ZGR_E_ARG, "zgr_plan_warmup: bad dtype");
+  if (B < 1 || K < 1) return fail(ZGR_E_ARG, "zgr_plan_warmup: B and K must be >= 1");
+  if (K > 1024) return fail(ZGR_E_SHAPE, "zgr_plan_warmup: K must be <= 1024");
+  if ((int64_t)B * K >= INT32_MAX) return fail(ZGR_E_SHAPE, "zgr_plan_warmup: B*K must be < 2^31");
+  if (d < 64 || d % 64 != 0 || !supported_hidden_size(d))
+    return fail(ZGR_E_SHAPE, "zgr_plan_warmup: d must be one of 64,128,256,512,768,1024,2048,4096");
+  if (n_warmup < 0) return fail(ZGR_E_ARG, "zgr_plan_warmup: n_warmup must be >= 0");
+  for (int l = 0; l < idx->L; ++l) {
+    if (!W_dev[l]) return fail(ZGR_E_ARG, "zgr_plan_warmup: null W_t");
+    if (force && (force[l] < ZGR_PROJ_AUTO || force[l] > ZGR_PROJ_SELECTIVE))
+      return fail(ZGR_E_ARG, "zgr_plan_warmup: force[t] must be AUTO, FULL or SELECTIVE");
+    // the slot code beam_rank * S_t + slot must fit 32 bits
+    if ((int64_t)K * std::max<int32_t>(1, idx->host[l].stride) >= (int64_t)UINT32_MAX)
+      return fail(ZGR_E_SHAPE, "zgr_plan_warmup: K * slot stride too large");
+  }
+  if (!idx->on_device) return fail(ZGR_E_STATE, "zgr_plan_warmup: index is not on the device");
+  hipStream_t s = (hipStream_t)stream;
+  zgr_plan* p = new (std::nothrow) zgr_plan();
+  if (!p) return fail(ZGR_E_NOMEM, "zgr_plan_warmup: host allocation");
+  p->idx = idx;
+  p->idx_generation = idx->generation;
+  p->L = idx->L;
+  p->V = idx->V;
+  p->d = d;
+  p->B = B;
+  p->K = K;
+  p->dtype = dtype;
+  p->W.assign(W_dev, W_dev + idx->L);
+  for (int l = 0; l < zgr::kMaxL; ++l) {
+    p->choice[l] = (force && l < idx->L) ? force[l] : ZGR_PROJ_AUTO;
+    p->us_full[l] = p->us_sel[l] = -1.f;
+  }
+  hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipGetDevice");
+  }
+  if (p->device != idx->device) {
+    delete p;
+    return fail(ZGR_E_STATE, "zgr_plan_warmup: index lives on another device");
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, p->device) == hipSuccess && prop.multiProcessorCount > 0)
+    p->n_cu = prop.multiProcessorCount;
+  // scratch sizes over all steps
+  const int64_t MK = (int64_t)B * K;
+  int64_t zmax = 0;
+  // any step may be called with up to K beams per request
+  for (int l = 0; l < idx->L; ++l)
+    zmax = std::max(zmax, MK * (int64_t)std::max(idx->host[l].stride, idx->V));
+  p->z_elems = zmax;
+  int32_t rc = ZGR_OK;
+  auto A = [&](void** dst, size_t bytes) {
+    if (rc == ZGR_OK) rc = plan_alloc(p, dst, bytes);
+  };
+  A((void**)&p->z, (size_t)zmax * 4);
+  A((void**)&p->nlegal, (size_t)MK * 4);
+  A((void**)&p->unit_start, (size_t)(MK + 1) * 4);
+  A((void**)&p->bkeys, (size_t)MK * K * 8);
+  A((void**)&p->bcount, (size_t)MK * 4);
+  A((void**)&p->err, 4);
+  A(&p->hidden, (size_t)MK * d * elem_size(dtype));
+  for (int i = 0; i < 2; ++i) {
+    A((void**)&p->row[i], (size_t)MK * 4);
+    A((void**)&p->cum[i], (size_t)MK * 4);
+    A((void**)&p->prefix[i], (size_t)MK * p->L * 4);
+  }
+  A((void**)&p->parent, (size_t)MK * 4);
+  A((void**)&p->token, (size_t)MK * 4);
+  if (rc != ZGR_OK) {
+    zgr_plan_free(p);
+    return rc;
+  }
+  e = hipMemsetAsync(p->err, 0, 4, s);
+  if (e == hipSuccess) e = hipMemsetAsync(p->prefix[0], 0xFF, (size_t)MK * p->L * 4, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    zgr_plan_free(p);
+    return hip_fail(e, "plan scratch init");
+  }
+  bool any_auto = false;
+  for (int l = 0; l < p->L; ++l) any_auto |= p->choice[l] == ZGR_PROJ_AUTO;
+  if (any_auto && n_warmup > 0 && hidden_fn) {
+    std::vector<float> tf[zgr::kMaxL], ts[zgr::kMaxL];
+    for (int w = 0; w < n_warmup; ++w) {
+      int fb = 0;
+      const int32_t r = decode_impl(p, hidden_fn, user, s, true, tf, ts, &fb);
+      if (r != ZGR_OK) {
+        zgr_plan_free(p);
+        return r;
+      }
+    }
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      zgr_plan_free(p);
+      return hip_fail(e, "hipStreamSynchronize after warm-up");
+    }
+    for (int l = 0; l < p->L; ++l) {
+      if (p->choice[l] != ZGR_PROJ_AUTO) continue;
+      p->us_full[l] = median(tf[l]);
+      p->us_sel[l] = median(ts[l]);
+      p->choice[l] = (p->us_full[l] < p->us_sel[l]) ? ZGR_PROJ_FULL : ZGR_PROJ_SELECTIVE;
+    }
+    const int32_t st = read_device_flag(p, s);
+    if (st != ZGR_OK) {
+      zgr_plan_free(p);
+      return st;
+    }
+  }
+  for (int l = 0; l < p->L; ++l)
+    if (p->choice[l] == ZGR_PROJ_AUTO) p->choice[l] = model_choice(p, l + 1);
+  *out = p;
+  return ZGR_OK;
+}
+
+int32_t zgr_plan_choice(const zgr_plan* p, int32_t t, int32_t* proj, float* us_full, float* us_sel) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_plan_choice: null plan");
+  if (t < 1 || t > p->L) return fail(ZGR_E_ARG, "zgr_plan_choice: t out of range");
+  if (proj) *proj = p->choice[t - 1];
+  if (us_full) *us_full = p->us_full[t - 1];
+  if (us_sel) *us_sel = p->us_sel[t - 1];
+  return ZGR_OK;
+}
+
+int32_t zgr_plan_set_choice(zgr_plan* p, int32_t t, int32_t proj) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_plan_set_choice: null plan");
+  if (t < 1 || t > p->L) return fail(ZGR_E_ARG, "zgr_plan_set_choice: t out of range");
+  if (proj != ZGR_PROJ_FULL && proj != ZGR_PROJ_SELECTIVE)
+    return fail(ZGR_E_ARG, "zgr_plan_set_choice: proj must be FULL or SELECTIVE");
+  p->choice[t - 1] = proj;
+  return ZGR_OK;
+}
+
+void zgr_plan_free(zgr_plan* p) {
+  if (!p) return;
+  if (!p->allocations.empty()) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (p->device >= 0 && cur != p->device) (void)hipSetDevice(p->device);
+    (void)hipDeviceSynchronize();
+    for (void* x : p->allocations) (void)hipFree(x);
+    if (cur >= 0 && cur != p->device) (void)hipSetDevice(cur);
+  }
+  delete p;
+}
+
+int32_t zgr_step(zgr_plan* p, int32_t t, const void* hidden_dev, const int32_t* row_in,
+                 const float* cum_in, int32_t k_in, int32_t* parent_out, int32_t* token_out,
+                 int32_t* row_out, float* cum_out, float* slot_dbg, void* stream) {
+  int32_t rc = check_args_step(p, t, hidden_dev, row_in, cum_in, k_in, parent_out, token_out,
+                               row_out, cum_out);
+  if (rc != ZGR_OK) return rc;
+  StepArgs a = make_args(p, t, hidden_dev, row_in, cum_in, k_in, parent_out, token_out, row_out,
+                         cum_out, slot_dbg, nullptr, nullptr);
+  return run_step(p, a, p->choice[t - 1], (hipStream_t)stream);
+}
+
+int32_t zgr_decode(zgr_plan* p, zgr_hidden_fn hidden_fn, void* user, int32_t top_k,
+                   int64_t* item_out, int32_t* sid_out, float* score_out, void* stream) {
+  if (!p || !hidden_fn || !item_out) return fail(ZGR_E_ARG, "zgr_decode: null argument");
+  if (top_k < 1 || top_k > p->K) return fail(ZGR_E_ARG, "zgr_decode: top_k must be in [1, K]");
+  if (!index_alive(p->idx, p->idx_generation))
+    return fail(ZGR_E_STATE, "zgr_decode: plan is stale (its index was freed)");
+  hipStream_t s = (hipStream_t)stream;
+  int cur = 0;
+  const int32_t rc = decode_impl(p, hidden_fn, user, s, false, nullptr, nullptr, &cur);
+  if (rc != ZGR_OK) return rc;
+  hipError_t e = launch_decode_final(p->row[cur], p->cum[cur], p->prefix[cur], p->B, p->K, p->L,
+                                     top_k, item_out, sid_out, score_out, s);
+  if (e != hipSuccess) return hip_fail(e, "decode final launch");
+  return read_device_flag(p, s);
+}
+
+int32_t zgr_plan_status(zgr_plan* p, void* stream) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_plan_status: null plan");
+  return read_device_flag(p, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal structures shared by the host index builder, the engine and the
+// kernel launchers.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/zgr.h"
+
+namespace zgr {
+
+constexpr int kMaxL = 8;
+
+// One step's table on the host.
+struct HostTable {
+  int32_t fmt = ZGR_FMT_SPARSE;
+  int64_t rows = 0;
+  int64_t nnz = 0;
+  int32_t stride = 0;     // slots per beam
+  int32_t max_legal = 0;  // largest row length
+  std::vector<int32_t> row_ptr;  // [rows + 1]
+  std::vector<uint16_t> tok;     // [nnz]
+  std::vector<uint32_t> bits;    // dense: [rows][words]
+};
+
+// One step's table in HBM (plain pointers, passed to kernels by value).
+struct DevTable {
+  int32_t fmt;
+  int32_t stride;
+  int32_t words;  // ceil(V / 32)
+  int32_t V;
+  int64_t rows;
+  const int32_t* row_ptr;
+  const uint16_t* tok;   // sparse only
+  const uint32_t* bits;  // dense only
+};
+
+}  // namespace zgr
+
+struct zgr_index {
+  int32_t L = 0, V = 0, bits = 0;
+  int64_t N = 0;
+  zgr::HostTable host[zgr::kMaxL];
+  zgr::DevTable dev[zgr::kMaxL];
+  bool on_device = false;
+  int device = -1;
+  std::vector<void*> allocations;
+  uint64_t generation = 0;
+};
+
+namespace zgr {
+
+// Registry of live indexes: a plan checks that the index it was made for
+// (pointer and generation) has not been freed.
+void index_register(const zgr_index* idx, uint64_t generation);
+void index_unregister(const zgr_index* idx);
+bool index_alive(const zgr_index* idx, uint64_t generation);
+
+// thread-local error detail
+int32_t fail(int32_t status, const std::string& msg);
+int32_t hip_fail(hipError_t e, const char* what);
+
+// ---- kernel launchers (zgr_kernels.hip) --------------------------------------------------
+struct StepArgs {
+  DevTable tab;
+  int32_t t, L;
+  int32_t B, K, k_in, M;  // M = B * k_in beams in
+  int32_t d, dtype;
+  const void* hidden;     // [M][d]
+  const void* W;          // [V][d]
+  const int32_t* row_in;
+  const float* cum_in;
+  int32_t* parent_out;
+  int32_t* token_out;
+  int32_t* row_out;
+  float* cum_out;
+  float* slot_dbg;
+  const int32_t* prefix_in;  // decode only: [M][L]
+  int32_t* prefix_out;       // decode only: [B*K][L]
+  // scratch
+  float* z;             // score buffer
+  int64_t ldz;          // its row stride
+  int32_t* nlegal;      // [M]
+  int32_t* unit_start;  // [M + 1]
+  uint64_t* bkeys;      // [M][K]
+  int32_t* bcount;      // [M]
+  int32_t* err;         // device error flag
+  int32_t n_cu;
+};
+
+hipError_t launch_selective_score(const StepArgs& a, hipStream_t s);
+hipError_t launch_full_projection(const StepArgs& a, hipStream_t s);
+hipError_t launch_beam_reduce(const StepArgs& a, bool token_indexed, hipStream_t s);
+hipError_t launch_request_select(const StepArgs& a, hipStream_t s);
+hipError_t launch_decode_init(int32_t* row, float* cum, int32_t B, int32_t K, hipStream_t s);
+hipError_t launch_decode_final(const int32_t* row, const float* cum, const int32_t* prefix,
+                               int32_t B, int32_t K, int32_t L, int32_t top_k, int64_t* item_out,
+                               int32_t* sid_out, float* score_out, hipStream_t s);
+
+// Tile of tokens handled by one work unit on dense steps, and of candidates on sparse steps.
+constexpr int kDenseTile = 1024;
+constexpr int kSparseTile = 64;
+
+}  // namespace zgr

@@ -1,0 +1,208 @@
+"""Shared helpers of the GPU parity tests (not collected by pytest).
+
+Parity protocol (tolerance tol: 1e-4 for fp32, 2e-2 for bf16/f16 storage;
+the oracle runs in double on the same stored values):
+  step check, teacher-forced (GPU and oracle get identical beams, hidden
+  vectors and cumulative scores):
+    - every beam's legal slots are exactly the oracle's legal tokens (sparse:
+      slot j = j-th legal token; dense: slot = token), other slots -inf;
+    - each legal log-prob within tol of the oracle's;
+    - the GPU's picks: all candidates scoring above tau + tol are picked and
+      none below tau - tol (tau = the oracle's K-th score), in non-increasing
+      oracle order up to 2 tol; cum_out within tol; next rows bit-exact;
+    - when the band |score - tau| <= tol holds only tau, the picks are the
+      oracle's picks exactly.
+  decode check: the GPU decode equals the GPU's own step-by-step trajectory,
+  every step of which passes the step check; where the oracle's own decode
+  meets no band ambiguity, the returned items are identical to the oracle's.
+"""
+import os
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import sid_constrained_beam_amd as zgr  # noqa: E402
+import workload  # noqa: E402
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
+
+
+def torch_dtype(dtype):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+
+
+def to_device_bits(bits, dtype):
+    """Stored values (float32 array, or uint16 bit patterns) -> device tensor of dtype."""
+    import torch
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return t.view(torch_dtype(dtype))
+
+
+class Setup:
+    """One workload on the GPU and in the oracle."""
+
+    def __init__(self, cfg, with_oracle=True):
+        import torch
+        self.cfg = cfg
+        self.sids = workload.catalog(cfg)
+        fmt = cfg.fmt
+        self.index, self.rank = zgr.zgr_index_upload(self.sids, cfg.V, fmt)
+        self.W_bits, self.W_f32 = [], []
+        for t in range(1, cfg.L + 1):
+            b, f = workload.weights(cfg, t)
+            self.W_bits.append(b)
+            self.W_f32.append(f)
+        self.W_dev = [to_device_bits(b, cfg.dtype) for b in self.W_bits]
+        torch.cuda.synchronize()
+        self.cat = oracle.Catalog(self.sids, cfg.V) if with_oracle else None
+        self.stats = [self.index.stats(t) for t in range(1, cfg.L + 1)]
+        self._decodes = {}
+
+    def hidden_source(self, req_base=0, per_decode=0):
+        """Hidden-vector callback: request ids req_base + i (advanced by
+        per_decode at each new decode, for warm-up traffic)."""
+        cfg = self.cfg
+        state = {"base": req_base - per_decode}
+
+        def fn(t, B, k_in, prefix_ptr, prefix_ld, hidden_ptr, stream_ptr):
+            if t == 1:
+                state["base"] += per_decode
+            M = B * k_in
+            prefix = np.empty((M, prefix_ld), np.int32)
+            zgr.copy_to_host(prefix, prefix_ptr, stream_ptr)
+            req = state["base"] + np.arange(M) // k_in
+            bits, _ = workload.hidden(cfg, t, req, prefix, want_f32=False)
+            zgr.copy_to_device(hidden_ptr, bits, stream_ptr)
+            return 0
+        return fn
+
+    def plan(self, force=None, n_warmup=0, B=None, K=None, warm_base=None):
+        cfg = self.cfg
+        B = B or cfg.B
+        K = K or cfg.K
+        hs = None
+        if n_warmup:
+            hs = self.hidden_source(req_base=warm_base if warm_base is not None else B, per_decode=B)
+        return zgr.zgr_plan_warmup(self.index, self.W_dev, cfg.dtype, cfg.d, B, K, hs, n_warmup,
+                                   force)
+
+    def oracle_decode(self, request, K=None):
+        cfg = self.cfg
+        key = (request, K or cfg.K)
+        if key not in self._decodes:
+            def hid(r, t, prefixes):
+                return workload.hidden(cfg, t, np.full(len(prefixes), r, np.int64), prefixes)[1]
+            self._decodes[key] = oracle.decode(self.cat, self.W_f32, hid, request, key[1],
+                                               keep_steps=True)
+        return self._decodes[key]
+
+
+def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True):
+    """Run zgr_step on given beams.  prefixes [B*k_in, t-1] (rows of dead beams
+    ignored), cum float32 [B*k_in] (-inf = dead).  Returns dict of numpy outputs
+    and the inputs used."""
+    import torch
+    cfg = setup.cfg
+    M = len(cum)
+    k_in = M // B
+    rows = np.full(M, -1, np.int32)
+    for i in range(M):
+        if np.isfinite(cum[i]):
+            rows[i] = setup.cat.node(prefixes[i, : t - 1]) if t > 1 else 0
+            assert rows[i] >= 0
+    req = np.repeat(np.asarray(requests, np.int64), k_in)
+    pre = prefixes if t > 1 else np.zeros((M, 1), np.int32)
+    bits, h32 = workload.hidden(cfg, t, req, np.ascontiguousarray(pre, np.int32))
+    dev = dict(
+        hidden=to_device_bits(bits, cfg.dtype),
+        row_in=torch.from_numpy(rows).cuda(),
+        cum_in=torch.from_numpy(np.asarray(cum, np.float32)).cuda(),
+        parent=torch.empty(B * K, dtype=torch.int32, device="cuda"),
+        token=torch.empty(B * K, dtype=torch.int32, device="cuda"),
+        row_out=torch.empty(B * K, dtype=torch.int32, device="cuda"),
+        cum_out=torch.empty(B * K, dtype=torch.float32, device="cuda"),
+    )
+    S = setup.stats[t - 1]["stride"]
+    dbg = torch.empty(M * S, dtype=torch.float32, device="cuda") if with_dbg else None
+    zgr.zgr_step(plan, t, dev["hidden"], dev["row_in"], dev["cum_in"], k_in, dev["parent"],
+                 dev["token"], dev["row_out"], dev["cum_out"], dbg)
+    zgr.zgr_plan_status(plan)
+    out = {k: dev[k].cpu().numpy() for k in ("parent", "token", "row_out", "cum_out")}
+    out["dbg"] = dbg.cpu().numpy().reshape(M, S) if with_dbg else None
+    out["h32"] = h32
+    out["rows"] = rows
+    return out
+
+
+def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True):
+    """Step check against the oracle on identical inputs.  Returns the number of
+    requests whose K-th score boundary was ambiguous."""
+    cfg = setup.cfg
+    M = len(cum)
+    k_in = M // B
+    st = setup.stats[t - 1]
+    dense = st["fmt"] == zgr.ZGR_FMT_DENSE
+    ambiguous = 0
+    for q in range(B):
+        sl = slice(q * k_in, (q + 1) * k_in)
+        pq = prefixes[sl, : t - 1] if t > 1 else np.zeros((k_in, 0), np.int32)
+        cq = np.asarray(cum[sl], np.float64)
+        res = setup.cat.step(t, setup.W_f32[t - 1], pq, cq, out["h32"][sl], K)
+        # (i) legal slots and their log-probs
+        if check_dbg and out["dbg"] is not None:
+            dbg = out["dbg"][sl]
+            for k in range(k_in):
+                m = res.cand_beam == k
+                toks = res.cand_token[m]
+                lp = res.cand_logp[m]
+                row = dbg[k]
+                legal_slots = toks if dense else np.arange(len(toks))
+                got_legal = np.nonzero(np.isfinite(row))[0]
+                assert np.array_equal(got_legal, np.sort(legal_slots)), (q, k, got_legal[:10], legal_slots[:10])
+                err = np.abs(row[legal_slots] - lp)
+                assert err.max(initial=0) <= tol, (q, k, err.max())
+        # (ii) selection by the band protocol
+        scores = {(int(b), int(v)): s for b, v, s in zip(res.cand_beam, res.cand_token, res.cand_score)}
+        allv = np.sort(np.fromiter(scores.values(), np.float64))[::-1]
+        kk = min(K, len(allv))
+        o = slice(q * K, (q + 1) * K)
+        par, tok, rowo, cumo = out["parent"][o], out["token"][o], out["row_out"][o], out["cum_out"][o]
+        assert np.all(par[kk:] == -1) and np.all(tok[kk:] == -1) and np.all(rowo[kk:] == -1)
+        assert np.all(np.isneginf(cumo[kk:]))
+        if kk == 0:
+            continue
+        tau = allv[kk - 1]
+        picks = []
+        for i in range(kk):
+            b = int(par[i]) - q * k_in
+            assert 0 <= b < k_in, (q, i, par[i])
+            key = (b, int(tok[i]))
+            assert key in scores, ("illegal pick", q, key)
+            s = scores[key]
+            assert abs(cumo[i] - s) <= tol, (q, i, cumo[i], s)
+            ext = np.concatenate([pq[b], [tok[i]]]).astype(np.int32)
+            assert rowo[i] == setup.cat.node(ext), (q, i)
+            picks.append(s)
+        assert len(set(zip(par[:kk].tolist(), tok[:kk].tolist()))) == kk
+        picks = np.array(picks)
+        above = sum(1 for s in scores.values() if s > tau + tol)
+        assert np.sum(picks > tau + tol) == above
+        assert np.all(picks >= tau - tol)
+        assert np.all(np.diff(picks) <= 2 * tol)
+        band = sum(1 for s in scores.values() if abs(s - tau) <= tol)
+        if band == 1:
+            want = list(zip(res.sel_beam.tolist(), res.sel_token.tolist()))
+            got = [(int(par[i]) - q * k_in, int(tok[i])) for i in range(kk)]
+            assert set(got) == set(want), (q, "selection differs without ambiguity")
+        else:
+            ambiguous += 1
+    return ambiguous

@@ -1,0 +1,103 @@
+"""The C ABI: every declared symbol is exported; argument errors are reported
+before any device work (these calls never touch a GPU)."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import sid_constrained_beam_amd as zgr
+
+
+def test_library_exports_every_declared_symbol():
+    names = zgr.header_symbols()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(zgr.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    for code in range(0, 10):
+        s = zgr.status_str(code)
+        assert s and s != "unknown status"
+    assert zgr.status_str(99) == "unknown status"
+
+
+def _expect(status, fn, *args):
+    with pytest.raises(zgr.ZgrError) as e:
+        fn(*args)
+    assert e.value.status == status, (e.value.status, e.value.detail)
+    return e.value
+
+
+def test_index_argument_errors():
+    ok = np.array([[0, 1], [1, 0]], np.int32)
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, ok, 1)            # V < 2
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, ok, 70000)        # V > 65536
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, np.zeros((0, 2), np.int32), 4)
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, np.zeros((3, 9), np.int32), 4)  # L > 8
+    e = _expect(zgr.ZGR_E_TOKEN_RANGE, zgr.zgr_index_build_host, np.array([[0, 1], [1, 4]], np.int32), 4)
+    assert "row 1" in e.detail
+    _expect(zgr.ZGR_E_TOKEN_RANGE, zgr.zgr_index_build_host, np.array([[0, -1]], np.int32), 4)
+    e = _expect(zgr.ZGR_E_DUP_SID, zgr.zgr_index_build_host,
+                np.array([[0, 1], [2, 3], [0, 1]], np.int32), 4)
+    assert "0" in e.detail and "2" in e.detail
+    _expect(zgr.ZGR_E_SHAPE, zgr.zgr_index_build_host, np.zeros((1, 5), np.int32), 65536)  # 80 bits
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, ok, 4, [3, 0])    # bad fmt code
+    L = zgr.lib()
+    h = ctypes.c_void_p()
+    assert L.zgr_index_build_host(None, 2, 2, 4, None, None, ctypes.byref(h)) == zgr.ZGR_E_ARG
+    assert L.zgr_index_stats(None, 1, None) == zgr.ZGR_E_ARG
+    assert L.zgr_index_to_device(None, None) == zgr.ZGR_E_ARG
+    L.zgr_index_free(None)  # no-op
+
+
+def test_index_stats_range():
+    idx, _ = zgr.zgr_index_build_host(np.array([[0, 1], [1, 0]], np.int32), 4)
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_stats, idx, 0)
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_stats, idx, 3)
+    assert zgr.zgr_index_shape(idx) == (2, 4, 2)
+
+
+def test_plan_and_step_argument_errors():
+    L = zgr.lib()
+    idx, _ = zgr.zgr_index_build_host(np.array([[0, 1], [1, 0]], np.int32), 4)
+    W = (ctypes.c_void_p * 2)(1, 1)
+    out = ctypes.c_void_p()
+    cb = zgr.HIDDEN_FN()
+    # null index / weights / out
+    assert L.zgr_plan_warmup(None, W, 0, 64, 1, 1, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_ARG
+    assert L.zgr_plan_warmup(idx.handle, None, 0, 64, 1, 1, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_ARG
+    # bad dtype, sizes, hidden size, K
+    assert L.zgr_plan_warmup(idx.handle, W, 7, 64, 1, 1, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_ARG
+    assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 0, 1, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_ARG
+    assert L.zgr_plan_warmup(idx.handle, W, 0, 100, 1, 1, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_SHAPE
+    assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 1, 2000, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_SHAPE
+    bad_force = (ctypes.c_int32 * 2)(0, 5)
+    assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 1, 1, cb, None, 0, bad_force, None, ctypes.byref(out)) == zgr.ZGR_E_ARG
+    # the index was built on the host only: a plan needs it on the device
+    assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 1, 1, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_STATE
+    assert "not on the device" in zgr.last_error()
+    # step / decode / choice on a null plan
+    assert L.zgr_step(None, 1, 1, 1, 1, 1, 1, 1, 1, 1, None, None) == zgr.ZGR_E_ARG
+    assert L.zgr_decode(None, cb, None, 1, 1, None, None, None) == zgr.ZGR_E_ARG
+    assert L.zgr_plan_choice(None, 1, None, None, None) == zgr.ZGR_E_ARG
+    assert L.zgr_plan_set_choice(None, 1, 1) == zgr.ZGR_E_ARG
+    assert L.zgr_plan_status(None, None) == zgr.ZGR_E_ARG
+    L.zgr_plan_free(None)
+
+
+def test_last_error_is_thread_local():
+    import threading
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, np.array([[0, 1]], np.int32), 1)
+    seen = {}
+
+    def other():
+        _expect(zgr.ZGR_E_DUP_SID, zgr.zgr_index_build_host, np.array([[0, 1], [0, 1]], np.int32), 4)
+        seen["other"] = zgr.last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert "share one SID" in seen["other"]
+    assert "V must be" in zgr.last_error()

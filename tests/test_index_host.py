@@ -1,0 +1,130 @@
+"""Host-built filter index against the oracle's trie (bit-exact), no GPU."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import sid_constrained_beam_amd as zgr
+import workload
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def row_prefixes(idx, L):
+    """Prefix of every row of every table, rebuilt from the tables alone:
+    entry e of row r in table t is row e of table t+1, with prefix(r) + tok[e]."""
+    pre = [np.zeros((1, 0), np.int32)]
+    for t in range(1, L + 1):
+        row_ptr, tok, bits = idx.host_table(t)
+        counts = np.diff(row_ptr)
+        parent = np.repeat(np.arange(len(counts)), counts)
+        nxt = np.concatenate([pre[-1][parent], tok.astype(np.int32)[:, None]], axis=1)
+        pre.append(nxt)
+    return pre
+
+
+def check_against_oracle(sids, V, fmt=None, sample=None, seed=0):
+    N, L = sids.shape
+    idx, rank = zgr.zgr_index_build_host(sids, V, fmt)
+    cat = oracle.Catalog(sids, V)
+    pre = row_prefixes(idx, L)
+    rng = np.random.default_rng(seed)
+    for t in range(1, L + 1):
+        st = idx.stats(t)
+        assert st["rows"] == cat.count(t - 1)
+        assert st["nnz"] == cat.count(t)
+        row_ptr, tok, bits = idx.host_table(t)
+        assert row_ptr[0] == 0 and row_ptr[-1] == st["nnz"]
+        counts = np.diff(row_ptr)
+        assert counts.min() >= 1  # every row leads to at least one item
+        assert st["max_legal"] == counts.max()
+        if st["fmt"] == zgr.ZGR_FMT_DENSE:
+            assert st["stride"] == V
+            assert bits is not None and bits.shape == (st["rows"], (V + 31) // 32)
+            # bitmap rows hold exactly the sorted legal tokens
+            pc = np.unpackbits(bits.view(np.uint8), axis=1, bitorder="little")[:, :V].sum(1)
+            assert np.array_equal(pc, counts)
+        else:
+            assert st["stride"] == counts.max() and bits is None
+        rows = np.arange(st["rows"]) if sample is None else rng.choice(st["rows"], min(sample, st["rows"]), replace=False)
+        for r in rows:
+            p = pre[t - 1][r]
+            assert cat.node(p) == r  # rows are lexicographic prefix ranks
+            legal = tok[row_ptr[r]:row_ptr[r + 1]]
+            assert np.array_equal(legal, cat.legal(p))
+            if bits is not None:
+                setb = np.nonzero(np.unpackbits(bits[r].view(np.uint8), bitorder="little"))[0]
+                assert np.array_equal(setb, legal)
+        # the next row of entry e is the rank of the extended prefix
+        ents = np.arange(st["nnz"]) if sample is None else rng.choice(st["nnz"], min(sample, st["nnz"]), replace=False)
+        for e in ents:
+            assert cat.node(pre[t][e]) == e
+    # item ids: position in the last table = oracle item id = lexicographic rank
+    for i in (range(N) if sample is None else rng.choice(N, min(sample, N), replace=False)):
+        assert cat.input_row(int(rank[i])) == i
+        assert np.array_equal(pre[L][rank[i]], sids[i])
+    return idx
+
+
+def test_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    sids = np.array(g["catalog"], np.int32)
+    for fmt in (None, ["D"] * 3, ["S"] * 3):
+        idx = check_against_oracle(sids, g["V"], fmt)
+        pre = row_prefixes(idx, 3)
+        for q in g["queries"]:
+            p = np.array(q["prefix"], np.int32)
+            t = len(p) + 1
+            match = [r for r in range(len(pre[t - 1])) if np.array_equal(pre[t - 1][r], p)]
+            if not q["legal"]:
+                assert not match
+                continue
+            row_ptr, tok, _ = idx.host_table(t)
+            r = match[0]
+            assert tok[row_ptr[r]:row_ptr[r + 1]].tolist() == q["legal"]
+
+
+def test_slot_example_layout():
+    g = json.load(open(os.path.join(GOLDEN, "slot_example.json")))
+    idx, _ = zgr.zgr_index_build_host(np.array(g["catalog"], np.int32), g["V"], ["D", "S"])
+    st = idx.stats(2)
+    assert st["fmt"] == zgr.ZGR_FMT_SPARSE
+    assert st["stride"] == g["slot_stride"]
+    row_ptr, tok, _ = idx.host_table(2)
+    assert np.diff(row_ptr).tolist() == g["legal_counts"]
+
+
+@pytest.mark.parametrize("fmt", [None, "D", "S"])
+@pytest.mark.parametrize("V,L,N,seed", [(4, 3, 40, 1), (16, 4, 900, 2), (300, 2, 5000, 3), (2, 6, 50, 4)])
+def test_random_catalogs(V, L, N, seed, fmt):
+    rng = np.random.default_rng(seed)
+    space = V ** L
+    codes = rng.choice(space, size=min(N, space), replace=False)
+    sids = np.stack([(codes // V ** (L - 1 - l)) % V for l in range(L)], 1).astype(np.int32)
+    check_against_oracle(sids, V, None if fmt is None else [fmt] * L)
+
+
+def test_format_policy_and_forced():
+    cfg = workload.CONFIGS["n1e4_v256"]
+    sids = workload.catalog(cfg)
+    idx, _ = zgr.zgr_index_build_host(sids, cfg.V)
+    for t in range(1, cfg.L + 1):
+        st = idx.stats(t)
+        dense_bytes = st["rows"] * ((cfg.V + 31) // 32) * 4
+        sparse_bytes = st["nnz"] * 2
+        want = zgr.ZGR_FMT_DENSE if dense_bytes < sparse_bytes else zgr.ZGR_FMT_SPARSE
+        assert st["fmt"] == want
+    d_idx, _ = zgr.zgr_index_build_host(sids, cfg.V, ["D"] * cfg.L)
+    s_idx, _ = zgr.zgr_index_build_host(sids, cfg.V, ["S"] * cfg.L)
+    for t in range(1, cfg.L + 1):
+        a, b = d_idx.host_table(t), s_idx.host_table(t)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name", ["n1e4_v256", "n1e6_v2048"])
+def test_config_catalogs_sampled(name):
+    cfg = workload.CONFIGS[name]
+    sids = workload.catalog(cfg)
+    check_against_oracle(sids, cfg.V, cfg.fmt, sample=None if cfg.N <= 10_000 else 300)
