@@ -1,0 +1,408 @@
+#!/usr/bin/env python3
+"""Filter+score+select latency per decode on one MI355X.
+
+One "step" of this benchmark is one full decode pass of the hot path: the L
+per-step calls (filter, score, legal-only log-softmax + cumulative add,
+per-request select) for a batch of B requests, with every step's inputs
+(hidden vectors, beam rows, cumulative scores) already resident in HBM.  The
+inputs are those of a real decode of the workload (recorded once, untimed);
+the hidden vectors stand in for the model, whose time the metric excludes.
+
+Default workload: L=3, V=2048, N=1e6 items (Zipf 1.1 per level), d=256,
+beam 64, batch 32, fp32 ("n1e6_v2048").  Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
+KERNEL_NAMES = {
+    "units": "k_units",
+    "selective": "k_score_selective",
+    "gemm": "k_gemm_nt / k_gemm_small",
+    "request": "k_request_step",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha():
+    p = os.path.join(ROOT, "sid_constrained_beam_amd", "csrc", "zgr_kernels.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+class Workload:
+    """Index, weights, a frozen plan and one recorded decode trajectory."""
+
+    def __init__(self, name, n_warmup_plan, force=None):
+        import torch
+
+        import sid_constrained_beam_amd as zgr
+        import workload
+        self.zgr = zgr
+        self.cfg = cfg = workload.CONFIGS[name]
+        t0 = time.time()
+        self.sids = workload.catalog(cfg)
+        self.index, _ = zgr.zgr_index_upload(self.sids, cfg.V, cfg.fmt)
+        self.W_f32 = []
+        self.W_dev = []
+        for t in range(1, cfg.L + 1):
+            bits, f32 = workload.weights(cfg, t)
+            self.W_f32.append(f32)
+            if cfg.dtype == "f32":
+                self.W_dev.append(torch.from_numpy(bits).cuda())
+            else:
+                dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float16
+                self.W_dev.append(torch.from_numpy(bits.view(np.int16)).cuda().view(dt))
+        log(f"[bench] {name}: catalog + index + weights in {time.time() - t0:.1f}s")
+        self.tables = [self.index.host_table(t) for t in range(1, cfg.L + 1)]
+        self.stats = [self.index.stats(t) for t in range(1, cfg.L + 1)]
+        # warm-up requests B .. B*(1+n)-1: never the measured ones
+        state = {"base": 0}
+
+        def warm_hidden(t, B, k_in, prefix_ptr, ld, hidden_ptr, stream_ptr):
+            if t == 1:
+                state["base"] += B
+            return self._fill_hidden(t, B, k_in, prefix_ptr, ld, hidden_ptr, stream_ptr, state["base"])
+        t0 = time.time()
+        self.plan = zgr.zgr_plan_warmup(self.index, self.W_dev, cfg.dtype, cfg.d, cfg.B, cfg.K,
+                                        warm_hidden, n_warmup_plan, force)
+        self.choices = [self.plan.choice(t) for t in range(1, cfg.L + 1)]
+        log(f"[bench] plan in {time.time() - t0:.1f}s: " + ", ".join(
+            f"t{t + 1}={'full' if c[0] == 1 else 'selective'} (full {c[1]:.1f}us, sel {c[2]:.1f}us)"
+            for t, c in enumerate(self.choices)))
+        self._record()
+
+    def _fill_hidden(self, t, B, k_in, prefix_ptr, ld, hidden_ptr, stream_ptr, base):
+        import workload
+        M = B * k_in
+        prefix = np.empty((M, ld), np.int32)
+        self.zgr.copy_to_host(prefix, prefix_ptr, stream_ptr)
+        bits, _ = workload.hidden(self.cfg, t, base + np.arange(M) // k_in, prefix, want_f32=False)
+        self.zgr.copy_to_device(hidden_ptr, bits, stream_ptr)
+        return 0
+
+    def _record(self):
+        """Run the measured requests 0..B-1 step by step and keep each step's inputs."""
+        import torch
+
+        import workload
+        cfg, zgr = self.cfg, self.zgr
+        B, K, L = cfg.B, cfg.K, cfg.L
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[cfg.dtype]
+        self.steps = []
+        prefixes = np.zeros((B, 1), np.int32)
+        rows = torch.zeros(B, dtype=torch.int32, device="cuda")
+        cum = torch.zeros(B, dtype=torch.float32, device="cuda")
+        self.out = dict(parent=torch.empty(B * K, dtype=torch.int32, device="cuda"),
+                        token=torch.empty(B * K, dtype=torch.int32, device="cuda"),
+                        row=torch.empty(B * K, dtype=torch.int32, device="cuda"),
+                        cum=torch.empty(B * K, dtype=torch.float32, device="cuda"))
+        for t in range(1, L + 1):
+            k_in = 1 if t == 1 else K
+            M = B * k_in
+            bits, _ = workload.hidden(cfg, t, np.arange(M) // k_in, prefixes, want_f32=False)
+            h = torch.from_numpy(bits if cfg.dtype == "f32" else bits.view(np.int16)).cuda()
+            if cfg.dtype != "f32":
+                h = h.view(dt)
+            self.steps.append(dict(t=t, k_in=k_in, hidden=h, row=rows.clone(), cum=cum.clone()))
+            zgr.zgr_step(self.plan, t, h, rows, cum, k_in, self.out["parent"], self.out["token"],
+                         self.out["row"], self.out["cum"])
+            zgr.zgr_plan_status(self.plan)
+            par = self.out["parent"].cpu().numpy()
+            tok = self.out["token"].cpu().numpy()
+            new = np.full((B * K, t), -1, np.int32)
+            ok = par >= 0
+            if t > 1:
+                new[ok, : t - 1] = prefixes[par[ok], : t - 1]
+            new[ok, t - 1] = tok[ok]
+            prefixes = new
+            rows = self.out["row"].clone()
+            cum = self.out["cum"].clone()
+        # per-step legal counts of the recorded beams (for the algorithmic work)
+        for st in self.steps:
+            row_ptr = self.tables[st["t"] - 1][0]
+            r = st["row"].cpu().numpy()
+            live = r >= 0
+            n = np.zeros(len(r), np.int64)
+            n[live] = row_ptr[r[live] + 1] - row_ptr[r[live]]
+            st["n"] = n
+            st["M"] = len(r)
+            st["live"] = int(live.sum())
+        torch.cuda.synchronize()
+
+    def run_decode(self, stream=None):
+        zgr = self.zgr
+        for st in self.steps:
+            zgr.zgr_step(self.plan, st["t"], st["hidden"], st["row"], st["cum"], st["k_in"],
+                         self.out["parent"], self.out["token"], self.out["row"], self.out["cum"],
+                         None, stream)
+
+    # ---- algorithmic work per launch (what the method must move or compute) ----
+    def light(self, st):
+        """Selective sparse steps whose scoring runs inside the request kernel
+        (same rule as the library: one block per request can gather them)."""
+        cfg = self.cfg
+        tab = self.stats[st["t"] - 1]
+        if tab["fmt"] != 2 or self.choices[st["t"] - 1][0] != 2:
+            return False
+        es = 4 if cfg.dtype == "f32" else 2
+        mean = tab["nnz"] / max(1, tab["rows"])
+        return st["k_in"] * min(mean, tab["stride"]) * cfg.d * es <= (1 << 20)
+
+    def work(self, kernel, st):
+        cfg = self.cfg
+        es = 4 if cfg.dtype == "f32" else 2
+        n = st["n"]
+        M, live = st["M"], st["live"]
+        tab = self.stats[st["t"] - 1]
+        dense = tab["fmt"] == 1
+        cand = int(n.sum())
+        gather = cand * (cfg.d * es + (0 if dense else 2) + 4) + live * (cfg.d * es + 8)
+        if kernel == "selective":
+            return "hbm", float(gather + M * 4 + (live * (cfg.V // 8) if dense else 0))
+        if kernel == "gemm":
+            return "mfma", 2.0 * M * cfg.V * cfg.d
+        if kernel == "request":
+            # z of every legal candidate, bitmap rows, beam state in, K beams out
+            b = cand * 4 + M * 12 + cfg.B * cfg.K * (16 + 4 * cfg.L)
+            if dense:
+                b += live * (cfg.V // 8 + cfg.V // 16)
+            if self.light(st):
+                b += gather
+            return "hbm", float(b)
+        if kernel == "units":
+            return "hbm", float(M * 16)
+        raise ValueError(kernel)
+
+
+def timed(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def read_traffic(kernel_name, workload):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}__{workload}__pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    try:
+        if vals.get("source_sha") != source_sha():
+            return None
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seconds):
+    """The CPU oracle's filter+score+select on a bounded sample of the same
+    workload's requests (single thread), scaled to one decode of B requests."""
+    import oracle
+    import workload
+    cfg = w.cfg
+    t0 = time.time()
+    cat = oracle.Catalog(w.sids, cfg.V)
+    build_s = time.time() - t0
+    spent = 0.0
+    done = 0
+    for r in range(10 ** 6):
+        prefixes = np.zeros((1, 0), np.int32)
+        cum = np.zeros(1)
+        for t in range(1, cfg.L + 1):
+            h = workload.hidden(cfg, t, np.full(len(prefixes), r, np.int64), prefixes)[1]
+            s0 = time.perf_counter()
+            res = cat.step(t, w.W_f32[t - 1], prefixes, cum, h, cfg.K)
+            spent += time.perf_counter() - s0
+            k = len(res.sel_beam)
+            new = np.empty((k, t), np.int32)
+            new[:, : t - 1] = prefixes[res.sel_beam]
+            new[:, t - 1] = res.sel_token
+            prefixes, cum = new, res.sel_score.copy()
+        done += 1
+        if spent >= seconds:
+            break
+    per_request_ms = spent / done * 1e3
+    return {"value": round(per_request_ms * cfg.B, 3), "unit": "ms", "cores": 1, "kind": "oracle",
+            "sample": f"requests 0..{done - 1} of the {cfg.name} workload decoded by the oracle "
+                      f"(double precision, one thread); {spent:.1f}s of step time (filter, score, "
+                      f"legal-only log-softmax, select; hidden-vector generation and the "
+                      f"{build_s:.1f}s trie build excluded), scaled to one decode of "
+                      f"{cfg.B} requests"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="n1e6_v2048")
+    ap.add_argument("--plan-warmup", type=int, default=5, help="warm-up decodes of the planner")
+    ap.add_argument("--force", default=None, help="comma list of full/selective per step")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph replay")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no "
+                                   "multi-GPU mode (requests would shard across GPUs with no "
+                                   "exchange, see the design notes)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import sid_constrained_beam_amd as zgr
+    torch.cuda.set_device(0)
+    force = args.force.split(",") if args.force else None
+    w = Workload(args.workload, args.plan_warmup, force)
+    cfg = w.cfg
+
+    # ---- timed region: whole decodes (L steps) over recorded HBM-resident inputs
+    stream = torch.cuda.Stream()
+    mode = "eager"
+    with torch.cuda.stream(stream):
+        w.run_decode(stream)
+        torch.cuda.synchronize()
+        if not args.eager:
+            try:
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph, stream=stream):
+                    w.run_decode(stream)
+                torch.cuda.synchronize()
+                # the replay must reproduce eager outputs
+                w.run_decode(stream)
+                torch.cuda.synchronize()
+                ref = {k: v.clone() for k, v in w.out.items()}
+                for _ in range(3):
+                    graph.replay()
+                    torch.cuda.synchronize()
+                    for k in ref:
+                        if not torch.equal(ref[k], w.out[k]):
+                            raise RuntimeError("graph replay differs from eager")
+                    w.run_decode(stream)
+                    torch.cuda.synchronize()
+                mode = "graph"
+            except Exception as e:  # noqa: BLE001 - fall back to eager timing, and say so
+                log(f"[bench] graph capture unavailable ({e}); timing eager launches")
+                mode = "eager"
+        fn = graph.replay if mode == "graph" else (lambda: w.run_decode(stream))
+        sec = timed(fn, args.steps, args.warmup)
+        eager_sec = sec if mode == "eager" else timed(lambda: w.run_decode(stream), args.steps,
+                                                      args.warmup)
+    ms = sec * 1e3
+    log(f"[bench] {mode}: {ms * 1e3:.1f} us per decode (eager {eager_sec * 1e6:.1f} us)")
+
+    # ---- per-kernel durations: HIP events around every launch, eager, same stream
+    with torch.cuda.stream(stream):
+        zgr.zgr_plan_profile(w.plan, True)
+        for _ in range(args.steps):
+            w.run_decode(stream)
+        torch.cuda.synchronize()
+    per = {}
+    total_kernel_ms = 0.0
+    for kname in zgr.KERNELS:
+        tot_ms, launches, units, bound = 0.0, 0, 0.0, None
+        for st in w.steps:
+            n, kms = zgr.zgr_plan_profile_read(w.plan, kname, st["t"])
+            if n == 0:
+                continue
+            b, u = w.work(kname, st)
+            bound = b
+            tot_ms += kms
+            launches += n
+            units += u * n
+            log(f"[bench]   t{st['t']} {kname:15s} {kms / n * 1e3:8.2f} us/launch  "
+                f"{'GB/s' if b == 'hbm' else 'TFLOP/s'} "
+                f"{(u / (kms / n * 1e-3)) / (1e9 if b == 'hbm' else 1e12):9.1f}  "
+                f"cand {int(st['n'].sum())}")
+        if launches:
+            per[kname] = dict(ms=tot_ms, launches=launches, units=units, bound=bound)
+            total_kernel_ms += tot_ms
+    zgr.zgr_plan_profile(w.plan, False)
+    dom = max(per, key=lambda k: per[k]["ms"])
+    d = per[dom]
+    avg_s = d["ms"] / d["launches"] * 1e-3
+    achieved_per_s = d["units"] / d["launches"] / avg_s
+    if d["bound"] == "hbm":
+        achieved, peak, unit = achieved_per_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = achieved_per_s / 1e12, MFMA_PEAK_TFS[cfg.dtype], "TFLOP/s"
+    roofline = {"bound": d["bound"], "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
+                "traffic": read_traffic(KERNEL_NAMES[dom], cfg.name),
+                "kernel": KERNEL_NAMES[dom], "avg_launch_us": round(avg_s * 1e6, 2),
+                "share_of_kernel_time": round(d["ms"] / total_kernel_ms, 3)}
+    cand_per_decode = sum(int(st["n"].sum()) for st in w.steps)
+    # algorithmic bytes of the decode's bandwidth-bound kernels (as run) per decode
+    hbm_bytes = 0.0
+    for st in w.steps:
+        proj = w.choices[st["t"] - 1][0]
+        names = ["request"] + (["gemm"] if proj == 1 else ([] if w.light(st) else ["units", "selective"]))
+        for k in names:
+            b, u = w.work(k, st)
+            if b == "hbm":
+                hbm_bytes += u
+    line = {
+        "metric": "filter+score+select latency per decode (ms) at batch 32; achieved HBM GB/s",
+        "value": round(ms, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: L={cfg.L}, V={cfg.V}, N={cfg.N}, d={cfg.d}, "
+                               f"beam={cfg.K}, batch={cfg.B}, {cfg.dtype}",
+                   "batch": cfg.B, "beam": cfg.K, "launch": mode,
+                   "projection": ["full" if c[0] == 1 else "selective" for c in w.choices]},
+        "candidates_per_s": round(cand_per_decode / sec, 1),
+        "candidates_per_decode": cand_per_decode,
+        "eager_ms": round(eager_sec * 1e3, 4),
+        "hbm_gbs_algorithmic": round(hbm_bytes / sec / 1e9, 1),
+        "roofline": roofline,
+    }
+    if args.calibrate_copy:
+        # a plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 5 copies of {args.calibrate_copy} MiB")
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

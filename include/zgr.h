@@ -224,6 +224,29 @@ int32_t zgr_decode(zgr_plan* plan, zgr_hidden_fn hidden_fn, void* user, int32_t 
  * flag: ZGR_OK or ZGR_E_DEVICE; ZGR_E_HIP if the sync fails. */
 int32_t zgr_plan_status(zgr_plan* plan, void* stream);
 
+/* ---- per-kernel timing ------------------------------------------------------------------ */
+
+/* Kernel classes of a step, for zgr_plan_profile_read. */
+#define ZGR_KERNEL_UNITS 0      /* per-beam legal counts and work-unit scan (selective) */
+#define ZGR_KERNEL_SELECTIVE 1  /* selective projection: weight rows gathered in place */
+#define ZGR_KERNEL_GEMM 2       /* full projection on MFMA */
+#define ZGR_KERNEL_REQUEST 3    /* per request: legal-only log-softmax, cumulative add, top-K,
+                                   next rows, prefixes (and, on light sparse steps, the
+                                   selective projection itself) */
+#define ZGR_KERNEL_COUNT 4
+
+/* Turn per-kernel timing on (enable != 0) or off and reset the counters.
+ * While on, zgr_step / zgr_decode bracket every kernel launch with two HIP
+ * events on the launch stream (this adds a little time per launch; do not
+ * capture such launches into graphs).  Errors: ZGR_E_ARG, ZGR_E_HIP. */
+int32_t zgr_plan_profile(zgr_plan* plan, int32_t enable);
+
+/* Synchronise on the recorded events and return, for kernel class `kernel`
+ * at step t, the number of timed launches and their summed duration (ms).
+ * Errors: ZGR_E_ARG, ZGR_E_HIP. */
+int32_t zgr_plan_profile_read(zgr_plan* plan, int32_t kernel, int32_t t, int64_t* launches,
+                              double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ ZGR_E_NOMEM, ZGR_E_HIP, ZGR_E_STATE, ZGR_E_CALLBACK, ZGR_E_DEVICE = 5, 6, 7, 8, 
 ZGR_F32, ZGR_BF16, ZGR_F16 = 0, 1, 2
 ZGR_FMT_AUTO, ZGR_FMT_DENSE, ZGR_FMT_SPARSE = 0, 1, 2
 ZGR_PROJ_AUTO, ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE = 0, 1, 2
+KERNELS = ["units", "selective", "gemm", "request"]
 
 DTYPE_CODES = {"f32": ZGR_F32, "bf16": ZGR_BF16, "f16": ZGR_F16}
 FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR_FMT_SPARSE}
@@ -80,6 +81,9 @@ def lib() -> ctypes.CDLL:
             "zgr_step": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P]),
             "zgr_decode": (_I32, [_P, HIDDEN_FN, _P, _I32, _P, _P, _P, _P]),
             "zgr_plan_status": (_I32, [_P, _P]),
+            "zgr_plan_profile": (_I32, [_P, _I32]),
+            "zgr_plan_profile_read": (_I32, [_P, _I32, _I32, ctypes.POINTER(_I64),
+                                             ctypes.POINTER(ctypes.c_double)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -332,6 +336,18 @@ def zgr_decode(plan: Plan, hidden_fn: HiddenCallable, top_k: int, item_out, sid_
 
 def zgr_plan_status(plan: Plan, stream=None):
     _check(lib().zgr_plan_status(plan.handle, _stream_ptr(stream)))
+
+
+def zgr_plan_profile(plan: Plan, enable: bool):
+    _check(lib().zgr_plan_profile(plan.handle, 1 if enable else 0))
+
+
+def zgr_plan_profile_read(plan: Plan, kernel, t: int):
+    """(launches, total_ms) of a kernel class ('selective', 'gemm', ... or id) at step t."""
+    k = KERNELS.index(kernel) if isinstance(kernel, str) else int(kernel)
+    n, ms = _I64(), ctypes.c_double()
+    _check(lib().zgr_plan_profile_read(plan.handle, k, t, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 # --------------------------------------------------------------------------- HIP memcpy helper

@@ -51,14 +51,25 @@ struct zgr_plan {
   int64_t z_elems = 0;
   int32_t* nlegal = nullptr;
   int32_t* unit_start = nullptr;
-  uint64_t* bkeys = nullptr;
-  int32_t* bcount = nullptr;
+  float* lse = nullptr;
+  uint64_t* part_keys = nullptr;
+  int32_t* part_cnt = nullptr;
   int32_t* err = nullptr;
   // decode state: double-buffered beams and prefixes, hidden vectors, outputs
   void* hidden = nullptr;
   int32_t *row[2] = {nullptr, nullptr}, *prefix[2] = {nullptr, nullptr};
   float* cum[2] = {nullptr, nullptr};
   int32_t *parent = nullptr, *token = nullptr;
+  // optional per-kernel timing: HIP events recorded around each launch on its stream
+  struct ProfRec {
+    hipEvent_t a, b;
+    int kernel, t;
+  };
+  bool profiling = false;
+  std::vector<ProfRec> pending;
+  std::vector<hipEvent_t> pool;
+  double prof_ms[ZGR_KERNEL_COUNT][zgr::kMaxL] = {};
+  int64_t prof_n[ZGR_KERNEL_COUNT][zgr::kMaxL] = {};
 };
 
 namespace {
@@ -136,31 +147,106 @@ StepArgs make_args(zgr_plan* p, int32_t t, const void* hidden, const int32_t* ro
   a.z = p->z;
   a.nlegal = p->nlegal;
   a.unit_start = p->unit_start;
-  a.bkeys = p->bkeys;
-  a.bcount = p->bcount;
+  a.lse = p->lse;
+  a.parts = 1;
+  a.part_keys = p->part_keys;
+  a.part_cnt = p->part_cnt;
   a.err = p->err;
   a.n_cu = p->n_cu;
   return a;
 }
 
+hipEvent_t prof_event(zgr_plan* p) {
+  if (!p->pool.empty()) {
+    hipEvent_t e = p->pool.back();
+    p->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch through fn, bracketed by two events when profiling is on.
+template <class F>
+hipError_t prof_launch(zgr_plan* p, int kernel, int t, hipStream_t s, F&& fn) {
+  if (!p->profiling) return fn();
+  hipEvent_t a = prof_event(p), b = prof_event(p);
+  if (!a || !b) return fn();
+  (void)hipEventRecord(a, s);
+  const hipError_t e = fn();
+  (void)hipEventRecord(b, s);
+  p->pending.push_back({a, b, kernel, t});
+  return e;
+}
+
+int32_t prof_flush(zgr_plan* p) {
+  for (auto& r : p->pending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (profiling)");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      p->prof_ms[r.kernel][r.t - 1] += ms;
+      p->prof_n[r.kernel][r.t - 1] += 1;
+    }
+    p->pool.push_back(r.a);
+    p->pool.push_back(r.b);
+  }
+  p->pending.clear();
+  return ZGR_OK;
+}
+
+// A selective sparse step is "light" when one block per request can gather
+// its candidates' weight rows itself: then the step is a single launch.
+bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
+  const HostTable& h = p->idx->host[a.t - 1];
+  if (h.fmt != ZGR_FMT_SPARSE) return false;
+  const double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
+  const double bytes = (double)a.k_in * std::min<double>(mean_n, h.stride) * p->d * elem_size(p->dtype);
+  return bytes <= (double)(1 << 20);
+}
+
+// Blocks per request for the request kernel.  A request whose candidates are
+// many (a dense or full-projection step, or a heavy sparse one) is split over
+// several blocks so that more compute units stream its scores, then merged;
+// light requests stay whole (one launch).
+int32_t request_parts(const zgr_plan* p, const StepArgs& a, int zmode) {
+  if (a.k_in < 2) return 1;
+  const HostTable& h = p->idx->host[a.t - 1];
+  const double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
+  const double est_c = a.k_in * std::min<double>(mean_n, h.stride);
+  const bool heavy = (zmode == 0) || est_c > 2048.0;
+  if (!heavy) return 1;
+  int P = std::max(1, p->n_cu / std::max(1, a.B));
+  P = std::min({P, a.k_in, kMaxParts, 14336 / std::max(1, a.K)});
+  return std::max(1, P);
+}
+
 // Enqueue one step with the given projection.
 int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
   const bool dense = a.tab.fmt == ZGR_FMT_DENSE;
+  const int t = a.t;
   hipError_t e;
+  int zmode;
   if (proj == ZGR_PROJ_FULL) {
     a.ldz = p->V;
-    e = launch_full_projection(a, s);
+    e = prof_launch(p, ZGR_KERNEL_GEMM, t, s, [&] { return launch_full_projection(a, s); });
     if (e != hipSuccess) return hip_fail(e, "full projection launch");
-    e = launch_beam_reduce(a, true, s);
+    zmode = 0;
+  } else if (!dense && light_sparse_step(p, a)) {
+    a.ldz = a.tab.stride;
+    zmode = 2;
   } else {
     a.ldz = a.tab.stride;
-    e = launch_selective_score(a, s);
+    e = prof_launch(p, ZGR_KERNEL_UNITS, t, s, [&] { return launch_units(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "unit count launch");
+    e = prof_launch(p, ZGR_KERNEL_SELECTIVE, t, s, [&] { return launch_selective_score(a, s); });
     if (e != hipSuccess) return hip_fail(e, "selective score launch");
-    e = launch_beam_reduce(a, dense, s);
+    zmode = dense ? 0 : 1;  // z is token-indexed on dense steps
   }
-  if (e != hipSuccess) return hip_fail(e, "beam reduce launch");
-  e = launch_request_select(a, s);
-  if (e != hipSuccess) return hip_fail(e, "request select launch");
+  a.parts = request_parts(p, a, zmode);
+  e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
+  if (e != hipSuccess) return hip_fail(e, "request step launch");
   return ZGR_OK;
 }
 
@@ -337,8 +423,9 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   A((void**)&p->z, (size_t)zmax * 4);
   A((void**)&p->nlegal, (size_t)MK * 4);
   A((void**)&p->unit_start, (size_t)(MK + 1) * 4);
-  A((void**)&p->bkeys, (size_t)MK * K * 8);
-  A((void**)&p->bcount, (size_t)MK * 4);
+  A((void**)&p->lse, (size_t)MK * 4);
+  A((void**)&p->part_keys, (size_t)B * kMaxParts * K * 8);
+  A((void**)&p->part_cnt, (size_t)B * kMaxParts * 4);
   A((void**)&p->err, 4);
   A(&p->hidden, (size_t)MK * d * elem_size(dtype));
   for (int i = 0; i < 2; ++i) {
@@ -412,8 +499,33 @@ int32_t zgr_plan_set_choice(zgr_plan* p, int32_t t, int32_t proj) {
   return ZGR_OK;
 }
 
+int32_t zgr_plan_profile(zgr_plan* p, int32_t enable) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_plan_profile: null plan");
+  const int32_t rc = prof_flush(p);
+  if (rc != ZGR_OK) return rc;
+  p->profiling = enable != 0;
+  std::memset(p->prof_ms, 0, sizeof(p->prof_ms));
+  std::memset(p->prof_n, 0, sizeof(p->prof_n));
+  return ZGR_OK;
+}
+
+int32_t zgr_plan_profile_read(zgr_plan* p, int32_t kernel, int32_t t, int64_t* launches,
+                              double* total_ms) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_plan_profile_read: null plan");
+  if (kernel < 0 || kernel >= ZGR_KERNEL_COUNT) return fail(ZGR_E_ARG, "zgr_plan_profile_read: bad kernel id");
+  if (t < 1 || t > p->L) return fail(ZGR_E_ARG, "zgr_plan_profile_read: t out of range");
+  const int32_t rc = prof_flush(p);
+  if (rc != ZGR_OK) return rc;
+  if (launches) *launches = p->prof_n[kernel][t - 1];
+  if (total_ms) *total_ms = p->prof_ms[kernel][t - 1];
+  return ZGR_OK;
+}
+
 void zgr_plan_free(zgr_plan* p) {
   if (!p) return;
+  (void)prof_flush(p);
+  for (hipEvent_t e : p->pool) (void)hipEventDestroy(e);
+  p->pool.clear();
   if (!p->allocations.empty()) {
     int cur = -1;
     (void)hipGetDevice(&cur);

@@ -294,10 +294,28 @@ extern "C" int32_t zgr_index_to_device(zgr_index* idx, void* stream) {
     d.words = words;
     d.V = idx->V;
     d.rows = h.rows;
-    void *rp = nullptr, *tk = nullptr, *bt = nullptr;
+    void *rp = nullptr, *tk = nullptr, *bt = nullptr, *rk = nullptr;
     int32_t rc = upload(h.row_ptr.data(), h.row_ptr.size() * 4, &rp);
     if (rc == ZGR_OK && h.fmt == ZGR_FMT_SPARSE) rc = upload(h.tok.data(), h.tok.size() * 2, &tk);
-    if (rc == ZGR_OK && h.fmt == ZGR_FMT_DENSE) rc = upload(h.bits.data(), h.bits.size() * 4, &bt);
+    std::vector<uint16_t> rank;
+    if (rc == ZGR_OK && h.fmt == ZGR_FMT_DENSE) {
+      rc = upload(h.bits.data(), h.bits.size() * 4, &bt);
+      // rank directory: set bits of the row before each word (a dense entry's
+      // next row is row_ptr[r] + rank + popcount within its word)
+      rank.resize(h.bits.size());
+      for (int64_t q = 0; q < h.rows; ++q) {
+        uint32_t acc = 0;
+        for (int32_t w = 0; w < words; ++w) {
+          rank[q * words + w] = (uint16_t)acc;
+          acc += (uint32_t)__builtin_popcount(h.bits[q * words + w]);
+        }
+      }
+      if (rc == ZGR_OK) rc = upload(rank.data(), rank.size() * 2, &rk);
+      if (rc == ZGR_OK) {
+        hipError_t se = hipStreamSynchronize(s);  // rank is a temporary
+        if (se != hipSuccess) rc = hip_fail(se, "hipStreamSynchronize");
+      }
+    }
     if (rc != ZGR_OK) {
       (void)hipStreamSynchronize(s);
       for (void* p : idx->allocations) (void)hipFree(p);
@@ -307,6 +325,7 @@ extern "C" int32_t zgr_index_to_device(zgr_index* idx, void* stream) {
     d.row_ptr = (const int32_t*)rp;
     d.tok = (const uint16_t*)tk;
     d.bits = (const uint32_t*)bt;
+    d.rank = (const uint16_t*)rk;
   }
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize after index upload");
@@ -343,7 +362,7 @@ extern "C" int32_t zgr_index_stats(const zgr_index* idx, int32_t t, zgr_step_sta
   out->stride = h.stride;
   out->max_legal = h.max_legal;
   out->reserved = 0;
-  out->bytes = (h.rows + 1) * 4 + (h.fmt == ZGR_FMT_DENSE ? h.rows * words * 4 : h.nnz * 2);
+  out->bytes = (h.rows + 1) * 4 + (h.fmt == ZGR_FMT_DENSE ? h.rows * words * 6 : h.nnz * 2);
   return ZGR_OK;
 }
 

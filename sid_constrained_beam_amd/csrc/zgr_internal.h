@@ -36,6 +36,7 @@ struct DevTable {
   const int32_t* row_ptr;
   const uint16_t* tok;   // sparse only
   const uint32_t* bits;  // dense only
+  const uint16_t* rank;  // dense only: [rows][words] set bits of the row before each word
 };
 
 }  // namespace zgr
@@ -85,16 +86,21 @@ struct StepArgs {
   int64_t ldz;          // its row stride
   int32_t* nlegal;      // [M]
   int32_t* unit_start;  // [M + 1]
-  uint64_t* bkeys;      // [M][K]
-  int32_t* bcount;      // [M]
+  float* lse;           // [M] per-beam log-sum-exp over legal tokens
+  int32_t parts;        // blocks per request in the request kernel (1 = no merge)
+  uint64_t* part_keys;  // [B * parts][K] best keys of each part
+  int32_t* part_cnt;    // [B * parts]
   int32_t* err;         // device error flag
   int32_t n_cu;
 };
 
+hipError_t launch_units(const StepArgs& a, hipStream_t s);
 hipError_t launch_selective_score(const StepArgs& a, hipStream_t s);
 hipError_t launch_full_projection(const StepArgs& a, hipStream_t s);
-hipError_t launch_beam_reduce(const StepArgs& a, bool token_indexed, hipStream_t s);
-hipError_t launch_request_select(const StepArgs& a, hipStream_t s);
+// zmode: 0 = z token-indexed, 1 = z slot-indexed, 2 = score inside the request kernel.
+// With a.parts > 1 each request is split over a.parts blocks, then merged.
+constexpr int kMaxParts = 16;
+hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s);
 hipError_t launch_decode_init(int32_t* row, float* cum, int32_t B, int32_t K, hipStream_t s);
 hipError_t launch_decode_final(const int32_t* row, const float* cum, const int32_t* prefix,
                                int32_t B, int32_t K, int32_t L, int32_t top_k, int64_t* item_out,

@@ -23,15 +23,16 @@
 //                      by a group of lanes (16-byte loads), h kept in registers,
 //                      a lane-group shuffle reduction, z stored at the slot.
 //   k_gemm_nt          full projection Z = H . W_t^T on MFMA (fp32, bf16, f16
-//                      inputs; fp32 accumulate), Z row = beam, column = token.
-//   k_beam_reduce      per beam: max and sum-exp over the legal slots only,
-//                      lse, cand = cum + (z - lse), then the beam's best
-//                      min(K, n_b) candidates as 64-bit keys (LDS radix select).
-//   k_request_select   per request: the best K keys over its beams (LDS radix
-//                      select), bitonic sort, decode (parent, token, cum) and
-//                      advance: next row = row_ptr[r] + slot (sparse: the
-//                      position is the next row) or row_ptr[r] + popcount of
-//                      the bitmap below the token (dense); prefix gather.
+//                      inputs; fp32 accumulate), Z row = beam, column = token;
+//   k_gemm_small       the same product for few beams (first step): 16x16 MFMA.
+//   k_request_step     one block per request: legal-only log-sum-exp of each
+//                      beam, cand = cum + (z - lse) for every legal candidate,
+//                      the best K by an LDS radix select, rank sort, decode
+//                      (parent, token, cum) and advance: next row = row_ptr[r]
+//                      + slot (sparse: the position is the next row) or
+//                      row_ptr[r] + rank directory + popcount (dense); prefix
+//                      gather.  On light sparse steps it also does the
+//                      selective projection itself (one launch per step).
 //
 // Ranking key (64 bits, larger = better): high word = order-preserving image
 // of the float cand, low word = ~(beam_rank * S_t + slot).  Keys are unique,
@@ -93,7 +94,7 @@ __device__ __forceinline__ uint64_t make_key(float cand, uint32_t slotcode) {
   return ((uint64_t)ord_of(cand) << 32) | (uint64_t)(0xFFFFFFFFu - slotcode);
 }
 
-// ---------------------------------------------------------------- block helpers (256 threads)
+// ---------------------------------------------------------------- wave / block helpers
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -105,10 +106,9 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
+  return ((uint64_t)hi << 32) | lo;
 }
 // inclusive prefix sum over the 64 lanes
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -121,42 +121,11 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Fixed-order block reductions (deterministic).
-__device__ float block_max(float v, float* sh) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r = fmaxf(r, sh[i]);
-  return r;
-}
-__device__ float block_sum(float v, float* sh) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) r += sh[i];
-  return r;
-}
-__device__ int block_sum_i(int v, int* sh) {
-  v = wave_sum_i(v);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  int r = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) r += sh[i];
-  return r;
-}
-// Exclusive prefix over the block's threads; *total gets the sum.
+// Exclusive prefix over the NT threads of a block (fixed order); *total = sum.
+// sh must hold NT/64 ints.
+template <int NT>
 __device__ int block_excl_scan(int v, int* sh, int* total) {
+  constexpr int NW = NT / 64;
   const int incl = wave_incl_scan(v);
   const int w = threadIdx.x >> 6;
   __syncthreads();
@@ -164,7 +133,7 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     if (i < w) before += sh[i];
     all += sh[i];
   }
@@ -172,26 +141,59 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   return before + incl - v;
 }
 
-// State of an LDS radix select for the `need` largest of a set of distinct
-// 64-bit keys, 8 bits per pass from the top.
+template <int NT>
+__device__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
+  constexpr int NW = NT / 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t u = shfl_xor_u64(v, o);
+    v = u > v ? u : v;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t r = sh[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = sh[i] > r ? sh[i] : r;
+  return r;
+}
+template <int NT>
+__device__ uint64_t block_min_u64(uint64_t v, uint64_t* sh) {
+  constexpr int NW = NT / 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t u = shfl_xor_u64(v, o);
+    v = u < v ? u : v;
+  }
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t r = sh[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) r = sh[i] < r ? sh[i] : r;
+  return r;
+}
+
+// State of a radix select for the `need` largest of a set of distinct 64-bit
+// keys, 8 bits per pass from the top: keys whose bits under `mask` equal
+// `prefix` are still undecided; keys above that prefix are already selected.
 struct RadixSel {
   uint64_t prefix;
   uint64_t mask;
   int need;
 };
 
-// One histogram pass has been accumulated in hist[256]; pick the digit that
-// holds the need-th largest key and narrow the state.  Returns true when every
-// key matching the new prefix is selected (no further pass needed).
-__device__ bool radix_narrow(RadixSel& s, int shift, int* hist, int* sh) {
-  // thread d looks at digit 255 - d: inclusive prefix over threads = count of
-  // keys whose digit is >= 255 - d
-  const int d = 255 - (int)threadIdx.x;
-  const int c = hist[d];
+// hist[256] holds the digit counts of the undecided keys at `shift`: pick the
+// digit holding the need-th largest and narrow.  True when every key under the
+// new prefix is selected.
+template <int NT>
+__device__ bool radix_narrow(RadixSel& s, int shift, const int* hist, int* sh) {
+  const int d = 255 - (int)threadIdx.x;  // thread i looks at digit 255 - i
+  const int c = (threadIdx.x < 256) ? hist[d] : 0;
   int total;
-  const int excl = block_excl_scan(c, sh, &total);
+  const int excl = block_excl_scan<NT>(c, sh, &total);
   __shared__ int pick_digit, pick_above, pick_count;
-  if (excl < s.need && excl + c >= s.need) {
+  if (threadIdx.x < 256 && excl < s.need && excl + c >= s.need) {
     pick_digit = d;
     pick_above = excl;
     pick_count = c;
@@ -207,10 +209,17 @@ __device__ bool radix_narrow(RadixSel& s, int shift, int* hist, int* sh) {
 
 // ---------------------------------------------------------------- k_units
 
+constexpr int kUnitsCache = 16384;
+
+// Per beam: legal count n_b and its work units (sparse: ceil(n_b / 64)
+// candidates; dense: ceil(V / 1024) token tiles), then the exclusive scan of
+// units over the M beams into unit_start[0..M] (unit_start[M] = total).
 __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_in, int32_t M,
                                                 DevTable tab, int32_t* __restrict__ nlegal,
                                                 int32_t* __restrict__ unit_start,
                                                 int32_t* __restrict__ err) {
+  __shared__ int ucache[kUnitsCache];
+  __shared__ int sh[16];
   const int per = (M + 1023) / 1024;
   const int b0 = threadIdx.x * per, b1 = min(M, b0 + per);
   const int dense_units = (tab.V + kDenseTile - 1) / kDenseTile;
@@ -227,22 +236,16 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
     return tab.fmt == ZGR_FMT_DENSE ? dense_units : (n + kSparseTile - 1) / kSparseTile;
   };
   int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += units_of(b, true);
-  // block-wide exclusive scan of 1024 per-thread totals
-  __shared__ int wsum[16];
-  const int incl = wave_incl_scan(mine);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 63) wsum[w] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int i = 0; i < 16; ++i) {
-    if (i < w) before += wsum[i];
-    total += wsum[i];
+  for (int b = b0; b < b1; ++b) {
+    const int u = units_of(b, true);
+    if (b < kUnitsCache) ucache[b] = u;
+    mine += u;
   }
-  int run = before + incl - mine;
+  int total;
+  int run = block_excl_scan<1024>(mine, sh, &total);
   for (int b = b0; b < b1; ++b) {
     unit_start[b] = run;
-    run += units_of(b, false);
+    run += (b < kUnitsCache) ? ucache[b] : units_of(b, false);
   }
   if (threadIdx.x == 0) unit_start[M] = total;
 }
@@ -349,207 +352,526 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
   }
 }
 
-// ---------------------------------------------------------------- k_beam_reduce
+// ---------------------------------------------------------------- k_request_step
 
-// Visit every legal candidate of row r: fn(slot, token).  Sparse: slot = rank
-// j, token = tok[row_ptr[r] + j]; dense: slot = token = set bit of the row.
-template <class F>
-__device__ __forceinline__ void for_each_legal(const DevTable& tab, int r, F&& fn) {
-  if (tab.fmt == ZGR_FMT_SPARSE) {
-    const int base = tab.row_ptr[r];
-    const int n = tab.row_ptr[r + 1] - base;
-    for (int j = threadIdx.x; j < n; j += kThreads) fn(j, (int)tab.tok[base + j]);
-  } else {
-    const uint32_t* row = tab.bits + (int64_t)r * tab.words;
-    for (int w = threadIdx.x; w < tab.words; w += kThreads) {
-      uint32_t x = row[w];
-      while (x) {
-        const int v = (w << 5) + __ffs(x) - 1;
-        x &= x - 1;
-        fn(v, v);
-      }
-    }
-  }
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelCap = 14336;  // candidates of a request whose keys fit in LDS (112 KiB)
+constexpr int kMaxK = 1024;
+
+// Distance histogram: 64 exact bins for distances below 64 ulps, then 64
+// sub-bins per octave (monotone in the distance; 1728 bins used).
+constexpr int kDistBins = 2 * kSelThreads;
+constexpr int kBoundary = kDistBins / 2;  // boundary keys resolved by rank counting
+
+__device__ __forceinline__ int dist_bin(uint32_t d) {
+  if (d < 64u) return (int)d;
+  const int e = 31 - __clz(d);
+  return ((e - 5) << 6) | (int)((d >> (e - 6)) & 63u);
 }
 
-// z source: token-indexed (full projection, or any dense step) or slot-indexed
-// (selective projection on a sparse step).
-template <bool TOKEN_IDX>
-__global__ __launch_bounds__(kThreads) void k_beam_reduce(
-    DevTable tab, int32_t M, int32_t k_in, int32_t K, const int32_t* __restrict__ row_in,
-    const float* __restrict__ cum_in, const float* __restrict__ z, int64_t ldz,
-    float* __restrict__ slot_dbg, uint64_t* __restrict__ bkeys, int32_t* __restrict__ bcount,
-    int32_t* __restrict__ err) {
-  __shared__ float shf[kWaves];
-  __shared__ int shi[kWaves + 1];
+// Each lane asks for cnt slots of a block-shared array: one atomic per wave.
+// Must be reached by all 64 lanes of the wave.
+__device__ __forceinline__ int wave_alloc(int cnt, int* counter) {
+  const int incl = wave_incl_scan(cnt);
+  const int total = __shfl(incl, 63);
+  int base = 0;
+  if ((threadIdx.x & 63) == 63 && total > 0) base = atomicAdd(counter, total);
+  base = __shfl(base, 63);
+  return base + incl - cnt;
+}
+
+// How z reaches the request kernel: token-indexed rows (full projection, or a
+// dense step), slot-indexed rows (selective projection of a sparse step), or
+// computed by the request kernel itself (selective projection of a light
+// sparse step: gather-dot in the block, no separate launches); kZParts is the
+// merge of a request split over several blocks.
+enum ZMode { kZToken = 0, kZSlot = 1, kZScore = 2, kZParts = 3 };
+
+// Combine two (max, sum of exp(x - max)) partials; lanes that saw nothing hold
+// (-inf, 0).  Symmetric, so both butterfly partners get identical bits.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  const float e1 = (m == mn) ? 1.f : __expf(m - mn);
+  const float e2 = (m2 == mn) ? 1.f : __expf(m2 - mn);
+  s = s * e1 + s2 * e2;
+  m = mn;
+}
+
+// One block per request, the whole step after scoring:
+//   1. each beam's legal count (its row of table t) and a prefix over the
+//      request's beams (candidate f of the request = beam, rank);
+//   2. (kZScore) z = W_t[token] . h_beam for every legal candidate, the weight
+//      row read in place by a lane group, z stored at the beam's slot;
+//   3. legal-only log-sum-exp of every beam (online max / sum of exp, fixed
+//      order; several waves per beam when the request has few beams);
+//   4. cand = cum + (z - lse) as a 64-bit key (ord(cand), ~(beam*S + slot));
+//      the K largest by radix select (in LDS up to 16384 candidates, else by
+//      passes over z);
+//   5. sorted by rank counting, decoded and advanced: next row = row_ptr[r] +
+//      slot (sparse: the position is the next row) or row_ptr[r] + rank
+//      directory + popcount (dense); prefixes gathered by parent.
+template <int MODE, int DT, int D>
+__global__ __launch_bounds__(kSelThreads) void k_request_step(
+    DevTable tab, int32_t t, int32_t L, int32_t k_in, int32_t K, const int32_t* __restrict__ row_in,
+    const float* __restrict__ cum_in, const void* __restrict__ hidden, const void* __restrict__ W,
+    float* __restrict__ z, int64_t ldz, int32_t vec4, int32_t P, uint64_t* __restrict__ part_keys,
+    int32_t* __restrict__ part_cnt, int32_t* __restrict__ parent_out,
+    int32_t* __restrict__ token_out, int32_t* __restrict__ row_out, float* __restrict__ cum_out,
+    const int32_t* __restrict__ prefix_in, int32_t* __restrict__ prefix_out,
+    float* __restrict__ slot_dbg, int32_t* __restrict__ err) {
+  constexpr int NT = kSelThreads;
+  constexpr bool TOKEN_IDX = (MODE == kZToken);
+  __shared__ uint64_t keys[kSelCap];
+  __shared__ uint64_t sel[kMaxK];
+  __shared__ int pre[kMaxK + 1];
+  __shared__ int brow[kMaxK];
+  __shared__ float bcum[kMaxK];
+  __shared__ float blse[kMaxK];
+  __shared__ float bmax[kMaxK];
+  __shared__ float pm[kSelWaves], ps[kSelWaves];
+  __shared__ __attribute__((aligned(16))) int dhist[kDistBins];
   __shared__ int hist[256];
-  __shared__ int pos;
-  const int b = blockIdx.x;
-  const int r = row_in[b];
-  const bool live = r >= 0 && r < tab.rows;
-  if (!live) {
-    if (threadIdx.x == 0) {
-      bcount[b] = 0;
-      if (r >= tab.rows) atomicOr(err, 1);
+  __shared__ int sh[kSelWaves];
+  __shared__ uint64_t sh64[kSelWaves];
+  __shared__ int pos, pos2, pick_bin, pick_above;
+  // P > 1: block (q, p) takes beams [blo, blo + nloc) of request q and
+  // leaves its best K keys in part_keys; the merge (MODE kZParts) picks the
+  // request's best K among the parts' keys.
+  constexpr bool MERGE = (MODE == kZParts);
+  const int q = MERGE ? blockIdx.x : blockIdx.x / P;
+  const int part = MERGE ? 0 : blockIdx.x - q * P;
+  const int kp = (k_in + P - 1) / P;
+  const int blo = MERGE ? 0 : min(k_in, part * kp);
+  const int nloc = MERGE ? k_in : min(k_in, blo + kp) - blo;
+  const int b0 = q * k_in + blo;
+  const bool dense = tab.fmt == ZGR_FMT_DENSE;
+  const uint32_t S = (uint32_t)tab.stride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+  // 1. the request's beams: row (-1 when dead), cumulative score, legal count,
+  //    work items (sparse: candidates; dense: bitmap words)
+  int cnt = 0, items = 0;
+  if ((int)threadIdx.x < nloc) {
+    int r = row_in[b0 + threadIdx.x];
+    if (r >= 0 && r < tab.rows) {
+      cnt = MERGE ? 0 : tab.row_ptr[r + 1] - tab.row_ptr[r];
+      items = dense ? (cnt > 0 ? tab.words : 0) : cnt;
+    } else {
+      if (r >= tab.rows && !MERGE) atomicOr(err, 1);
+      r = -1;
     }
-    if (slot_dbg)
-      for (int j = threadIdx.x; j < tab.stride; j += kThreads)
-        slot_dbg[(int64_t)b * tab.stride + j] = -INFINITY;
-    return;
+    brow[threadIdx.x] = r;
+    bcum[threadIdx.x] = cum_in[b0 + threadIdx.x];
   }
-  const int n = tab.row_ptr[r + 1] - tab.row_ptr[r];
-  const float* zb = z + (int64_t)b * ldz;
-  auto zval = [&](int slot, int token) -> float { return TOKEN_IDX ? zb[token] : zb[slot]; };
-  // log-softmax over the legal tokens only
-  float m = -INFINITY;
-  for_each_legal(tab, r, [&](int slot, int token) { m = fmaxf(m, zval(slot, token)); });
-  m = block_max(m, shf);
-  float s = 0.f;
-  for_each_legal(tab, r, [&](int slot, int token) { s += __expf(zval(slot, token) - m); });
-  s = block_sum(s, shf);
-  const float lse = m + __logf(s);
-  const float cum = cum_in[b];
-  if (slot_dbg) {
-    float* dbg = slot_dbg + (int64_t)b * tab.stride;
-    for (int j = threadIdx.x; j < tab.stride; j += kThreads) dbg[j] = -INFINITY;
-    __syncthreads();
-    for_each_legal(tab, r, [&](int slot, int token) { dbg[slot] = zval(slot, token) - lse; });
+  int T, C;
+  const int ex = block_excl_scan<NT>(items, sh, &T);
+  if ((int)threadIdx.x < nloc) pre[threadIdx.x] = ex;
+  block_excl_scan<NT>(cnt, sh, &C);
+  if (threadIdx.x == 0) {
+    pre[nloc] = T;
+    pos = 0;
   }
-  const uint32_t code0 = (uint32_t)(b % k_in) * (uint32_t)tab.stride;
-  auto key_of = [&](int slot, int token) {
-    return make_key(cum + (zval(slot, token) - lse), code0 + (uint32_t)slot);
-  };
-  uint64_t* out = bkeys + (int64_t)b * K;
-  if (threadIdx.x == 0) pos = 0;
   __syncthreads();
-  if (n <= K) {
-    for_each_legal(tab, r, [&](int slot, int token) {
-      const int p = atomicAdd(&pos, 1);
-      if (p < K) out[p] = key_of(slot, token);
-    });
-    if (threadIdx.x == 0) bcount[b] = n;
-    return;
-  }
-  RadixSel sel{0, 0, K};
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    hist[threadIdx.x] = 0;
-    __syncthreads();
-    for_each_legal(tab, r, [&](int slot, int token) {
-      const uint64_t k = key_of(slot, token);
-      if ((k & sel.mask) == sel.prefix) atomicAdd(&hist[(k >> shift) & 0xFF], 1);
-    });
-    __syncthreads();
-    if (radix_narrow(sel, shift, hist, shi)) break;
-  }
-  for_each_legal(tab, r, [&](int slot, int token) {
-    const uint64_t k = key_of(slot, token);
-    if ((k & sel.mask) >= sel.prefix) {
-      const int p = atomicAdd(&pos, 1);
-      if (p < K) out[p] = k;
+  auto beam_of = [&](int f) {  // last beam with pre[b] <= f
+    int lo = 0, hi = nloc;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= f)
+        lo = mid;
+      else
+        hi = mid;
     }
-  });
-  if (threadIdx.x == 0) bcount[b] = K;
-}
+    return lo;
+  };
 
-// ---------------------------------------------------------------- k_request_select
+  // 2. selective projection inside the block
+  if constexpr (MODE == kZScore) {
+    using Sh = SelShape<DT, D>;
+    constexpr int G = Sh::G, NV = Sh::NV, VEC = Sh::VEC, ES = Sh::ES;
+    constexpr int NGB = NT / G;
+    const int gl = threadIdx.x % G, grp = threadIdx.x / G;
+    for (int f = grp; f < T; f += NGB) {
+      const int bl = beam_of(f), j = f - pre[bl], b = b0 + bl;
+      const int token = tab.tok[tab.row_ptr[brow[bl]] + j];
+      const char* hb = (const char*)hidden + (int64_t)b * D * ES;
+      const char* wr = (const char*)W + (int64_t)token * D * ES;
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        float h[VEC], w[VEC];
+        load16<DT>(hb + (int64_t)(c * G + gl) * 16, h);
+        load16<DT>(wr + (int64_t)(c * G + gl) * 16, w);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc = fmaf(w[e], h[e], acc);
+      }
+#pragma unroll
+      for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+      if (gl == 0) z[(int64_t)b * ldz + j] = acc;
+    }
+    __syncthreads();
+  }
 
-constexpr int kMaxSort = 1024;
-
-__device__ void bitonic_sort_desc(uint64_t* a, int P) {
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += kThreads) {
-        const int l = i ^ j;
-        if (l > i) {
-          const uint64_t x = a[i], y = a[l];
-          const bool desc = (i & k) == 0;
-          if (desc ? (x < y) : (x > y)) {
-            a[i] = y;
-            a[l] = x;
+  // 3. legal-only log-sum-exp of every beam, LPB threads per beam (online
+  //    max / sum of exp, fixed order).  When the request's candidates fit in
+  //    LDS, the same pass leaves each one's (z, beam*S + slot) in keys[]:
+  //    sparse at its flat index, dense at an offset from a block scan of the
+  //    threads' legal counts.
+  int LPB = 1;
+  while (LPB < NT && LPB * 2 * max(nloc, 1) <= NT) LPB *= 2;
+  const int bl3 = threadIdx.x / LPB, lb = threadIdx.x - bl3 * LPB;
+  const int r3 = (!MERGE && bl3 < nloc) ? brow[bl3] : -1;
+  bool store = C <= kSelCap;
+  const bool dvec = dense && vec4;
+  const float* z3 = z + (int64_t)(b0 + (bl3 < nloc ? bl3 : 0)) * ldz;
+  const uint32_t* row3 = (dense && r3 >= 0) ? tab.bits + (int64_t)r3 * tab.words : nullptr;
+  const int base3 = (r3 >= 0) ? tab.row_ptr[r3] : 0;
+  const int n3 = (r3 >= 0) ? tab.row_ptr[r3 + 1] - base3 : 0;
+  int at = 0;
+  const int ng = tab.V >> 2;  // float4 groups of a dense row (vector path)
+  constexpr int U = 8;        // loads issued together per thread
+  if (dense && store) {
+    int mine = 0;
+    if (r3 >= 0) {
+      if (dvec) {
+        for (int g0 = lb; g0 < ng; g0 += LPB * U) {
+          uint32_t wv[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int g = g0 + u * LPB;
+            wv[u] = g < ng ? row3[g >> 3] : 0u;
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int g = g0 + u * LPB;
+            mine += __popc((wv[u] >> ((g & 7) * 4)) & 0xFu);
           }
         }
+      } else {
+        for (int v = lb; v < tab.V; v += LPB) mine += (row3[v >> 5] >> (v & 31)) & 1u;
       }
-      __syncthreads();
+    }
+    int tot;
+    at = block_excl_scan<NT>(mine, sh, &tot);
+  } else if (store && bl3 < nloc) {
+    at = pre[bl3];
+  }
+  float m = -INFINITY, s = 0.f;
+  auto add = [&](float zv, uint32_t code, int where) {
+    if (zv > m) {
+      s = s * __expf(m - zv) + 1.f;
+      m = zv;
+    } else {
+      s += __expf(zv - m);
+    }
+    if (store) keys[where] = ((uint64_t)__float_as_uint(zv) << 32) | code;
+  };
+  if (r3 >= 0) {
+    const uint32_t code0 = (uint32_t)(blo + bl3) * S;
+    if (!dense) {
+      for (int j0 = lb; j0 < n3; j0 += LPB * U) {
+        float zv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * LPB;
+          if (j < n3) zv[u] = TOKEN_IDX ? z3[tab.tok[base3 + j]] : z3[j];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int j = j0 + u * LPB;
+          if (j < n3) add(zv[u], code0 + (uint32_t)j, at + j);
+        }
+      }
+    } else if (dvec) {
+      for (int g0 = lb; g0 < ng; g0 += LPB * U) {
+        uint32_t wv[U];
+        float4 zz[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int g = g0 + u * LPB;
+          wv[u] = g < ng ? row3[g >> 3] : 0u;
+          if (g < ng) zz[u] = *(const float4*)(z3 + 4 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int g = g0 + u * LPB;
+          const uint32_t m4 = (wv[u] >> ((g & 7) * 4)) & 0xFu;
+          const uint32_t c4 = code0 + 4u * (uint32_t)g;
+          if (m4 & 1u) add(zz[u].x, c4, at++);
+          if (m4 & 2u) add(zz[u].y, c4 + 1, at++);
+          if (m4 & 4u) add(zz[u].z, c4 + 2, at++);
+          if (m4 & 8u) add(zz[u].w, c4 + 3, at++);
+        }
+      }
+    } else {
+      for (int v = lb; v < tab.V; v += LPB)
+        if ((row3[v >> 5] >> (v & 31)) & 1u) add(z3[v], code0 + (uint32_t)v, at++);
     }
   }
-}
+  if (LPB <= 64) {
+    for (int o = LPB >> 1; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
+    if (lb == 0 && bl3 < nloc) {
+      blse[bl3] = m + __logf(s);
+      bmax[bl3] = m;
+    }
+  } else {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
+    if (lane == 0) {
+      pm[wave] = m;
+      ps[wave] = s;
+    }
+    __syncthreads();
+    const int wpb = LPB >> 6;
+    if ((int)threadIdx.x < nloc) {
+      float mm = pm[threadIdx.x * wpb], ss = ps[threadIdx.x * wpb];
+      for (int i = 1; i < wpb; ++i) lse_combine(mm, ss, pm[threadIdx.x * wpb + i], ps[threadIdx.x * wpb + i]);
+      blse[threadIdx.x] = mm + __logf(ss);
+      bmax[threadIdx.x] = mm;
+    }
+  }
+  __syncthreads();
+  // the request's best key: each beam's best candidate is its max legal z
+  // (cand is monotone in z within a beam), computed with the same operations
+  uint32_t omax = 0;
+  {
+    uint32_t o = 0;
+    if (!MERGE && (int)threadIdx.x < nloc && brow[threadIdx.x] >= 0)
+      o = ord_of(bcum[threadIdx.x] + (bmax[threadIdx.x] - blse[threadIdx.x]));
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) o = max(o, (uint32_t)__shfl_xor((int)o, d));
+    if (lane == 0) sh[wave] = (int)o;
+    __syncthreads();
+    for (int i = 0; i < kSelWaves; ++i) omax = max(omax, (uint32_t)sh[i]);
+    __syncthreads();
+  }
+  if (slot_dbg && !MERGE) {
+    for (int bl = wave; bl < nloc; bl += kSelWaves) {
+      const int b = b0 + bl;
+      const int r = brow[bl];
+      float* dbg = slot_dbg + (int64_t)b * S;
+      const float* zb = z + (int64_t)b * ldz;
+      const int base = r >= 0 ? tab.row_ptr[r] : 0;
+      const int n = r >= 0 ? tab.row_ptr[r + 1] - base : 0;
+      const float l = blse[bl];
+      for (int j = lane; j < (int)S; j += 64) {
+        float v = -INFINITY;
+        if (r >= 0) {
+          if (!dense) {
+            if (j < n) v = (TOKEN_IDX ? zb[tab.tok[base + j]] : zb[j]) - l;
+          } else if ((tab.bits[(int64_t)r * tab.words + (j >> 5)] >> (j & 31)) & 1u) {
+            v = zb[j] - l;
+          }
+        }
+        dbg[j] = v;
+      }
+    }
+  }
 
-__global__ __launch_bounds__(kThreads) void k_request_select(
-    DevTable tab, int32_t t, int32_t L, int32_t k_in, int32_t K,
-    const int32_t* __restrict__ row_in, const uint64_t* __restrict__ bkeys,
-    const int32_t* __restrict__ bcount, int32_t* __restrict__ parent_out,
-    int32_t* __restrict__ token_out, int32_t* __restrict__ row_out, float* __restrict__ cum_out,
-    const int32_t* __restrict__ prefix_in, int32_t* __restrict__ prefix_out) {
-  __shared__ uint64_t sel[kMaxSort];
-  __shared__ int hist[256];
-  __shared__ int shi[kWaves + 1];
-  __shared__ int pos;
-  const int q = blockIdx.x;  // request
-  const int b0 = q * k_in;
-  int mine = 0;
-  for (int i = threadIdx.x; i < k_in; i += kThreads) mine += bcount[b0 + i];
-  const int C = block_sum_i(mine, shi);
-  const int nsel = min(C, K);
-  const int slots = k_in * K;
-  auto for_each_key = [&](auto&& fn) {
-    for (int i = threadIdx.x; i < slots; i += kThreads) {
-      const int bb = i / K, j = i - bb * K;
-      if (j < bcount[b0 + bb]) fn(bkeys[(int64_t)(b0 + bb) * K + j]);
+  if constexpr (MERGE) {
+    // the parts' keys (already final) into LDS, in part order
+    int c = 0;
+    if ((int)threadIdx.x < P) c = part_cnt[q * P + threadIdx.x];
+    const int exp_ = block_excl_scan<NT>(c, sh, &C);
+    if ((int)threadIdx.x < P) pre[threadIdx.x] = exp_;
+    __syncthreads();
+    uint32_t o = 0;
+    for (int f = threadIdx.x; f < P * K; f += NT) {
+      const int pi = f / K, i = f - pi * K;
+      if (i < part_cnt[q * P + pi]) {
+        const uint64_t kk = part_keys[(int64_t)(q * P + pi) * K + i];
+        keys[pre[pi] + i] = kk;
+        o = max(o, (uint32_t)(kk >> 32));
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) o = max(o, (uint32_t)__shfl_xor((int)o, d));
+    if (lane == 0) sh[wave] = (int)o;
+    __syncthreads();
+    omax = 0;
+    for (int i = 0; i < kSelWaves; ++i) omax = max(omax, (uint32_t)sh[i]);
+    store = true;
+    T = C;
+    __syncthreads();
+  }
+
+  // 4. keys: ord(cum + (z - lse)) over ~(beam*S + slot); the K largest.
+  // Log-scaled histogram of each key's distance below the best key's ord:
+  // bins above the boundary bin are taken whole, the boundary bin is resolved
+  // exactly among its own keys.
+  auto bin_of = [&](uint64_t k) { return dist_bin(omax - (uint32_t)(k >> 32)); };
+  for (int i = threadIdx.x; i < kDistBins; i += NT) dhist[i] = 0;
+  __syncthreads();
+  if (MERGE) {
+    if (C > K)
+      for (int i = threadIdx.x; i < C; i += NT) atomicAdd(&dhist[bin_of(keys[i])], 1);
+    __syncthreads();
+  } else if (store) {
+    for (int i = threadIdx.x; i < C; i += NT) {
+      const uint64_t e = keys[i];
+      const uint32_t code = (uint32_t)e;
+      const int bl = (int)(code / S) - blo;
+      const uint64_t k = make_key(bcum[bl] + (__uint_as_float((uint32_t)(e >> 32)) - blse[bl]), code);
+      keys[i] = k;
+      if (C > K) atomicAdd(&dhist[bin_of(k)], 1);
+    }
+    __syncthreads();
+  }
+  // without room in LDS, keys are recomputed from z in every pass
+  auto enumerate = [&](auto&& fn) {
+    for (int f = threadIdx.x; f < T; f += NT) {
+      const int bl = beam_of(f), i = f - pre[bl];
+      const int b = b0 + bl;
+      const int r = brow[bl];
+      const float c = bcum[bl], l = blse[bl];
+      const float* zb = z + (int64_t)b * ldz;
+      const uint32_t code0 = (uint32_t)(blo + bl) * S;
+      if (!dense) {
+        const float zv = TOKEN_IDX ? zb[tab.tok[tab.row_ptr[r] + i]] : zb[i];
+        fn(make_key(c + (zv - l), code0 + (uint32_t)i));
+      } else {
+        uint32_t y = tab.bits[(int64_t)r * tab.words + i];
+        while (y) {
+          const int v = (i << 5) + __ffs(y) - 1;
+          y &= y - 1;
+          fn(make_key(c + (zb[v] - l), code0 + (uint32_t)v));
+        }
+      }
     }
   };
-  if (threadIdx.x == 0) pos = 0;
-  __syncthreads();
+  const int nsel = min(C, K);
   if (C <= K) {
-    for_each_key([&](uint64_t k) {
-      const int p = atomicAdd(&pos, 1);
-      if (p < K) sel[p] = k;
-    });
+    for (int i = threadIdx.x; i < C; i += NT) sel[i] = keys[i];  // C <= K <= kSelCap: stored
   } else {
-    RadixSel rs{0, 0, K};
-    for (int shift = 56; shift >= 0; shift -= 8) {
-      hist[threadIdx.x] = 0;
+    if (!store) {
+      enumerate([&](uint64_t k) { atomicAdd(&dhist[bin_of(k)], 1); });
       __syncthreads();
-      for_each_key([&](uint64_t k) {
-        if ((k & rs.mask) == rs.prefix) atomicAdd(&hist[(k >> shift) & 0xFF], 1);
-      });
-      __syncthreads();
-      if (radix_narrow(rs, shift, hist, shi)) break;
     }
-    for_each_key([&](uint64_t k) {
-      if ((k & rs.mask) >= rs.prefix) {
-        const int p = atomicAdd(&pos, 1);
-        if (p < K) sel[p] = k;
+    // thread i owns bins 2i, 2i+1 (bin order = decreasing key)
+    const int h0 = dhist[2 * threadIdx.x], h1 = dhist[2 * threadIdx.x + 1];
+    int tot;
+    const int ex2 = block_excl_scan<NT>(h0 + h1, sh, &tot);
+    if (ex2 < K && ex2 + h0 + h1 >= K) {
+      if (ex2 + h0 >= K) {
+        pick_bin = 2 * threadIdx.x;
+        pick_above = ex2;
+      } else {
+        pick_bin = 2 * threadIdx.x + 1;
+        pick_above = ex2 + h0;
       }
-    });
+    }
+    if (threadIdx.x == 0) {
+      pos = 0;
+      pos2 = 0;
+    }
+    __syncthreads();
+    const int bstar = pick_bin, above = pick_above, need = K - above;
+    uint64_t* bnd = (uint64_t*)dhist;  // the histogram is done: its space holds the boundary keys
+    if (store) {
+      for (int i0 = 0; i0 < C; i0 += NT) {
+        const int i = i0 + threadIdx.x;
+        const uint64_t k = i < C ? keys[i] : 0ull;
+        const int bn = i < C ? bin_of(k) : kDistBins;
+        if (__ballot(bn <= bstar) == 0) continue;  // wave-uniform: nothing to keep here
+        const int a1 = wave_alloc(bn < bstar ? 1 : 0, &pos);
+        if (bn < bstar && a1 < kMaxK) sel[a1] = k;
+        const int a2 = wave_alloc(bn == bstar ? 1 : 0, &pos2);
+        if (bn == bstar && a2 < kBoundary) bnd[a2] = k;
+      }
+    } else {
+      enumerate([&](uint64_t k) {
+        const int bn = bin_of(k);
+        if (bn < bstar) {
+          const int p = atomicAdd(&pos, 1);
+          if (p < kMaxK) sel[p] = k;
+        }
+        if (bn == bstar) {
+          const int a2 = atomicAdd(&pos2, 1);
+          if (a2 < kBoundary) bnd[a2] = k;
+        }
+      });
+    }
+    __syncthreads();
+    const int nb = pos2;
+    if (nb <= kBoundary) {
+      // exact among the boundary keys: rank = keys above it (keys are distinct)
+      if ((int)threadIdx.x < nb) {
+        const uint64_t k = bnd[threadIdx.x];
+        int rk = 0;
+        for (int j = 0; j < nb; ++j) rk += bnd[j] > k ? 1 : 0;
+        if (rk < need) sel[above + rk] = k;
+      }
+    } else {
+      // very many keys in one bin (e.g. exactly tied scores): radix select
+      // over the full keys of that bin
+      RadixSel rs{0, 0, need};
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+        __syncthreads();
+        auto count = [&](uint64_t k) {
+          if (bin_of(k) == bstar && (k & rs.mask) == rs.prefix) atomicAdd(&hist[(k >> shift) & 0xFF], 1);
+        };
+        if (store) {
+          for (int i = threadIdx.x; i < C; i += NT) count(keys[i]);
+        } else {
+          enumerate(count);
+        }
+        __syncthreads();
+        if (radix_narrow<NT>(rs, shift, hist, sh)) break;
+      }
+      if (threadIdx.x == 0) pos = above;
+      __syncthreads();
+      auto take = [&](uint64_t k) {
+        if (bin_of(k) == bstar && (k & rs.mask) >= rs.prefix) {
+          const int p = atomicAdd(&pos, 1);
+          if (p < kMaxK) sel[p] = k;
+        }
+      };
+      if (store) {
+        for (int i = threadIdx.x; i < C; i += NT) take(keys[i]);
+      } else {
+        enumerate(take);
+      }
+    }
   }
   __syncthreads();
-  int P = 1;
-  while (P < K) P <<= 1;
-  for (int i = nsel + threadIdx.x; i < P; i += kThreads) sel[i] = 0;  // 0 sorts last
+
+  if (!MERGE && P > 1) {
+    // a part: its best keys go to the merge unsorted
+    for (int i = threadIdx.x; i < nsel; i += NT) part_keys[(int64_t)blockIdx.x * K + i] = sel[i];
+    if (threadIdx.x == 0) part_cnt[blockIdx.x] = nsel;
+    return;
+  }
+
+  // 5. sorted position of a selected key = number of selected keys above it
+  uint64_t mine = 0;
+  int rank = 0;
+  if ((int)threadIdx.x < nsel) {
+    mine = sel[threadIdx.x];
+    for (int j = 0; j < nsel; ++j) rank += sel[j] > mine ? 1 : 0;
+  }
   __syncthreads();
-  bitonic_sort_desc(sel, P);
-  const uint32_t S = (uint32_t)tab.stride;
-  for (int o = threadIdx.x; o < K; o += kThreads) {
+  if ((int)threadIdx.x < nsel) keys[rank] = mine;
+  __syncthreads();
+  for (int o = threadIdx.x; o < K; o += NT) {
     const int64_t oi = (int64_t)q * K + o;
     if (o < nsel) {
-      const uint64_t key = sel[o];
+      const uint64_t key = keys[o];
       const uint32_t code = 0xFFFFFFFFu - (uint32_t)key;
       const int bl = (int)(code / S);
       const int slot = (int)(code - (uint32_t)bl * S);
       const int b = b0 + bl;
-      const int r = row_in[b];
+      const int r = brow[bl];
       int token, next;
-      if (tab.fmt == ZGR_FMT_SPARSE) {
-        next = tab.row_ptr[r] + slot;
+      if (!dense) {
+        next = tab.row_ptr[r] + slot;  // the entry's position is its next row
         token = tab.tok[next];
       } else {
         token = slot;
-        const uint32_t* row = tab.bits + (int64_t)r * tab.words;
-        int below = 0;
-        const int wfull = slot >> 5;
-        for (int w = 0; w < wfull; ++w) below += __popc(row[w]);
-        below += __popc(row[wfull] & ((1u << (slot & 31)) - 1u));
-        next = tab.row_ptr[r] + below;
+        // entries of the row before this token: the rank directory gives the
+        // count before its word, popcount the rest of the word
+        const int64_t w = (int64_t)r * tab.words + (slot >> 5);
+        next = tab.row_ptr[r] + tab.rank[w] + __popc(tab.bits[w] & ((1u << (slot & 31)) - 1u));
       }
       parent_out[oi] = b;
       token_out[oi] = token;
@@ -694,6 +1016,67 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
     }
 }
 
+// ---------------------------------------------------------------- k_gemm_small (MFMA 16x16)
+
+// Full projection for few beams (the first step has one beam per request):
+// 32x32 output tiles per block, one 16x16 MFMA tile per wave over the whole
+// hidden size, operands streamed from global memory with 16-byte loads (the
+// four 16-lane groups of a wave cover 64 contiguous bytes of each row).  The
+// k order inside a 64-byte chunk is permuted identically for both operands.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict__ A,
+                                                         const void* __restrict__ Bm,
+                                                         float* __restrict__ C, int32_t M,
+                                                         int32_t N, int32_t D, int64_t ldc) {
+  constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nbn = (N + 31) / 32;
+  const int tm = blockIdx.x / nbn, tn = blockIdx.x - tm * nbn;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int m = tm * 32 + (wave >> 1) * 16 + l16;
+  const int n = tn * 32 + (wave & 1) * 16 + l16;
+  const int64_t rowbytes = (int64_t)D * ES;
+  const char* ap = (const char*)A + (int64_t)min(m, M - 1) * rowbytes + g * 16;
+  const char* bp = (const char*)Bm + (int64_t)min(n, N - 1) * rowbytes + g * 16;
+  const int nch = (int)(rowbytes / 64);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nch; c += U) {
+    uint4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c + u < nch) {
+        a[u] = *(const uint4*)(ap + (int64_t)(c + u) * 64);
+        b[u] = *(const uint4*)(bp + (int64_t)(c + u) * 64);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (c + u >= nch) break;
+      if constexpr (DT == ZGR_F32) {
+        const f32x4 av = __builtin_bit_cast(f32x4, a[u]);
+        const f32x4 bv = __builtin_bit_cast(f32x4, b[u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], acc, 0, 0, 0);
+      } else if constexpr (DT == ZGR_BF16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[u]),
+                                                      __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a[u]),
+                                                     __builtin_bit_cast(f16x8, b[u]), acc, 0, 0, 0);
+      }
+    }
+  }
+  // 16x16 accumulator layout: lane -> column l16, register v -> row 4*g + v
+  if (n < N) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = tm * 32 + (wave >> 1) * 16 + 4 * g + v;
+      if (row < M) C[(int64_t)row * ldc + n] = acc[v];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- decode helpers
 
 __global__ void k_decode_init(int32_t* row, float* cum, int32_t B, int32_t K) {
@@ -741,6 +1124,21 @@ hipError_t launch_sel_d(const StepArgs& a, hipStream_t s) {
   }
 }
 
+template <int DT>
+hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
+  const int V = a.tab.V;
+  const int nbm = (a.M + kTileM - 1) / kTileM, nbn = (V + kTileN - 1) / kTileN;
+  if (nbm * nbn < a.n_cu) {
+    const int grid = ((a.M + 31) / 32) * ((V + 31) / 32);
+    hipLaunchKernelGGL(k_gemm_small<DT>, dim3(grid), dim3(kThreads), 0, s, a.hidden, a.W, a.z, a.M, V,
+                       a.d, a.ldz);
+  } else {
+    hipLaunchKernelGGL(k_gemm_nt<DT>, dim3(nbm * nbn), dim3(kThreads), 0, s, a.hidden, a.W, a.z, a.M,
+                       V, a.d, a.ldz);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool supported_hidden_size(int d) {
@@ -748,11 +1146,13 @@ bool supported_hidden_size(int d) {
          d == 4096;
 }
 
-hipError_t launch_selective_score(const StepArgs& a, hipStream_t s) {
+hipError_t launch_units(const StepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_units, dim3(1), dim3(1024), 0, s, a.row_in, a.M, a.tab, a.nlegal,
                      a.unit_start, a.err);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_selective_score(const StepArgs& a, hipStream_t s) {
   switch (a.dtype) {
     case ZGR_F32: return launch_sel_d<ZGR_F32>(a, s);
     case ZGR_BF16: return launch_sel_d<ZGR_BF16>(a, s);
@@ -762,43 +1162,67 @@ hipError_t launch_selective_score(const StepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_full_projection(const StepArgs& a, hipStream_t s) {
-  const int V = a.tab.V;
-  const int nbm = (a.M + kTileM - 1) / kTileM, nbn = (V + kTileN - 1) / kTileN;
-  const dim3 grid(nbm * nbn);
   switch (a.dtype) {
-    case ZGR_F32:
-      hipLaunchKernelGGL(k_gemm_nt<ZGR_F32>, grid, dim3(kThreads), 0, s, a.hidden, a.W, a.z, a.M, V,
-                         a.d, a.ldz);
-      break;
-    case ZGR_BF16:
-      hipLaunchKernelGGL(k_gemm_nt<ZGR_BF16>, grid, dim3(kThreads), 0, s, a.hidden, a.W, a.z, a.M, V,
-                         a.d, a.ldz);
-      break;
-    case ZGR_F16:
-      hipLaunchKernelGGL(k_gemm_nt<ZGR_F16>, grid, dim3(kThreads), 0, s, a.hidden, a.W, a.z, a.M, V,
-                         a.d, a.ldz);
-      break;
+    case ZGR_F32: return launch_proj_typed<ZGR_F32>(a, s);
+    case ZGR_BF16: return launch_proj_typed<ZGR_BF16>(a, s);
+    case ZGR_F16: return launch_proj_typed<ZGR_F16>(a, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+#define ZGR_STEP_ARGS                                                                            \
+  a.tab, a.t, a.L, a.k_in, a.K, a.row_in, a.cum_in, a.hidden, a.W, a.z, a.ldz, vec4, a.parts,      \
+      a.part_keys, a.part_cnt, a.parent_out, a.token_out, a.row_out, a.cum_out, a.prefix_in,       \
+      a.prefix_out, a.slot_dbg, a.err
+
+template <int DT, int D>
+hipError_t launch_scored_step(const StepArgs& a, int vec4, hipStream_t s) {
+  hipLaunchKernelGGL((k_request_step<kZScore, DT, D>), dim3(a.B * a.parts), dim3(kSelThreads), 0, s,
+                     ZGR_STEP_ARGS);
   return hipGetLastError();
 }
 
-hipError_t launch_beam_reduce(const StepArgs& a, bool token_indexed, hipStream_t s) {
-  if (token_indexed)
-    hipLaunchKernelGGL(k_beam_reduce<true>, dim3(a.M), dim3(kThreads), 0, s, a.tab, a.M, a.k_in, a.K,
-                       a.row_in, a.cum_in, a.z, a.ldz, a.slot_dbg, a.bkeys, a.bcount, a.err);
-  else
-    hipLaunchKernelGGL(k_beam_reduce<false>, dim3(a.M), dim3(kThreads), 0, s, a.tab, a.M, a.k_in, a.K,
-                       a.row_in, a.cum_in, a.z, a.ldz, a.slot_dbg, a.bkeys, a.bcount, a.err);
-  return hipGetLastError();
+template <int DT>
+hipError_t launch_scored_step_d(const StepArgs& a, int vec4, hipStream_t s) {
+  switch (a.d) {
+    case 64: return launch_scored_step<DT, 64>(a, vec4, s);
+    case 128: return launch_scored_step<DT, 128>(a, vec4, s);
+    case 256: return launch_scored_step<DT, 256>(a, vec4, s);
+    case 512: return launch_scored_step<DT, 512>(a, vec4, s);
+    case 768: return launch_scored_step<DT, 768>(a, vec4, s);
+    case 1024: return launch_scored_step<DT, 1024>(a, vec4, s);
+    case 2048: return launch_scored_step<DT, 2048>(a, vec4, s);
+    case 4096: return launch_scored_step<DT, 4096>(a, vec4, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
-hipError_t launch_request_select(const StepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_request_select, dim3(a.B), dim3(kThreads), 0, s, a.tab, a.t, a.L, a.k_in, a.K,
-                     a.row_in, a.bkeys, a.bcount, a.parent_out, a.token_out, a.row_out, a.cum_out,
-                     a.prefix_in, a.prefix_out);
+hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s) {
+  const int vec4 = (a.ldz % 4 == 0 && a.tab.V % 4 == 0) ? 1 : 0;
+  const dim3 grid(a.B * a.parts);
+  hipError_t e = hipSuccess;
+  if (zmode == kZScore) {
+    switch (a.dtype) {
+      case ZGR_F32: e = launch_scored_step_d<ZGR_F32>(a, vec4, s); break;
+      case ZGR_BF16: e = launch_scored_step_d<ZGR_BF16>(a, vec4, s); break;
+      case ZGR_F16: e = launch_scored_step_d<ZGR_F16>(a, vec4, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (zmode == kZToken) {
+    hipLaunchKernelGGL((k_request_step<kZToken, ZGR_F32, 64>), grid, dim3(kSelThreads), 0, s,
+                       ZGR_STEP_ARGS);
+    e = hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((k_request_step<kZSlot, ZGR_F32, 64>), grid, dim3(kSelThreads), 0, s,
+                       ZGR_STEP_ARGS);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess || a.parts == 1) return e;
+  hipLaunchKernelGGL((k_request_step<kZParts, ZGR_F32, 64>), dim3(a.B), dim3(kSelThreads), 0, s,
+                     ZGR_STEP_ARGS);
   return hipGetLastError();
 }
+#undef ZGR_STEP_ARGS
 
 hipError_t launch_decode_init(int32_t* row, float* cum, int32_t B, int32_t K, hipStream_t s) {
   const int n = B * K;
