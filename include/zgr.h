@@ -232,14 +232,18 @@ int32_t zgr_plan_status(zgr_plan* plan, void* stream);
 #define ZGR_KERNEL_GEMM 2       /* full projection on MFMA */
 #define ZGR_KERNEL_REQUEST 3    /* per request: legal-only log-softmax, cumulative add, top-K,
                                    next rows, prefixes (and, on light sparse steps, the
-                                   selective projection itself) */
+                                   selective projection itself); a request split over several
+                                   blocks adds a second, merging dispatch */
 #define ZGR_KERNEL_COUNT 4
 
-/* Turn per-kernel timing on (enable != 0) or off and reset the counters.
- * While on, zgr_step / zgr_decode bracket every kernel launch with two HIP
- * events on the launch stream (this adds a little time per launch; do not
- * capture such launches into graphs).  Errors: ZGR_E_ARG, ZGR_E_HIP. */
-int32_t zgr_plan_profile(zgr_plan* plan, int32_t enable);
+/* Per-kernel timing: repeat > 0 turns it on, 0 off; counters are reset.
+ * While on, every kernel launch of zgr_step / zgr_decode is issued `repeat`
+ * times back to back between two HIP events on the launch stream and the
+ * bracket's duration divided by `repeat` is recorded (the step kernels are
+ * idempotent, so results are unchanged; repeat > 1 amortises the events'
+ * own cost for short kernels).  Do not capture such launches into graphs.
+ * Errors: ZGR_E_ARG (repeat outside [0, 1000]), ZGR_E_HIP. */
+int32_t zgr_plan_profile(zgr_plan* plan, int32_t repeat);
 
 /* Synchronise on the recorded events and return, for kernel class `kernel`
  * at step t, the number of timed launches and their summed duration (ms).

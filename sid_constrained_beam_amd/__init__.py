@@ -338,8 +338,9 @@ def zgr_plan_status(plan: Plan, stream=None):
     _check(lib().zgr_plan_status(plan.handle, _stream_ptr(stream)))
 
 
-def zgr_plan_profile(plan: Plan, enable: bool):
-    _check(lib().zgr_plan_profile(plan.handle, 1 if enable else 0))
+def zgr_plan_profile(plan: Plan, repeat: int):
+    """repeat > 0: time every launch, issued `repeat` times between two events; 0: off."""
+    _check(lib().zgr_plan_profile(plan.handle, int(repeat)))
 
 
 def zgr_plan_profile_read(plan: Plan, kernel, t: int):

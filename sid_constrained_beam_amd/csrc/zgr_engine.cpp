@@ -63,9 +63,9 @@ struct zgr_plan {
   // optional per-kernel timing: HIP events recorded around each launch on its stream
   struct ProfRec {
     hipEvent_t a, b;
-    int kernel, t;
+    int kernel, t, repeat;
   };
-  bool profiling = false;
+  int profiling = 0;  // launches per timed bracket (0 = timing off)
   std::vector<ProfRec> pending;
   std::vector<hipEvent_t> pool;
   double prof_ms[ZGR_KERNEL_COUNT][zgr::kMaxL] = {};
@@ -167,16 +167,19 @@ hipEvent_t prof_event(zgr_plan* p) {
   return e;
 }
 
-// Launch through fn, bracketed by two events when profiling is on.
+// Launch through fn; when timing is on, the launch is issued `profiling`
+// times back to back between two events (every kernel of a step is
+// idempotent: it only reads its inputs and overwrites its outputs).
 template <class F>
 hipError_t prof_launch(zgr_plan* p, int kernel, int t, hipStream_t s, F&& fn) {
-  if (!p->profiling) return fn();
+  if (p->profiling <= 0) return fn();
   hipEvent_t a = prof_event(p), b = prof_event(p);
   if (!a || !b) return fn();
   (void)hipEventRecord(a, s);
-  const hipError_t e = fn();
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < p->profiling && e == hipSuccess; ++i) e = fn();
   (void)hipEventRecord(b, s);
-  p->pending.push_back({a, b, kernel, t});
+  p->pending.push_back({a, b, kernel, t, p->profiling});
   return e;
 }
 
@@ -186,7 +189,7 @@ int32_t prof_flush(zgr_plan* p) {
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize (profiling)");
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
-      p->prof_ms[r.kernel][r.t - 1] += ms;
+      p->prof_ms[r.kernel][r.t - 1] += ms / r.repeat;
       p->prof_n[r.kernel][r.t - 1] += 1;
     }
     p->pool.push_back(r.a);
@@ -247,6 +250,10 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
   a.parts = request_parts(p, a, zmode);
   e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
   if (e != hipSuccess) return hip_fail(e, "request step launch");
+  if (a.parts > 1) {
+    e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_merge(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "request merge launch");
+  }
   return ZGR_OK;
 }
 
@@ -499,11 +506,12 @@ int32_t zgr_plan_set_choice(zgr_plan* p, int32_t t, int32_t proj) {
   return ZGR_OK;
 }
 
-int32_t zgr_plan_profile(zgr_plan* p, int32_t enable) {
+int32_t zgr_plan_profile(zgr_plan* p, int32_t repeat) {
   if (!p) return fail(ZGR_E_ARG, "zgr_plan_profile: null plan");
+  if (repeat < 0 || repeat > 1000) return fail(ZGR_E_ARG, "zgr_plan_profile: repeat must be in [0, 1000]");
   const int32_t rc = prof_flush(p);
   if (rc != ZGR_OK) return rc;
-  p->profiling = enable != 0;
+  p->profiling = repeat;
   std::memset(p->prof_ms, 0, sizeof(p->prof_ms));
   std::memset(p->prof_n, 0, sizeof(p->prof_n));
   return ZGR_OK;

@@ -101,6 +101,8 @@ hipError_t launch_full_projection(const StepArgs& a, hipStream_t s);
 // With a.parts > 1 each request is split over a.parts blocks, then merged.
 constexpr int kMaxParts = 16;
 hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s);
+// after launch_request_step with a.parts > 1: the per-request merge of the parts
+hipError_t launch_request_merge(const StepArgs& a, hipStream_t s);
 hipError_t launch_decode_init(int32_t* row, float* cum, int32_t B, int32_t K, hipStream_t s);
 hipError_t launch_decode_final(const int32_t* row, const float* cum, const int32_t* prefix,
                                int32_t B, int32_t K, int32_t L, int32_t top_k, int64_t* item_out,

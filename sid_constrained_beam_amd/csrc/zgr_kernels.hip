@@ -1217,7 +1217,11 @@ hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s) {
                        ZGR_STEP_ARGS);
     e = hipGetLastError();
   }
-  if (e != hipSuccess || a.parts == 1) return e;
+  return e;
+}
+
+hipError_t launch_request_merge(const StepArgs& a, hipStream_t s) {
+  const int vec4 = 0;
   hipLaunchKernelGGL((k_request_step<kZParts, ZGR_F32, 64>), dim3(a.B), dim3(kSelThreads), 0, s,
                      ZGR_STEP_ARGS);
   return hipGetLastError();

@@ -273,3 +273,29 @@ def test_callback_failure_reported():
     with pytest.raises(zgr.ZgrError) as e:
         zgr.zgr_decode(plan, lambda *a: 3, cfg.K, item)
     assert e.value.status == zgr.ZGR_E_CALLBACK
+
+
+def test_profiled_launches_keep_results():
+    """Timing mode repeats each (idempotent) launch between events: the decode's
+    results are unchanged and every step records its kernels."""
+    import torch
+    s = setup_of("n1e6_v2048")
+    cfg = s.cfg
+    plan = s.plan(force=["full", "full", "selective"])
+    outs = []
+    for repeat in (0, 3):
+        zgr.zgr_plan_profile(plan, repeat)
+        item = torch.empty(cfg.B * cfg.K, dtype=torch.int64, device="cuda")
+        sc = torch.empty(cfg.B * cfg.K, dtype=torch.float32, device="cuda")
+        zgr.zgr_decode(plan, s.hidden_source(0), cfg.K, item, None, sc)
+        outs.append((item.cpu().numpy(), sc.cpu().numpy()))
+        if repeat:
+            for t in range(1, cfg.L + 1):
+                n, ms = zgr.zgr_plan_profile_read(plan, "request", t)
+                assert n >= 1 and ms > 0
+            assert zgr.zgr_plan_profile_read(plan, "gemm", 1)[0] == 1
+            assert zgr.zgr_plan_profile_read(plan, "gemm", 3)[0] == 0
+    zgr.zgr_plan_profile(plan, 0)
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    with pytest.raises(zgr.ZgrError):
+        zgr.zgr_plan_profile(plan, -1)
