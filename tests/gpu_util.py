@@ -132,34 +132,42 @@ def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True):
         cum_out=torch.empty(B * K, dtype=torch.float32, device="cuda"),
     )
     S = setup.stats[t - 1]["stride"]
-    dbg = torch.empty(M * S, dtype=torch.float32, device="cuda") if with_dbg else None
+    dbg = torch.empty(M * S, dtype=torch.float32, device="cuda") if with_dbg is not False else None
     zgr.zgr_step(plan, t, dev["hidden"], dev["row_in"], dev["cum_in"], k_in, dev["parent"],
                  dev["token"], dev["row_out"], dev["cum_out"], dbg)
     zgr.zgr_plan_status(plan)
     out = {k: dev[k].cpu().numpy() for k in ("parent", "token", "row_out", "cum_out")}
-    out["dbg"] = dbg.cpu().numpy().reshape(M, S) if with_dbg else None
+    if with_dbg is True:
+        out["dbg"] = dbg.cpu().numpy().reshape(M, S)
+    elif with_dbg:
+        # only the rows of the listed requests (full-size workloads)
+        d2 = dbg.view(M, S)
+        out["dbg"] = {q: d2[q * k_in:(q + 1) * k_in].cpu().numpy() for q in with_dbg}
+    else:
+        out["dbg"] = None
     out["h32"] = h32
     out["rows"] = rows
     return out
 
 
-def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True):
-    """Step check against the oracle on identical inputs.  Returns the number of
-    requests whose K-th score boundary was ambiguous."""
+def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests=None):
+    """Step check against the oracle on identical inputs (all requests, or the
+    listed ones).  Returns the number of requests whose K-th score boundary
+    was ambiguous."""
     cfg = setup.cfg
     M = len(cum)
     k_in = M // B
     st = setup.stats[t - 1]
     dense = st["fmt"] == zgr.ZGR_FMT_DENSE
     ambiguous = 0
-    for q in range(B):
+    for q in (range(B) if requests is None else requests):
         sl = slice(q * k_in, (q + 1) * k_in)
         pq = prefixes[sl, : t - 1] if t > 1 else np.zeros((k_in, 0), np.int32)
         cq = np.asarray(cum[sl], np.float64)
         res = setup.cat.step(t, setup.W_f32[t - 1], pq, cq, out["h32"][sl], K)
         # (i) legal slots and their log-probs
         if check_dbg and out["dbg"] is not None:
-            dbg = out["dbg"][sl]
+            dbg = out["dbg"][q] if isinstance(out["dbg"], dict) else out["dbg"][sl]
             for k in range(k_in):
                 m = res.cand_beam == k
                 toks = res.cand_token[m]
