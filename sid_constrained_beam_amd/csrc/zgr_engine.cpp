@@ -213,15 +213,17 @@ bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
 // many (a dense or full-projection step, or a heavy sparse one) is split over
 // several blocks so that more compute units stream its scores, then merged;
 // light requests stay whole (one launch).
-int32_t request_parts(const zgr_plan* p, const StepArgs& a, int zmode) {
+int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool heavy_step) {
   if (a.k_in < 2) return 1;
   const HostTable& h = p->idx->host[a.t - 1];
   const double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
   const double est_c = a.k_in * std::min<double>(mean_n, h.stride);
-  const bool heavy = (zmode == 0) || est_c > 2048.0;
-  if (!heavy) return 1;
+  if (!heavy_step && est_c <= 2048.0) return 1;
+  // enough parts to cover the compute units, and enough that a part's
+  // candidates (estimated) fit the LDS key array
   int P = std::max(1, p->n_cu / std::max(1, a.B));
-  P = std::min({P, a.k_in, kMaxParts, 14336 / std::max(1, a.K)});
+  P = std::max(P, (int)std::ceil(est_c / (0.75 * kSelCapHost)));
+  P = std::min({P, a.k_in, kMaxParts, kSelCapHost / std::max(1, a.K)});
   return std::max(1, P);
 }
 
@@ -231,11 +233,13 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
   const int t = a.t;
   hipError_t e;
   int zmode;
+  // z layout: by legal rank on dense steps and on selective sparse steps,
+  // token-indexed after a full projection of a sparse step
   if (proj == ZGR_PROJ_FULL) {
     a.ldz = p->V;
     e = prof_launch(p, ZGR_KERNEL_GEMM, t, s, [&] { return launch_full_projection(a, s); });
     if (e != hipSuccess) return hip_fail(e, "full projection launch");
-    zmode = 0;
+    zmode = dense ? 1 : 0;
   } else if (!dense && light_sparse_step(p, a)) {
     a.ldz = a.tab.stride;
     zmode = 2;
@@ -245,9 +249,9 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     if (e != hipSuccess) return hip_fail(e, "unit count launch");
     e = prof_launch(p, ZGR_KERNEL_SELECTIVE, t, s, [&] { return launch_selective_score(a, s); });
     if (e != hipSuccess) return hip_fail(e, "selective score launch");
-    zmode = dense ? 0 : 1;  // z is token-indexed on dense steps
+    zmode = 1;
   }
-  a.parts = request_parts(p, a, zmode);
+  a.parts = request_parts(p, a, proj == ZGR_PROJ_FULL || dense);
   e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
   if (e != hipSuccess) return hip_fail(e, "request step launch");
   if (a.parts > 1) {

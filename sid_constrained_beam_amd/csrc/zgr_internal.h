@@ -99,7 +99,8 @@ hipError_t launch_selective_score(const StepArgs& a, hipStream_t s);
 hipError_t launch_full_projection(const StepArgs& a, hipStream_t s);
 // zmode: 0 = z token-indexed, 1 = z slot-indexed, 2 = score inside the request kernel.
 // With a.parts > 1 each request is split over a.parts blocks, then merged.
-constexpr int kMaxParts = 16;
+constexpr int kMaxParts = 32;
+constexpr int kSelCapHost = 14336;  // candidates whose keys fit the request kernel's LDS
 hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s);
 // after launch_request_step with a.parts > 1: the per-request merge of the parts
 hipError_t launch_request_merge(const StepArgs& a, hipStream_t s);

@@ -21,7 +21,8 @@
 //                      dense: set bits of the row's bitmap) and computes
 //                      z = W_t[token] . h_beam with the weight row read in place
 //                      by a group of lanes (16-byte loads), h kept in registers,
-//                      a lane-group shuffle reduction, z stored at the slot.
+//                      a lane-group shuffle reduction, z stored at the slot
+//                      (sparse: rank j; dense: the token's legal rank).
 //   k_gemm_nt          full projection Z = H . W_t^T on MFMA (fp32, bf16, f16
 //                      inputs; fp32 accumulate), Z row = beam, column = token;
 //   k_gemm_small       the same product for few beams (first step): 16x16 MFMA.
@@ -278,6 +279,7 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
   using S = SelShape<DT, D>;
   constexpr int G = S::G, NV = S::NV, VEC = S::VEC, NG = S::NG, ES = S::ES;
   __shared__ uint16_t lst[kDenseTile];
+  __shared__ int lpos[kDenseTile];
   __shared__ int lst_count;
   const int gl = threadIdx.x % G;   // lane within the candidate group
   const int grp = threadIdx.x / G;  // group within the block
@@ -331,6 +333,7 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       __syncthreads();  // previous unit's readers are done with lst
       if (threadIdx.x < 64) {
         const uint32_t word = (lane < nw) ? tab.bits[(int64_t)r * tab.words + w0 + lane] : 0u;
+        int rk = (lane < nw) ? (int)tab.rank[(int64_t)r * tab.words + w0 + lane] : 0;
         const int pc = __popc(word);
         const int incl = wave_incl_scan(pc);
         int pos = incl - pc;
@@ -338,16 +341,14 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
         while (x) {
           const int k = __ffs(x) - 1;
           x &= x - 1;
-          lst[pos++] = (uint16_t)(v0 + lane * 32 + k);
+          lst[pos] = (uint16_t)(v0 + lane * 32 + k);
+          lpos[pos++] = rk++;  // z of a dense row is stored by legal rank
         }
         if (lane == 63) lst_count = incl;
       }
       __syncthreads();
       const int cnt = lst_count;
-      for (int i = grp; i < cnt; i += NG) {
-        const int v = lst[i];
-        score(v, v);
-      }
+      for (int i = grp; i < cnt; i += NG) score(lst[i], lpos[i]);
     }
   }
 }
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelCap = 14336;  // candidates of a request whose keys fit in LDS (112 KiB)
+constexpr int kSelCap = kSelCapHost;  // candidates of a request whose keys fit in LDS (112 KiB)
 constexpr int kMaxK = 1024;
 
 // Distance histogram: 64 exact bins for distances below 64 ulps, then 64
@@ -398,47 +399,55 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
   m = mn;
 }
 
-// One block per request, the whole step after scoring:
-//   1. each beam's legal count (its row of table t) and a prefix over the
-//      request's beams (candidate f of the request = beam, rank);
+// One block per request (or per part of a request), the step after scoring:
+//   1. each beam's row of table t, legal count and row base; prefixes over the
+//      block's beams of candidates (candidate f = beam, legal rank) and of
+//      work items (sparse: candidates; dense: bitmap words);
 //   2. (kZScore) z = W_t[token] . h_beam for every legal candidate, the weight
-//      row read in place by a lane group, z stored at the beam's slot;
+//      row read in place by a lane group;
 //   3. legal-only log-sum-exp of every beam (online max / sum of exp, fixed
-//      order; several waves per beam when the request has few beams);
+//      order; several waves per beam when the block has few beams); when the
+//      block's candidates fit in LDS the same pass leaves each one's
+//      (z, beam*S + slot) in keys[] at its flat index;
 //   4. cand = cum + (z - lse) as a 64-bit key (ord(cand), ~(beam*S + slot));
-//      the K largest by radix select (in LDS up to 16384 candidates, else by
-//      passes over z);
-//   5. sorted by rank counting, decoded and advanced: next row = row_ptr[r] +
-//      slot (sparse: the position is the next row) or row_ptr[r] + rank
-//      directory + popcount (dense); prefixes gathered by parent.
+//      the K largest through a distance histogram (in LDS, or by passes over
+//      z when they do not fit);
+//   5. a part hands its best K to the merge; otherwise sort by rank counting,
+//      decode and advance: next row = row_ptr[r] + slot (sparse: the position
+//      is the next row) or row_ptr[r] + legal rank (dense); prefix gather.
+// Scores z[b][j] are stored by legal rank j on sparse selective steps and on
+// every dense step; after a full projection of a sparse step they are
+// token-indexed (kZToken).  On dense rows the token of rank j is the row's
+// j-th set bit; the rank directory gives each word's first rank.
 template <int MODE, int DT, int D>
 __global__ __launch_bounds__(kSelThreads) void k_request_step(
     DevTable tab, int32_t t, int32_t L, int32_t k_in, int32_t K, const int32_t* __restrict__ row_in,
     const float* __restrict__ cum_in, const void* __restrict__ hidden, const void* __restrict__ W,
-    float* __restrict__ z, int64_t ldz, int32_t vec4, int32_t P, uint64_t* __restrict__ part_keys,
+    float* __restrict__ z, int64_t ldz, int32_t P, uint64_t* __restrict__ part_keys,
     int32_t* __restrict__ part_cnt, int32_t* __restrict__ parent_out,
     int32_t* __restrict__ token_out, int32_t* __restrict__ row_out, float* __restrict__ cum_out,
     const int32_t* __restrict__ prefix_in, int32_t* __restrict__ prefix_out,
     float* __restrict__ slot_dbg, int32_t* __restrict__ err) {
   constexpr int NT = kSelThreads;
   constexpr bool TOKEN_IDX = (MODE == kZToken);
+  constexpr bool MERGE = (MODE == kZParts);
   __shared__ uint64_t keys[kSelCap];
   __shared__ uint64_t sel[kMaxK];
-  __shared__ int pre[kMaxK + 1];
+  __shared__ int pre[kMaxK + 1];   // work-item prefix over the block's beams
+  __shared__ int cpre[kMaxK + 1];  // candidate prefix over the block's beams
   __shared__ int brow[kMaxK];
+  __shared__ int bbase[kMaxK];
   __shared__ float bcum[kMaxK];
   __shared__ float blse[kMaxK];
-  __shared__ float bmax[kMaxK];
   __shared__ float pm[kSelWaves], ps[kSelWaves];
   __shared__ __attribute__((aligned(16))) int dhist[kDistBins];
   __shared__ int hist[256];
   __shared__ int sh[kSelWaves];
-  __shared__ uint64_t sh64[kSelWaves];
   __shared__ int pos, pos2, pick_bin, pick_above;
+  __shared__ unsigned int omax_sh;
   // P > 1: block (q, p) takes beams [blo, blo + nloc) of request q and
   // leaves its best K keys in part_keys; the merge (MODE kZParts) picks the
   // request's best K among the parts' keys.
-  constexpr bool MERGE = (MODE == kZParts);
   const int q = MERGE ? blockIdx.x : blockIdx.x / P;
   const int part = MERGE ? 0 : blockIdx.x - q * P;
   const int kp = (k_in + P - 1) / P;
@@ -449,200 +458,205 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   const uint32_t S = (uint32_t)tab.stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // 1. the request's beams: row (-1 when dead), cumulative score, legal count,
-  //    work items (sparse: candidates; dense: bitmap words)
+  // 1. the block's beams
   int cnt = 0, items = 0;
   if ((int)threadIdx.x < nloc) {
     int r = row_in[b0 + threadIdx.x];
+    int base = 0;
     if (r >= 0 && r < tab.rows) {
-      cnt = MERGE ? 0 : tab.row_ptr[r + 1] - tab.row_ptr[r];
+      base = tab.row_ptr[r];
+      cnt = MERGE ? 0 : tab.row_ptr[r + 1] - base;
       items = dense ? (cnt > 0 ? tab.words : 0) : cnt;
     } else {
       if (r >= tab.rows && !MERGE) atomicOr(err, 1);
       r = -1;
     }
     brow[threadIdx.x] = r;
+    bbase[threadIdx.x] = base;
     bcum[threadIdx.x] = cum_in[b0 + threadIdx.x];
   }
   int T, C;
   const int ex = block_excl_scan<NT>(items, sh, &T);
   if ((int)threadIdx.x < nloc) pre[threadIdx.x] = ex;
-  block_excl_scan<NT>(cnt, sh, &C);
+  const int exc = block_excl_scan<NT>(cnt, sh, &C);
+  if ((int)threadIdx.x < nloc) cpre[threadIdx.x] = exc;
   if (threadIdx.x == 0) {
     pre[nloc] = T;
+    cpre[nloc] = C;
     pos = 0;
+    omax_sh = 0u;
   }
   __syncthreads();
-  auto beam_of = [&](int f) {  // last beam with pre[b] <= f
+  auto beam_of = [&](const int* pf, int f) {  // last beam with pf[b] <= f
     int lo = 0, hi = nloc;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= f)
+      if (pf[mid] <= f)
         lo = mid;
       else
         hi = mid;
     }
     return lo;
   };
+  bool store = C <= kSelCap;
 
-  // 2. selective projection inside the block
+  // 2. selective projection inside the block: U2 candidates per lane group
+  //    with their token and row loads issued together; z goes to its slot and,
+  //    when the block's candidates fit in LDS, to keys[] as (z, beam*S + slot)
   if constexpr (MODE == kZScore) {
     using Sh = SelShape<DT, D>;
     constexpr int G = Sh::G, NV = Sh::NV, VEC = Sh::VEC, ES = Sh::ES;
     constexpr int NGB = NT / G;
+    constexpr int U2 = 2;
     const int gl = threadIdx.x % G, grp = threadIdx.x / G;
-    for (int f = grp; f < T; f += NGB) {
-      const int bl = beam_of(f), j = f - pre[bl], b = b0 + bl;
-      const int token = tab.tok[tab.row_ptr[brow[bl]] + j];
-      const char* hb = (const char*)hidden + (int64_t)b * D * ES;
-      const char* wr = (const char*)W + (int64_t)token * D * ES;
-      float acc = 0.f;
+    for (int f0 = grp; f0 < C; f0 += NGB * U2) {
+      int bls[U2], js[U2], toks[U2];
+#pragma unroll
+      for (int u = 0; u < U2; ++u) {
+        const int f = f0 + u * NGB;
+        bls[u] = f < C ? beam_of(cpre, f) : 0;
+        js[u] = f < C ? f - cpre[bls[u]] : 0;
+        toks[u] = f < C ? (int)tab.tok[bbase[bls[u]] + js[u]] : 0;
+      }
+      float acc[U2];
+#pragma unroll
+      for (int u = 0; u < U2; ++u) acc[u] = 0.f;
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        float h[VEC], w[VEC];
-        load16<DT>(hb + (int64_t)(c * G + gl) * 16, h);
-        load16<DT>(wr + (int64_t)(c * G + gl) * 16, w);
+        float h[U2][VEC], w[U2][VEC];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc = fmaf(w[e], h[e], acc);
+        for (int u = 0; u < U2; ++u) {
+          const char* hb = (const char*)hidden + (int64_t)(b0 + bls[u]) * D * ES;
+          const char* wr = (const char*)W + (int64_t)toks[u] * D * ES;
+          load16<DT>(hb + (int64_t)(c * G + gl) * 16, h[u]);
+          load16<DT>(wr + (int64_t)(c * G + gl) * 16, w[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U2; ++u)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[u] = fmaf(w[u][e], h[u][e], acc[u]);
       }
 #pragma unroll
-      for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-      if (gl == 0) z[(int64_t)b * ldz + j] = acc;
+      for (int u = 0; u < U2; ++u) {
+#pragma unroll
+        for (int o = G / 2; o >= 1; o >>= 1) acc[u] += __shfl_xor(acc[u], o);
+        const int f = f0 + u * NGB;
+        if (gl == 0 && f < C) {
+          z[(int64_t)(b0 + bls[u]) * ldz + js[u]] = acc[u];
+          if (store)
+            keys[f] = ((uint64_t)__float_as_uint(acc[u]) << 32) |
+                      ((uint32_t)(blo + bls[u]) * S + (uint32_t)js[u]);
+        }
+      }
     }
     __syncthreads();
   }
 
-  // 3. legal-only log-sum-exp of every beam, LPB threads per beam (online
-  //    max / sum of exp, fixed order).  When the request's candidates fit in
-  //    LDS, the same pass leaves each one's (z, beam*S + slot) in keys[]:
-  //    sparse at its flat index, dense at an offset from a block scan of the
-  //    threads' legal counts.
-  int LPB = 1;
-  while (LPB < NT && LPB * 2 * max(nloc, 1) <= NT) LPB *= 2;
-  const int bl3 = threadIdx.x / LPB, lb = threadIdx.x - bl3 * LPB;
-  const int r3 = (!MERGE && bl3 < nloc) ? brow[bl3] : -1;
-  bool store = C <= kSelCap;
-  const bool dvec = dense && vec4;
-  const float* z3 = z + (int64_t)(b0 + (bl3 < nloc ? bl3 : 0)) * ldz;
-  const uint32_t* row3 = (dense && r3 >= 0) ? tab.bits + (int64_t)r3 * tab.words : nullptr;
-  const int base3 = (r3 >= 0) ? tab.row_ptr[r3] : 0;
-  const int n3 = (r3 >= 0) ? tab.row_ptr[r3 + 1] - base3 : 0;
-  int at = 0;
-  const int ng = tab.V >> 2;  // float4 groups of a dense row (vector path)
-  constexpr int U = 8;        // loads issued together per thread
-  if (dense && store) {
-    int mine = 0;
+  // 3. legal-only log-sum-exp of every beam, LPB threads per beam
+  if constexpr (!MERGE) {
+    int LPB = 1;
+    while (LPB < NT && LPB * 2 * max(nloc, 1) <= NT) LPB *= 2;
+    const int bl3 = threadIdx.x / LPB, lb = threadIdx.x - bl3 * LPB;
+    const int r3 = (bl3 < nloc) ? brow[bl3] : -1;
+    const float* z3 = z + (int64_t)(b0 + (bl3 < nloc ? bl3 : 0)) * ldz;
+    const int at = (bl3 < nloc) ? cpre[bl3] : 0;
+    const int n3 = (r3 >= 0) ? cpre[bl3 + 1] - at : 0;
+    const uint32_t code0 = (uint32_t)(blo + bl3) * S;
+    float m = -INFINITY, s = 0.f;
+    auto acc_lse = [&](float zv) {
+      if (zv > m) {
+        s = s * __expf(m - zv) + 1.f;
+        m = zv;
+      } else {
+        s += __expf(zv - m);
+      }
+    };
+    constexpr int U = 8;  // loads issued together per thread
     if (r3 >= 0) {
-      if (dvec) {
-        for (int g0 = lb; g0 < ng; g0 += LPB * U) {
-          uint32_t wv[U];
+      if (MODE == kZScore && store) {
+        // the projection left the scores in keys[]
+        for (int j = lb; j < n3; j += LPB) acc_lse(__uint_as_float((uint32_t)(keys[at + j] >> 32)));
+      } else if (!dense) {
+        for (int j0 = lb; j0 < n3; j0 += LPB * U) {
+          float zv[U];
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            const int g = g0 + u * LPB;
-            wv[u] = g < ng ? row3[g >> 3] : 0u;
+            const int j = j0 + u * LPB;
+            if (j < n3) zv[u] = TOKEN_IDX ? z3[tab.tok[bbase[bl3] + j]] : z3[j];
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            const int g = g0 + u * LPB;
-            mine += __popc((wv[u] >> ((g & 7) * 4)) & 0xFu);
+            const int j = j0 + u * LPB;
+            if (j < n3) {
+              acc_lse(zv[u]);
+              if (store) keys[at + j] = ((uint64_t)__float_as_uint(zv[u]) << 32) | (code0 + (uint32_t)j);
+            }
           }
         }
       } else {
-        for (int v = lb; v < tab.V; v += LPB) mine += (row3[v >> 5] >> (v & 31)) & 1u;
-      }
-    }
-    int tot;
-    at = block_excl_scan<NT>(mine, sh, &tot);
-  } else if (store && bl3 < nloc) {
-    at = pre[bl3];
-  }
-  float m = -INFINITY, s = 0.f;
-  auto add = [&](float zv, uint32_t code, int where) {
-    if (zv > m) {
-      s = s * __expf(m - zv) + 1.f;
-      m = zv;
-    } else {
-      s += __expf(zv - m);
-    }
-    if (store) keys[where] = ((uint64_t)__float_as_uint(zv) << 32) | code;
-  };
-  if (r3 >= 0) {
-    const uint32_t code0 = (uint32_t)(blo + bl3) * S;
-    if (!dense) {
-      for (int j0 = lb; j0 < n3; j0 += LPB * U) {
-        float zv[U];
+        // dense: scores by legal rank; the token of rank j is the j-th set bit
+        for (int j0 = lb; j0 < n3; j0 += LPB * U) {
+          float zv[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = j0 + u * LPB;
-          if (j < n3) zv[u] = TOKEN_IDX ? z3[tab.tok[base3 + j]] : z3[j];
-        }
+          for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * LPB;
+            if (j < n3) zv[u] = z3[j];
+          }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = j0 + u * LPB;
-          if (j < n3) add(zv[u], code0 + (uint32_t)j, at + j);
+          for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * LPB;
+            if (j < n3) {
+              acc_lse(zv[u]);
+              if (store) keys[at + j] = (uint64_t)__float_as_uint(zv[u]) << 32;  // code after the barrier
+            }
+          }
         }
       }
-    } else if (dvec) {
-      for (int g0 = lb; g0 < ng; g0 += LPB * U) {
-        uint32_t wv[U];
-        float4 zz[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int g = g0 + u * LPB;
-          wv[u] = g < ng ? row3[g >> 3] : 0u;
-          if (g < ng) zz[u] = *(const float4*)(z3 + 4 * g);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int g = g0 + u * LPB;
-          const uint32_t m4 = (wv[u] >> ((g & 7) * 4)) & 0xFu;
-          const uint32_t c4 = code0 + 4u * (uint32_t)g;
-          if (m4 & 1u) add(zz[u].x, c4, at++);
-          if (m4 & 2u) add(zz[u].y, c4 + 1, at++);
-          if (m4 & 4u) add(zz[u].z, c4 + 2, at++);
-          if (m4 & 8u) add(zz[u].w, c4 + 3, at++);
-        }
+    }
+    if (LPB <= 64) {
+      for (int o = LPB >> 1; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
+      if (lb == 0 && bl3 < nloc) {
+        const float l = m + __logf(s);
+        blse[bl3] = l;
+        // best candidate of the beam (cand is monotone in z within a beam)
+        if (r3 >= 0) atomicMax(&omax_sh, ord_of(bcum[bl3] + (m - l)));
       }
     } else {
-      for (int v = lb; v < tab.V; v += LPB)
-        if ((row3[v >> 5] >> (v & 31)) & 1u) add(z3[v], code0 + (uint32_t)v, at++);
-    }
-  }
-  if (LPB <= 64) {
-    for (int o = LPB >> 1; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
-    if (lb == 0 && bl3 < nloc) {
-      blse[bl3] = m + __logf(s);
-      bmax[bl3] = m;
-    }
-  } else {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
-    if (lane == 0) {
-      pm[wave] = m;
-      ps[wave] = s;
-    }
-    __syncthreads();
-    const int wpb = LPB >> 6;
-    if ((int)threadIdx.x < nloc) {
-      float mm = pm[threadIdx.x * wpb], ss = ps[threadIdx.x * wpb];
-      for (int i = 1; i < wpb; ++i) lse_combine(mm, ss, pm[threadIdx.x * wpb + i], ps[threadIdx.x * wpb + i]);
-      blse[threadIdx.x] = mm + __logf(ss);
-      bmax[threadIdx.x] = mm;
+      for (int o = 32; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
+      if (lane == 0) {
+        pm[wave] = m;
+        ps[wave] = s;
+      }
+      __syncthreads();
+      const int wpb = LPB >> 6;
+      if ((int)threadIdx.x < nloc) {
+        float mm = pm[threadIdx.x * wpb], ss = ps[threadIdx.x * wpb];
+        for (int i = 1; i < wpb; ++i) lse_combine(mm, ss, pm[threadIdx.x * wpb + i], ps[threadIdx.x * wpb + i]);
+        const float l = mm + __logf(ss);
+        blse[threadIdx.x] = l;
+        if (brow[threadIdx.x] >= 0) atomicMax(&omax_sh, ord_of(bcum[threadIdx.x] + (mm - l)));
+      }
     }
   }
   __syncthreads();
-  // the request's best key: each beam's best candidate is its max legal z
-  // (cand is monotone in z within a beam), computed with the same operations
-  uint32_t omax = 0;
-  {
-    uint32_t o = 0;
-    if (!MERGE && (int)threadIdx.x < nloc && brow[threadIdx.x] >= 0)
-      o = ord_of(bcum[threadIdx.x] + (bmax[threadIdx.x] - blse[threadIdx.x]));
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) o = max(o, (uint32_t)__shfl_xor((int)o, d));
-    if (lane == 0) sh[wave] = (int)o;
-    __syncthreads();
-    for (int i = 0; i < kSelWaves; ++i) omax = max(omax, (uint32_t)sh[i]);
+  if (!MERGE && dense && store) {
+    // slot codes of the dense candidates: each (beam, word) pair walks its set
+    // bits; a bit's legal rank is the word's directory entry plus the set bits
+    // below it
+    for (int u = threadIdx.x; u < nloc * tab.words; u += NT) {
+      const int bl = u / tab.words, w = u - bl * tab.words;
+      const int r = brow[bl];
+      if (r < 0) continue;
+      uint32_t x = tab.bits[(int64_t)r * tab.words + w];
+      int j = cpre[bl] + tab.rank[(int64_t)r * tab.words + w];
+      const uint32_t code0 = (uint32_t)(blo + bl) * S + (uint32_t)(w << 5);
+      while (x) {
+        const int k = __ffs(x) - 1;
+        x &= x - 1;
+        keys[j++] |= code0 + (uint32_t)k;
+      }
+    }
     __syncthreads();
   }
   if (slot_dbg && !MERGE) {
@@ -651,22 +665,24 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       const int r = brow[bl];
       float* dbg = slot_dbg + (int64_t)b * S;
       const float* zb = z + (int64_t)b * ldz;
-      const int base = r >= 0 ? tab.row_ptr[r] : 0;
-      const int n = r >= 0 ? tab.row_ptr[r + 1] - base : 0;
+      const int n = r >= 0 ? cpre[bl + 1] - cpre[bl] : 0;
       const float l = blse[bl];
       for (int j = lane; j < (int)S; j += 64) {
         float v = -INFINITY;
         if (r >= 0) {
           if (!dense) {
-            if (j < n) v = (TOKEN_IDX ? zb[tab.tok[base + j]] : zb[j]) - l;
-          } else if ((tab.bits[(int64_t)r * tab.words + (j >> 5)] >> (j & 31)) & 1u) {
-            v = zb[j] - l;
+            if (j < n) v = (TOKEN_IDX ? zb[tab.tok[bbase[bl] + j]] : zb[j]) - l;
+          } else {
+            const int64_t w = (int64_t)r * tab.words + (j >> 5);
+            const uint32_t x = tab.bits[w];
+            if ((x >> (j & 31)) & 1u) v = zb[tab.rank[w] + __popc(x & ((1u << (j & 31)) - 1u))] - l;
           }
         }
         dbg[j] = v;
       }
     }
   }
+  uint32_t omax = omax_sh;
 
   if constexpr (MERGE) {
     // the parts' keys (already final) into LDS, in part order
@@ -691,7 +707,6 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     omax = 0;
     for (int i = 0; i < kSelWaves; ++i) omax = max(omax, (uint32_t)sh[i]);
     store = true;
-    T = C;
     __syncthreads();
   }
 
@@ -720,21 +735,22 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   // without room in LDS, keys are recomputed from z in every pass
   auto enumerate = [&](auto&& fn) {
     for (int f = threadIdx.x; f < T; f += NT) {
-      const int bl = beam_of(f), i = f - pre[bl];
+      const int bl = beam_of(pre, f), i = f - pre[bl];
       const int b = b0 + bl;
       const int r = brow[bl];
       const float c = bcum[bl], l = blse[bl];
       const float* zb = z + (int64_t)b * ldz;
       const uint32_t code0 = (uint32_t)(blo + bl) * S;
       if (!dense) {
-        const float zv = TOKEN_IDX ? zb[tab.tok[tab.row_ptr[r] + i]] : zb[i];
+        const float zv = TOKEN_IDX ? zb[tab.tok[bbase[bl] + i]] : zb[i];
         fn(make_key(c + (zv - l), code0 + (uint32_t)i));
       } else {
         uint32_t y = tab.bits[(int64_t)r * tab.words + i];
+        int j = tab.rank[(int64_t)r * tab.words + i];
         while (y) {
           const int v = (i << 5) + __ffs(y) - 1;
           y &= y - 1;
-          fn(make_key(c + (zb[v] - l), code0 + (uint32_t)v));
+          fn(make_key(c + (zb[j++] - l), code0 + (uint32_t)v));
         }
       }
     }
@@ -864,14 +880,14 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       const int r = brow[bl];
       int token, next;
       if (!dense) {
-        next = tab.row_ptr[r] + slot;  // the entry's position is its next row
+        next = bbase[bl] + slot;  // the entry's position is its next row
         token = tab.tok[next];
       } else {
         token = slot;
         // entries of the row before this token: the rank directory gives the
         // count before its word, popcount the rest of the word
         const int64_t w = (int64_t)r * tab.words + (slot >> 5);
-        next = tab.row_ptr[r] + tab.rank[w] + __popc(tab.bits[w] & ((1u << (slot & 31)) - 1u));
+        next = bbase[bl] + tab.rank[w] + __popc(tab.bits[w] & ((1u << (slot & 31)) - 1u));
       }
       parent_out[oi] = b;
       token_out[oi] = token;
@@ -900,56 +916,91 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kTileM = 128, kTileN = 128, kTileKBytes = 128;
+constexpr int kTileKBytes = 128;
 constexpr int kLdsRow = kTileKBytes + 16;  // padded row pitch in bytes
 
 // C[m][n] = sum_k A[m][k] * B[n][k]: A = hidden [M][D], B = W_t [N][D], both
-// k-contiguous.  128x128 block tile, 4 waves each owning 64x64 as 2x2 MFMA
-// 32x32 blocks, 128-byte k-slices staged through LDS with a register prefetch
-// of the next slice.
-template <int DT>
+// k-contiguous.  BM x BN block tile, 4 waves in 2x2 each owning (BM/2)x(BN/2)
+// as MFMA 32x32 blocks, 128-byte k-slices staged through LDS with a register
+// prefetch of the next slice.
+// compact != 0 (dense table): only legal columns are written, at their legal
+// rank within the beam's row (rank directory + popcount below the column);
+// dead beams are skipped.  The tile's rows, bitmap words and rank entries are
+// loaded into LDS before the k loop so the epilogue does not wait on them.
+// compact == 0: full rows, column = token.
+template <int DT, int BM, int BN>
 __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A,
                                                       const void* __restrict__ Bm,
                                                       float* __restrict__ C, int32_t M, int32_t N,
-                                                      int32_t D, int64_t ldc) {
+                                                      int32_t D, int64_t ldc, int32_t compact,
+                                                      DevTable tab,
+                                                      const int32_t* __restrict__ row_in) {
   constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
   constexpr int TK = kTileKBytes / ES;  // k elements per slice
-  __shared__ __attribute__((aligned(16))) char As[kTileM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) char Bs[kTileN * kLdsRow];
-  const int nbm = (M + kTileM - 1) / kTileM;
+  constexpr int WM = BM / 2, WN = BN / 2, IB = WM / 32, JB = WN / 32;
+  constexpr int NA = BM * 8 / kThreads, NB = BN * 8 / kThreads;  // 16-byte chunks per thread
+  constexpr int TW = BN / 32;                                     // bitmap words per tile row
+  __shared__ __attribute__((aligned(16))) char As[BM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) char Bs[BN * kLdsRow];
+  __shared__ int trow[BM];
+  __shared__ uint32_t tbits[BM * TW];
+  __shared__ int trank[BM * TW];
+  const int nbm = (M + BM - 1) / BM;
   const int tm = blockIdx.x % nbm, tn = blockIdx.x / nbm;
-  const int m0 = tm * kTileM, n0 = tn * kTileN;
+  const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const char* Ab = (const char*)A;
   const char* Bb = (const char*)Bm;
   const int64_t rowbytes = (int64_t)D * ES;
-  // global -> register staging: 4 x 16 bytes of A and of B per thread
-  uint4 ra[4], rb[4];
+  if (compact) {
+    for (int i = threadIdx.x; i < BM; i += kThreads) {
+      const int gm = m0 + i;
+      const int r = gm < M ? row_in[gm] : -1;
+      trow[i] = (r >= 0 && r < tab.rows) ? r : -1;
+      for (int k = 0; k < TW; ++k) {
+        const int wd = (n0 >> 5) + k;
+        const bool ok = r >= 0 && r < tab.rows && wd < tab.words;
+        tbits[i * TW + k] = ok ? tab.bits[(int64_t)r * tab.words + wd] : 0u;
+        trank[i * TW + k] = ok ? (int)tab.rank[(int64_t)r * tab.words + wd] : 0;
+      }
+    }
+  }
+  // global -> register staging of A and B slices
+  uint4 ra[NA], rb[NB];
   auto gload = [&](int kbyte) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NA; ++i) {
       const int c = threadIdx.x + i * kThreads;
       const int row = c >> 3, col = (c & 7) * 16;
-      const int gm = m0 + row, gn = n0 + row;
+      const int gm = m0 + row;
       ra[i] = (gm < M) ? *(const uint4*)(Ab + gm * rowbytes + kbyte + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int row = c >> 3, col = (c & 7) * 16;
+      const int gn = n0 + row;
       rb[i] = (gn < N) ? *(const uint4*)(Bb + gn * rowbytes + kbyte + col) : make_uint4(0, 0, 0, 0);
     }
   };
   auto sstore = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NA; ++i) {
       const int c = threadIdx.x + i * kThreads;
-      const int row = c >> 3, col = (c & 7) * 16;
-      *(uint4*)(As + row * kLdsRow + col) = ra[i];
-      *(uint4*)(Bs + row * kLdsRow + col) = rb[i];
+      *(uint4*)(As + (c >> 3) * kLdsRow + (c & 7) * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      *(uint4*)(Bs + (c >> 3) * kLdsRow + (c & 7) * 16) = rb[i];
     }
   };
-  f32x16 acc[2][2];
+  f32x16 acc[IB][JB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   const int half = lane >> 5, l32 = lane & 31;
@@ -965,18 +1016,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
 #pragma unroll
       for (int kc = 0; kc < TK / 8; ++kc) {
         const int off = kc * 32 + half * 16;
-        f32x4 a[2], bv[2];
+        f32x4 a[IB], bv[JB];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          a[i] = *(const f32x4*)(As + (wm * 64 + i * 32 + l32) * kLdsRow + off);
-          bv[i] = *(const f32x4*)(Bs + (wn * 64 + i * 32 + l32) * kLdsRow + off);
-        }
+        for (int i = 0; i < IB; ++i) a[i] = *(const f32x4*)(As + (wm * WM + i * 32 + l32) * kLdsRow + off);
+#pragma unroll
+        for (int j = 0; j < JB; ++j) bv[j] = *(const f32x4*)(Bs + (wn * WN + j * 32 + l32) * kLdsRow + off);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < IB; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < JB; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], bv[j][s], acc[i][j], 0, 0, 0);
       }
     } else {
@@ -984,34 +1034,52 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
 #pragma unroll
       for (int kc = 0; kc < TK / 16; ++kc) {
         const int off = kc * 32 + half * 16;
+        uint4 ua[IB], ub[JB];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint4 ua = *(const uint4*)(As + (wm * 64 + i * 32 + l32) * kLdsRow + off);
+        for (int i = 0; i < IB; ++i) ua[i] = *(const uint4*)(As + (wm * WM + i * 32 + l32) * kLdsRow + off);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint4 ub = *(const uint4*)(Bs + (wn * 64 + j * 32 + l32) * kLdsRow + off);
+        for (int j = 0; j < JB; ++j) ub[j] = *(const uint4*)(Bs + (wn * WN + j * 32 + l32) * kLdsRow + off);
+#pragma unroll
+        for (int i = 0; i < IB; ++i)
+#pragma unroll
+          for (int j = 0; j < JB; ++j) {
             if constexpr (DT == ZGR_BF16) {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8, ua), __builtin_bit_cast(bf16x8, ub), acc[i][j], 0, 0, 0);
+                  __builtin_bit_cast(bf16x8, ua[i]), __builtin_bit_cast(bf16x8, ub[j]), acc[i][j], 0, 0, 0);
             } else {
               acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  __builtin_bit_cast(f16x8, ua), __builtin_bit_cast(f16x8, ub), acc[i][j], 0, 0, 0);
+                  __builtin_bit_cast(f16x8, ua[i]), __builtin_bit_cast(f16x8, ub[j]), acc[i][j], 0, 0, 0);
             }
           }
-        }
       }
     }
   }
   // 32x32 accumulator layout: lane -> column l32, register v -> row 8*(v/4) + 4*half + v%4
+  if (!compact) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < IB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + l32;
+      for (int j = 0; j < JB; ++j) {
+        const int col = n0 + wn * WN + j * 32 + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (row < M && col < N) C[(int64_t)row * ldc + col] = acc[i][j][v];
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < IB; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const int kw = (wn * WN + j * 32) >> 5;  // the block's 32 columns are one bitmap word
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (row < M && col < N) C[(int64_t)row * ldc + col] = acc[i][j][v];
+        const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        const uint32_t x = tbits[rl * TW + kw];
+        if ((x >> l32) & 1u)
+          C[(int64_t)(m0 + rl) * ldc + trank[rl * TW + kw] + __popc(x & ((1u << l32) - 1u))] = acc[i][j][v];
       }
     }
 }
@@ -1027,7 +1095,12 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict__ A,
                                                          const void* __restrict__ Bm,
                                                          float* __restrict__ C, int32_t M,
-                                                         int32_t N, int32_t D, int64_t ldc) {
+                                                         int32_t N, int32_t D, int64_t ldc,
+                                                         int32_t compact, DevTable tab,
+                                                         const int32_t* __restrict__ row_in) {
+  __shared__ int trow[32];
+  __shared__ uint32_t tbits[32];
+  __shared__ int trank[32];
   constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
   constexpr int U = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1068,12 +1141,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict_
     }
   }
   // 16x16 accumulator layout: lane -> column l16, register v -> row 4*g + v
-  if (n < N) {
+  if (!compact) {
+    if (n < N) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = tm * 32 + (wave >> 1) * 16 + 4 * g + v;
-      if (row < M) C[(int64_t)row * ldc + n] = acc[v];
+      for (int v = 0; v < 4; ++v) {
+        const int row = tm * 32 + (wave >> 1) * 16 + 4 * g + v;
+        if (row < M) C[(int64_t)row * ldc + n] = acc[v];
+      }
     }
+    return;
+  }
+  // dense table: legal columns only, at their legal rank (the block's 32
+  // columns are one bitmap word)
+  if (threadIdx.x < 32) {
+    const int gm = tm * 32 + threadIdx.x;
+    int r = gm < M ? row_in[gm] : -1;
+    r = (r >= 0 && r < tab.rows) ? r : -1;
+    const bool ok = r >= 0 && tn < tab.words;
+    trow[threadIdx.x] = r;
+    tbits[threadIdx.x] = ok ? tab.bits[(int64_t)r * tab.words + tn] : 0u;
+    trank[threadIdx.x] = ok ? (int)tab.rank[(int64_t)r * tab.words + tn] : 0;
+  }
+  __syncthreads();
+  const int bit = (wave & 1) * 16 + l16;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int rl = (wave >> 1) * 16 + 4 * g + v;
+    const uint32_t x = tbits[rl];
+    if ((x >> bit) & 1u)
+      C[(int64_t)(tm * 32 + rl) * ldc + trank[rl] + __popc(x & ((1u << bit) - 1u))] = acc[v];
   }
 }
 
@@ -1127,14 +1223,18 @@ hipError_t launch_sel_d(const StepArgs& a, hipStream_t s) {
 template <int DT>
 hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
   const int V = a.tab.V;
-  const int nbm = (a.M + kTileM - 1) / kTileM, nbn = (V + kTileN - 1) / kTileN;
-  if (nbm * nbn < a.n_cu) {
-    const int grid = ((a.M + 31) / 32) * ((V + 31) / 32);
-    hipLaunchKernelGGL(k_gemm_small<DT>, dim3(grid), dim3(kThreads), 0, s, a.hidden, a.W, a.z, a.M, V,
-                       a.d, a.ldz);
+  const int compact = a.tab.fmt == ZGR_FMT_DENSE ? 1 : 0;
+  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((V + bn - 1) / bn); };
+  // the largest tile that still gives every compute unit two blocks (or one)
+  if (tiles(128, 128) >= 2 * a.n_cu) {
+    hipLaunchKernelGGL((k_gemm_nt<DT, 128, 128>), dim3(tiles(128, 128)), dim3(kThreads), 0, s, a.hidden,
+                       a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
+  } else if (tiles(64, 64) >= a.n_cu) {
+    hipLaunchKernelGGL((k_gemm_nt<DT, 64, 64>), dim3(tiles(64, 64)), dim3(kThreads), 0, s, a.hidden,
+                       a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   } else {
-    hipLaunchKernelGGL(k_gemm_nt<DT>, dim3(nbm * nbn), dim3(kThreads), 0, s, a.hidden, a.W, a.z, a.M,
-                       V, a.d, a.ldz);
+    hipLaunchKernelGGL(k_gemm_small<DT>, dim3(tiles(32, 32)), dim3(kThreads), 0, s, a.hidden, a.W, a.z,
+                       a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   }
   return hipGetLastError();
 }
@@ -1171,41 +1271,40 @@ hipError_t launch_full_projection(const StepArgs& a, hipStream_t s) {
 }
 
 #define ZGR_STEP_ARGS                                                                            \
-  a.tab, a.t, a.L, a.k_in, a.K, a.row_in, a.cum_in, a.hidden, a.W, a.z, a.ldz, vec4, a.parts,      \
+  a.tab, a.t, a.L, a.k_in, a.K, a.row_in, a.cum_in, a.hidden, a.W, a.z, a.ldz, a.parts,            \
       a.part_keys, a.part_cnt, a.parent_out, a.token_out, a.row_out, a.cum_out, a.prefix_in,       \
       a.prefix_out, a.slot_dbg, a.err
 
 template <int DT, int D>
-hipError_t launch_scored_step(const StepArgs& a, int vec4, hipStream_t s) {
+hipError_t launch_scored_step(const StepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_request_step<kZScore, DT, D>), dim3(a.B * a.parts), dim3(kSelThreads), 0, s,
                      ZGR_STEP_ARGS);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t launch_scored_step_d(const StepArgs& a, int vec4, hipStream_t s) {
+hipError_t launch_scored_step_d(const StepArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 64: return launch_scored_step<DT, 64>(a, vec4, s);
-    case 128: return launch_scored_step<DT, 128>(a, vec4, s);
-    case 256: return launch_scored_step<DT, 256>(a, vec4, s);
-    case 512: return launch_scored_step<DT, 512>(a, vec4, s);
-    case 768: return launch_scored_step<DT, 768>(a, vec4, s);
-    case 1024: return launch_scored_step<DT, 1024>(a, vec4, s);
-    case 2048: return launch_scored_step<DT, 2048>(a, vec4, s);
-    case 4096: return launch_scored_step<DT, 4096>(a, vec4, s);
+    case 64: return launch_scored_step<DT, 64>(a, s);
+    case 128: return launch_scored_step<DT, 128>(a, s);
+    case 256: return launch_scored_step<DT, 256>(a, s);
+    case 512: return launch_scored_step<DT, 512>(a, s);
+    case 768: return launch_scored_step<DT, 768>(a, s);
+    case 1024: return launch_scored_step<DT, 1024>(a, s);
+    case 2048: return launch_scored_step<DT, 2048>(a, s);
+    case 4096: return launch_scored_step<DT, 4096>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s) {
-  const int vec4 = (a.ldz % 4 == 0 && a.tab.V % 4 == 0) ? 1 : 0;
   const dim3 grid(a.B * a.parts);
   hipError_t e = hipSuccess;
   if (zmode == kZScore) {
     switch (a.dtype) {
-      case ZGR_F32: e = launch_scored_step_d<ZGR_F32>(a, vec4, s); break;
-      case ZGR_BF16: e = launch_scored_step_d<ZGR_BF16>(a, vec4, s); break;
-      case ZGR_F16: e = launch_scored_step_d<ZGR_F16>(a, vec4, s); break;
+      case ZGR_F32: e = launch_scored_step_d<ZGR_F32>(a, s); break;
+      case ZGR_BF16: e = launch_scored_step_d<ZGR_BF16>(a, s); break;
+      case ZGR_F16: e = launch_scored_step_d<ZGR_F16>(a, s); break;
       default: return hipErrorInvalidValue;
     }
   } else if (zmode == kZToken) {
@@ -1221,7 +1320,6 @@ hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s) {
 }
 
 hipError_t launch_request_merge(const StepArgs& a, hipStream_t s) {
-  const int vec4 = 0;
   hipLaunchKernelGGL((k_request_step<kZParts, ZGR_F32, 64>), dim3(a.B), dim3(kSelThreads), 0, s,
                      ZGR_STEP_ARGS);
   return hipGetLastError();
