@@ -255,6 +255,73 @@ def cpu_baseline(w, seconds):
                       f"{cfg.B} requests"}
 
 
+def rebuild_bench(name, reps):
+    """Index rebuild pipeline (host build + upload to HBM) of one catalog:
+    single-threaded build with one plain copy per array, against the
+    chunk-parallel build with the double-buffered pinned upload, from a
+    shuffled catalog and from one already in SID order.  The catalog itself is
+    generated untimed."""
+    import torch
+
+    import sid_constrained_beam_amd as zgr
+    import workload
+    torch.cuda.set_device(0)
+    torch.cuda.synchronize()
+    cfg = workload.CONFIGS[name]
+    t0 = time.time()
+    sids = workload.catalog(cfg)
+    log(f"[rebuild] catalog {name}: {len(sids)} SIDs generated in {time.time() - t0:.1f} s")
+    # untimed: first host-to-device copies of the process (runtime set-up)
+    for opt in (dict(threads=1, upload="direct"), dict()):
+        idx, _ = zgr.zgr_index_upload(sids[: min(len(sids), 1_000_000)], cfg.V, cfg.fmt, **opt)
+        idx.free()
+    variants = [("single_thread_direct", dict(threads=1, upload="direct"), 1, False),
+                ("parallel_direct", dict(upload="direct"), reps, False),
+                ("parallel_staged", dict(), reps, False),
+                ("parallel_staged_presorted", dict(), reps, True)]
+    out = {}
+    presorted = None
+    for label, opt, n, use_sorted in variants:
+        src = presorted if use_sorted else sids
+        runs = []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            idx, rank = zgr.zgr_index_upload(src, cfg.V, cfg.fmt, want_rank=True, **opt)
+            wall = time.perf_counter() - t0
+            tm = zgr.zgr_index_times(idx)
+            tm["wall_s"] = wall
+            runs.append(tm)
+            if presorted is None:
+                presorted = np.empty_like(sids)
+                presorted[rank] = sids
+            idx.free()
+            del idx, rank
+        best = min(runs, key=lambda r: r["wall_s"])
+        out[label] = {
+            "wall_s": round(best["wall_s"], 3),
+            "threads": best["threads"],
+            "upload": best["upload"],
+            **{k: round(best[k], 1) for k in ("keys_ms", "sort_ms", "layout_ms", "encode_ms",
+                                               "build_ms", "alloc_ms", "upload_ms")},
+            "h2d_GBs": round(best["device_bytes"] / (best["upload_ms"] * 1e6), 2)
+            if best["upload_ms"] > 0 else None,
+        }
+        log(f"[rebuild] {label}: {out[label]}")
+    single = out["single_thread_direct"]["wall_s"]
+    best = out["parallel_staged"]["wall_s"]
+    print(json.dumps({
+        "metric": "index rebuild time (host build + upload to HBM)",
+        "value": best, "unit": "s", "higher_is_better": False, "n_gpus": 1,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": name, "items": int(cfg.N), "L": cfg.L, "V": cfg.V,
+                   "fmt": "".join(cfg.fmt) if cfg.fmt else "auto",
+                   "device_bytes": int(runs[-1]["device_bytes"]),
+                   "host_cpus": os.cpu_count()},
+        "speedup_vs_single_thread": round(single / best, 2),
+        "variants": out,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,12 +335,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--rebuild", default=None, metavar="WORKLOAD",
+                    help="time the index rebuild pipeline of this workload's catalog instead")
+    ap.add_argument("--rebuild-reps", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no "
                                    "multi-GPU mode (requests would shard across GPUs with no "
                                    "exchange, see the design notes)", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.rebuild:
+        rebuild_bench(args.rebuild, args.rebuild_reps)
+        return
     import torch
 
     import sid_constrained_beam_amd as zgr

@@ -123,6 +123,70 @@ int32_t zgr_index_to_device(zgr_index* idx, void* stream);
 int32_t zgr_index_upload(const int32_t* sids, int64_t N, int32_t L, int32_t V, const int32_t* fmt,
                          void* stream, zgr_index** out, int64_t* rank_of_input);
 
+/* ---- index rebuild pipeline ---------------------------------------------------------
+ * The index is rebuilt whenever the catalog or the model's codebook changes
+ * (ZeroGR description, "overall pipeline": the index is built offline and
+ * rebuilt on every update), so its build and upload bound the update window.
+ * The host build sorts the packed SIDs and lays the tables out in two passes
+ * over chunks of the sorted keys (count, prefix-sum of the chunk counts, fill)
+ * on host_threads threads; the result does not depend on the thread count.
+ * The upload copies through two pinned staging buffers in turn, so host
+ * copies into one overlap the DMA of the other. */
+#define ZGR_UPLOAD_STAGED 0 /* double-buffered pinned staging (default) */
+#define ZGR_UPLOAD_DIRECT 1 /* one hipMemcpyAsync per array from the pageable host tables */
+
+typedef struct {
+  int32_t host_threads;  /* 0 = hardware threads (at most 16) for large catalogs; else 1..64 */
+  int32_t upload;        /* ZGR_UPLOAD_STAGED or ZGR_UPLOAD_DIRECT */
+  int64_t staging_bytes; /* bytes per staging buffer; 0 = 64 MiB (clamped to [4 KiB, upload size]) */
+} zgr_build_opts;
+
+/* Wall-clock milliseconds of each phase of the last build / upload. */
+typedef struct {
+  double keys_ms;    /* pack SIDs into keys, token range check */
+  double sort_ms;    /* radix sort of the keys (skipped for a catalog already in SID order) */
+  double layout_ms;  /* duplicate check, count, offsets, fill of row_ptr / tok, item ids */
+  double encode_ms;  /* per table: largest row, format, bitmap and rank directory */
+  double build_ms;   /* whole host build */
+  double alloc_ms;   /* hipMalloc of the device tables */
+  double upload_ms;  /* host to HBM copies, synchronised */
+  int64_t device_bytes; /* bytes uploaded */
+  int32_t threads;      /* host threads the build used */
+  int32_t upload;       /* ZGR_UPLOAD_* used */
+} zgr_build_times;
+
+/* zgr_index_build_host with options (NULL = defaults); times (nullable)
+ * receives the build phases.  Errors: as zgr_index_build_host, and ZGR_E_ARG
+ * for a negative host_threads. */
+int32_t zgr_index_build_host_ex(const int32_t* sids, int64_t N, int32_t L, int32_t V,
+                                const int32_t* fmt, int64_t* rank_of_input,
+                                const zgr_build_opts* opts, zgr_build_times* times,
+                                zgr_index** out);
+
+/* zgr_index_to_device with options (NULL = defaults: staged, 64 MiB buffers);
+ * times (nullable) receives the build and upload phases.  Pinned staging
+ * buffers are allocated for the call and freed before it returns.
+ * Errors: as zgr_index_to_device, and ZGR_E_ARG for an unknown upload mode or
+ * negative sizes; on failure no device memory stays allocated. */
+int32_t zgr_index_to_device_ex(zgr_index* idx, void* stream, const zgr_build_opts* opts,
+                               zgr_build_times* times);
+
+/* zgr_index_build_host_ex followed by zgr_index_to_device_ex. */
+int32_t zgr_index_upload_ex(const int32_t* sids, int64_t N, int32_t L, int32_t V,
+                            const int32_t* fmt, void* stream, const zgr_build_opts* opts,
+                            zgr_build_times* times, zgr_index** out, int64_t* rank_of_input);
+
+/* Phases of the index's build and upload.  Errors: ZGR_E_ARG. */
+int32_t zgr_index_times(const zgr_index* idx, zgr_build_times* out);
+
+/* Device copies of table t (valid while idx lives; NULL where the table's
+ * format has no such array): row_ptr int32 [rows+1], tok uint16 [nnz]
+ * (sparse), bits uint32 [rows][ceil(V/32)] and rank uint16 [rows][ceil(V/32)]
+ * (dense; set bits of the row before each word).  Errors: ZGR_E_ARG,
+ * ZGR_E_STATE (not uploaded). */
+int32_t zgr_index_device_table(const zgr_index* idx, int32_t t, const void** row_ptr,
+                               const void** tok, const void** bits, const void** rank);
+
 /* Per-step statistics, t in 1..L.  Errors: ZGR_E_ARG. */
 int32_t zgr_index_stats(const zgr_index* idx, int32_t t, zgr_step_stats* out);
 

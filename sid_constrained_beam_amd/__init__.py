@@ -24,6 +24,8 @@ ZGR_E_NOMEM, ZGR_E_HIP, ZGR_E_STATE, ZGR_E_CALLBACK, ZGR_E_DEVICE = 5, 6, 7, 8, 
 ZGR_F32, ZGR_BF16, ZGR_F16 = 0, 1, 2
 ZGR_FMT_AUTO, ZGR_FMT_DENSE, ZGR_FMT_SPARSE = 0, 1, 2
 ZGR_PROJ_AUTO, ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE = 0, 1, 2
+ZGR_UPLOAD_STAGED, ZGR_UPLOAD_DIRECT = 0, 1
+UPLOAD_CODES = {"staged": ZGR_UPLOAD_STAGED, "direct": ZGR_UPLOAD_DIRECT}
 KERNELS = ["units", "selective", "gemm", "request"]
 
 DTYPE_CODES = {"f32": ZGR_F32, "bf16": ZGR_BF16, "f16": ZGR_F16}
@@ -40,6 +42,23 @@ HIDDEN_FN = ctypes.CFUNCTYPE(ctypes.c_int32, _P, _I32, _I32, _I32, _P, _I32, _P,
 class StepStats(ctypes.Structure):
     _fields_ = [("rows", _I64), ("nnz", _I64), ("fmt", _I32), ("stride", _I32), ("bytes", _I64),
                 ("max_legal", _I32), ("reserved", _I32)]
+
+
+class BuildOpts(ctypes.Structure):
+    _fields_ = [("host_threads", _I32), ("upload", _I32), ("staging_bytes", _I64)]
+
+
+class BuildTimes(ctypes.Structure):
+    _fields_ = [("keys_ms", ctypes.c_double), ("sort_ms", ctypes.c_double),
+                ("layout_ms", ctypes.c_double), ("encode_ms", ctypes.c_double),
+                ("build_ms", ctypes.c_double), ("alloc_ms", ctypes.c_double),
+                ("upload_ms", ctypes.c_double), ("device_bytes", _I64), ("threads", _I32),
+                ("upload", _I32)]
+
+    def as_dict(self) -> dict:
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["upload"] = {v: k for k, v in UPLOAD_CODES.items()}.get(d["upload"], d["upload"])
+        return d
 
 
 class ZgrError(RuntimeError):
@@ -66,6 +85,16 @@ def lib() -> ctypes.CDLL:
             "zgr_index_build_host": (_I32, [_P, _I64, _I32, _I32, _P, _P, ctypes.POINTER(_P)]),
             "zgr_index_to_device": (_I32, [_P, _P]),
             "zgr_index_upload": (_I32, [_P, _I64, _I32, _I32, _P, _P, ctypes.POINTER(_P), _P]),
+            "zgr_index_build_host_ex": (_I32, [_P, _I64, _I32, _I32, _P, _P,
+                                               ctypes.POINTER(BuildOpts),
+                                               ctypes.POINTER(BuildTimes), ctypes.POINTER(_P)]),
+            "zgr_index_to_device_ex": (_I32, [_P, _P, ctypes.POINTER(BuildOpts),
+                                              ctypes.POINTER(BuildTimes)]),
+            "zgr_index_upload_ex": (_I32, [_P, _I64, _I32, _I32, _P, _P, ctypes.POINTER(BuildOpts),
+                                           ctypes.POINTER(BuildTimes), ctypes.POINTER(_P), _P]),
+            "zgr_index_times": (_I32, [_P, ctypes.POINTER(BuildTimes)]),
+            "zgr_index_device_table": (_I32, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                              ctypes.POINTER(_P), ctypes.POINTER(_P)]),
             "zgr_index_stats": (_I32, [_P, _I32, ctypes.POINTER(StepStats)]),
             "zgr_index_host_table": (_I32, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                             ctypes.POINTER(_P)]),
@@ -171,34 +200,85 @@ def _fmt_array(fmt, L):
     return a
 
 
-def zgr_index_build_host(sids: np.ndarray, V: int, fmt=None, want_rank: bool = True):
-    """Host-only build.  Returns (Index, rank_of_input int64 [N] or None)."""
+def _opts(threads: int, upload, staging_bytes: int):
+    if threads == 0 and upload in (None, "staged") and staging_bytes == 0:
+        return None
+    code = UPLOAD_CODES[upload] if isinstance(upload, str) else (
+        ZGR_UPLOAD_STAGED if upload is None else int(upload))
+    return BuildOpts(int(threads), code, int(staging_bytes))
+
+
+def _ref(x):
+    return None if x is None else ctypes.byref(x)
+
+
+def zgr_index_build_host(sids: np.ndarray, V: int, fmt=None, want_rank: bool = True,
+                         threads: int = 0, times: bool = False):
+    """Host-only build on `threads` threads (0 = automatic).  Returns
+    (Index, rank_of_input int64 [N] or None), plus the phase times as a dict
+    when `times`."""
     sids = np.ascontiguousarray(sids, dtype=np.int32)
     N, L = sids.shape
     f = _fmt_array(fmt, L)
     rank = np.empty(N, dtype=np.int64) if want_rank else None
     h = ctypes.c_void_p()
-    _check(lib().zgr_index_build_host(sids.ctypes.data, N, L, V,
-                                      None if f is None else f.ctypes.data,
-                                      None if rank is None else rank.ctypes.data, ctypes.byref(h)))
-    return Index(h), rank
+    o = _opts(threads, None, 0)
+    tm = BuildTimes() if times else None
+    fp = None if f is None else f.ctypes.data
+    rp = None if rank is None else rank.ctypes.data
+    if o is None and tm is None:
+        _check(lib().zgr_index_build_host(sids.ctypes.data, N, L, V, fp, rp, ctypes.byref(h)))
+    else:
+        _check(lib().zgr_index_build_host_ex(sids.ctypes.data, N, L, V, fp, rp, _ref(o), _ref(tm),
+                                             ctypes.byref(h)))
+    return (Index(h), rank, tm.as_dict()) if times else (Index(h), rank)
 
 
-def zgr_index_to_device(index: Index, stream=None):
-    _check(lib().zgr_index_to_device(index.handle, _stream_ptr(stream)))
+def zgr_index_to_device(index: Index, stream=None, threads: int = 0, upload=None,
+                        staging_bytes: int = 0):
+    """Copy a host-built index to HBM; returns the build and upload phase times."""
+    o = _opts(threads, upload, staging_bytes)
+    tm = BuildTimes()
+    if o is None:
+        _check(lib().zgr_index_to_device(index.handle, _stream_ptr(stream)))
+        _check(lib().zgr_index_times(index.handle, ctypes.byref(tm)))
+    else:
+        _check(lib().zgr_index_to_device_ex(index.handle, _stream_ptr(stream), ctypes.byref(o),
+                                            ctypes.byref(tm)))
+    return tm.as_dict()
 
 
-def zgr_index_upload(sids: np.ndarray, V: int, fmt=None, stream=None, want_rank: bool = True):
+def zgr_index_upload(sids: np.ndarray, V: int, fmt=None, stream=None, want_rank: bool = True,
+                     threads: int = 0, upload=None, staging_bytes: int = 0):
     """Build on the host and copy to HBM.  Returns (Index, rank_of_input)."""
     sids = np.ascontiguousarray(sids, dtype=np.int32)
     N, L = sids.shape
     f = _fmt_array(fmt, L)
     rank = np.empty(N, dtype=np.int64) if want_rank else None
     h = ctypes.c_void_p()
-    _check(lib().zgr_index_upload(sids.ctypes.data, N, L, V, None if f is None else f.ctypes.data,
-                                  _stream_ptr(stream), ctypes.byref(h),
-                                  None if rank is None else rank.ctypes.data))
+    o = _opts(threads, upload, staging_bytes)
+    fp = None if f is None else f.ctypes.data
+    rp = None if rank is None else rank.ctypes.data
+    if o is None:
+        _check(lib().zgr_index_upload(sids.ctypes.data, N, L, V, fp, _stream_ptr(stream),
+                                      ctypes.byref(h), rp))
+    else:
+        _check(lib().zgr_index_upload_ex(sids.ctypes.data, N, L, V, fp, _stream_ptr(stream),
+                                         ctypes.byref(o), None, ctypes.byref(h), rp))
     return Index(h), rank
+
+
+def zgr_index_times(index: Index) -> dict:
+    tm = BuildTimes()
+    _check(lib().zgr_index_times(index.handle, ctypes.byref(tm)))
+    return tm.as_dict()
+
+
+def zgr_index_device_table(index: Index, t: int):
+    """Device pointers of table t: (row_ptr, tok, bits, rank), 0 where absent."""
+    ptrs = [_P() for _ in range(4)]
+    _check(lib().zgr_index_device_table(index.handle, t, *[ctypes.byref(p) for p in ptrs]))
+    return tuple(p.value or 0 for p in ptrs)
 
 
 def zgr_index_stats(index: Index, t: int) -> dict:

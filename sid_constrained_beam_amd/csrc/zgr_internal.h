@@ -24,6 +24,7 @@ struct HostTable {
   std::vector<int32_t> row_ptr;  // [rows + 1]
   std::vector<uint16_t> tok;     // [nnz]
   std::vector<uint32_t> bits;    // dense: [rows][words]
+  std::vector<uint16_t> rank;    // dense: [rows][words] set bits of the row before each word
 };
 
 // One step's table in HBM (plain pointers, passed to kernels by value).
@@ -50,6 +51,7 @@ struct zgr_index {
   int device = -1;
   std::vector<void*> allocations;
   uint64_t generation = 0;
+  zgr_build_times times{};  // phases of the last build and upload
 };
 
 namespace zgr {

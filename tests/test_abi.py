@@ -52,6 +52,32 @@ def test_index_argument_errors():
     L.zgr_index_free(None)  # no-op
 
 
+def test_rebuild_argument_errors():
+    L = zgr.lib()
+    ok = np.array([[0, 1], [1, 0]], np.int32)
+    h = ctypes.c_void_p()
+    tm = zgr.BuildTimes()
+    neg = zgr.BuildOpts(-1, zgr.ZGR_UPLOAD_STAGED, 0)
+    bad_mode = zgr.BuildOpts(0, 7, 0)
+    neg_stage = zgr.BuildOpts(0, zgr.ZGR_UPLOAD_STAGED, -4)
+    # checks run before any HIP call
+    assert L.zgr_index_build_host_ex(ok.ctypes.data, 2, 2, 4, None, None, ctypes.byref(neg), None,
+                                     ctypes.byref(h)) == zgr.ZGR_E_ARG
+    for o in (bad_mode, neg_stage):
+        assert L.zgr_index_upload_ex(ok.ctypes.data, 2, 2, 4, None, None, ctypes.byref(o), None,
+                                     ctypes.byref(h), None) == zgr.ZGR_E_ARG
+    assert L.zgr_index_upload_ex(ok.ctypes.data, 2, 2, 4, None, None, None, None, None, None) == zgr.ZGR_E_ARG
+    assert L.zgr_index_to_device_ex(None, None, None, None) == zgr.ZGR_E_ARG
+    assert L.zgr_index_times(None, ctypes.byref(tm)) == zgr.ZGR_E_ARG
+    idx, _ = zgr.zgr_index_build_host(ok, 4)
+    assert L.zgr_index_to_device_ex(idx.handle, None, ctypes.byref(bad_mode), None) == zgr.ZGR_E_ARG
+    assert L.zgr_index_to_device_ex(idx.handle, None, ctypes.byref(neg_stage), None) == zgr.ZGR_E_ARG
+    _expect(zgr.ZGR_E_STATE, zgr.zgr_index_device_table, idx, 1)  # host-only index
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_device_table, idx, 3)
+    t = zgr.zgr_index_times(idx)
+    assert t["threads"] == 1 and t["upload_ms"] == 0.0 and t["device_bytes"] > 0
+
+
 def test_index_stats_range():
     idx, _ = zgr.zgr_index_build_host(np.array([[0, 1], [1, 0]], np.int32), 4)
     _expect(zgr.ZGR_E_ARG, zgr.zgr_index_stats, idx, 0)

@@ -25,9 +25,9 @@ def row_prefixes(idx, L):
     return pre
 
 
-def check_against_oracle(sids, V, fmt=None, sample=None, seed=0):
+def check_against_oracle(sids, V, fmt=None, sample=None, seed=0, threads=0):
     N, L = sids.shape
-    idx, rank = zgr.zgr_index_build_host(sids, V, fmt)
+    idx, rank = zgr.zgr_index_build_host(sids, V, fmt, threads=threads)
     cat = oracle.Catalog(sids, V)
     pre = row_prefixes(idx, L)
     rng = np.random.default_rng(seed)
@@ -128,3 +128,71 @@ def test_config_catalogs_sampled(name):
     cfg = workload.CONFIGS[name]
     sids = workload.catalog(cfg)
     check_against_oracle(sids, cfg.V, cfg.fmt, sample=None if cfg.N <= 10_000 else 300)
+
+
+def _random_sids(V, L, N, seed):
+    rng = np.random.default_rng(seed)
+    codes = rng.choice(V ** L, size=min(N, V ** L), replace=False)
+    return np.stack([(codes // V ** (L - 1 - l)) % V for l in range(L)], 1).astype(np.int32)
+
+
+@pytest.mark.parametrize("V,L,N,seed", [(4, 3, 40, 1), (16, 4, 900, 2), (300, 2, 5000, 3), (2, 6, 50, 4)])
+@pytest.mark.parametrize("threads", [2, 3, 7, 64])
+def test_chunked_layout_matches_oracle(V, L, N, seed, threads):
+    """Chunk boundaries fall inside rows at every table; the chunked count /
+    offset / fill passes must still give the oracle's trie."""
+    check_against_oracle(_random_sids(V, L, N, seed), V, threads=threads)
+
+
+@pytest.mark.parametrize("fmt", [None, "D", "S"])
+def test_layout_independent_of_threads(fmt):
+    cfg = workload.CONFIGS["n1e4_v256"]
+    sids = workload.catalog(cfg)
+    f = None if fmt is None else [fmt] * cfg.L
+    ref, ref_rank = zgr.zgr_index_build_host(sids, cfg.V, f, threads=1)
+    for T in (2, 5, 16, 64):
+        idx, rank, tm = zgr.zgr_index_build_host(sids, cfg.V, f, threads=T, times=True)
+        assert tm["threads"] == T
+        assert all(tm[k] >= 0 for k in ("keys_ms", "sort_ms", "layout_ms", "encode_ms", "build_ms"))
+        assert np.array_equal(rank, ref_rank)
+        for t in range(1, cfg.L + 1):
+            assert idx.stats(t) == ref.stats(t)
+            for a, b in zip(idx.host_table(t), ref.host_table(t)):
+                assert (a is None and b is None) or np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("threads", [1, 4, 9])
+def test_chunked_errors(threads):
+    # duplicates sit at every possible chunk boundary: report the first pair
+    sids = _random_sids(16, 3, 400, 7)
+    order = np.lexsort(sids.T[::-1])
+    sids = sids[order]
+    dup = np.concatenate([sids[:200], sids[199:]])  # sorted row 199 appears twice
+    with pytest.raises(zgr.ZgrError) as e:
+        zgr.zgr_index_build_host(dup, 16, threads=threads)
+    assert e.value.status == zgr.ZGR_E_DUP_SID
+    assert "rows 199 and 200" in e.value.detail
+    bad = sids.copy()
+    bad[321, 2] = 16
+    with pytest.raises(zgr.ZgrError) as e:
+        zgr.zgr_index_build_host(bad, 16, threads=threads)
+    assert e.value.status == zgr.ZGR_E_TOKEN_RANGE and "row 321" in e.value.detail
+
+
+@pytest.mark.parametrize("threads", [1, 3])
+def test_presorted_catalog(threads):
+    """A catalog given in SID order skips the sort; item ids are then the
+    input rows.  Equal neighbours are still duplicates."""
+    cfg = workload.CONFIGS["n1e4_v256"]
+    sids = workload.catalog(cfg)
+    srt = sids[np.lexsort(sids.T[::-1])]
+    ref, _ = zgr.zgr_index_build_host(sids, cfg.V, threads=threads)
+    idx, rank = zgr.zgr_index_build_host(srt, cfg.V, threads=threads)
+    assert np.array_equal(rank, np.arange(len(srt)))
+    for t in range(1, cfg.L + 1):
+        for a, b in zip(idx.host_table(t), ref.host_table(t)):
+            assert (a is None and b is None) or np.array_equal(a, b)
+    dup = np.concatenate([srt[:50], srt[49:]])
+    with pytest.raises(zgr.ZgrError) as e:
+        zgr.zgr_index_build_host(dup, cfg.V, threads=threads)
+    assert e.value.status == zgr.ZGR_E_DUP_SID and "rows 49 and 50" in e.value.detail
