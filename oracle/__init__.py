@@ -61,6 +61,10 @@ def lib():
         L.orc_node.argtypes = [_P, _P, ctypes.c_int32]
         L.orc_legal.restype = ctypes.c_int64
         L.orc_legal.argtypes = [_P, _P, ctypes.c_int32, _P, ctypes.c_int64]
+        L.orc_step_mode.restype = ctypes.c_int
+        L.orc_step_mode.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32,
+                                    ctypes.c_int32, _P, _P, _P, ctypes.c_int32, ctypes.c_int64,
+                                    _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.orc_step.restype = ctypes.c_int
         L.orc_step.argtypes = [_P, ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                ctypes.c_int32, ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -71,6 +75,11 @@ def lib():
 
 class OracleError(RuntimeError):
     pass
+
+
+# Decoding modes (oracle.c, orc_step_mode): the method, and the two orders it
+# is compared with.
+MODES = {"filter_first": 0, "score_first": 1, "unconstrained": 2}
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -132,10 +141,11 @@ class Catalog:
         return int(lib().orc_input_row(self._h, item))
 
     def step(self, t: int, W: np.ndarray, prefix: np.ndarray, cum: np.ndarray, h: np.ndarray,
-             K: int) -> StepResult:
+             K: int, mode: str = "filter_first") -> StepResult:
         """One step of one request.  W [V, d] float32 (stored values widened),
         prefix [k_in, t-1] int32, cum [k_in] (float64; -inf = dead beam),
-        h [k_in, d] float32."""
+        h [k_in, d] float32.  mode: a key of MODES."""
+        m = MODES[mode]
         W = np.ascontiguousarray(W, dtype=np.float32)
         h = np.ascontiguousarray(h, dtype=np.float32)
         cum = np.ascontiguousarray(cum, dtype=np.float64)
@@ -146,7 +156,7 @@ class Catalog:
         cap = 0
         for k in range(k_in):
             if np.isfinite(cum[k]):
-                cap += len(self.legal(prefix[k]))
+                cap += self.V if m == 2 else len(self.legal(prefix[k]))
         cap = max(cap, 1)
         cb = np.empty(cap, np.int32)
         ct = np.empty(cap, np.int32)
@@ -158,7 +168,7 @@ class Catalog:
         sn = np.empty(K, np.int64)
         n_cand = ctypes.c_int64()
         n_sel = ctypes.c_int32()
-        rc = lib().orc_step(self._h, t, W.ctypes.data, d, k_in,
+        rc = lib().orc_step_mode(self._h, m, t, W.ctypes.data, d, k_in,
                             prefix.ctypes.data if t > 1 else None, cum.ctypes.data, h.ctypes.data,
                             K, cap, cb.ctypes.data, ct.ctypes.data, cl.ctypes.data, cs.ctypes.data,
                             ctypes.byref(n_cand), sb.ctypes.data, st.ctypes.data, ss.ctypes.data,
@@ -181,11 +191,14 @@ HiddenFn = Callable[[int, int, np.ndarray], np.ndarray]
 
 
 def decode(cat: Catalog, W: List[np.ndarray], hidden: HiddenFn, request: int, K: int,
-           top_k: Optional[int] = None, keep_steps: bool = False) -> DecodeResult:
-    """Filter-first beam search for one request.
+           top_k: Optional[int] = None, keep_steps: bool = False,
+           mode: str = "filter_first") -> DecodeResult:
+    """Beam search for one request (filter-first unless `mode` says otherwise).
 
     W[t-1] is the step-t weight matrix [V, d] (float32 values as stored);
     hidden(request, t, prefixes [k_in, t-1]) returns [k_in, d] float32.
+    In the unconstrained mode a returned SID need not be a catalog item: its
+    item id is then -1.
     """
     top_k = K if top_k is None else top_k
     L = cat.L
@@ -195,7 +208,7 @@ def decode(cat: Catalog, W: List[np.ndarray], hidden: HiddenFn, request: int, K:
     res = None
     for t in range(1, L + 1):
         h = hidden(request, t, prefixes)
-        res = cat.step(t, W[t - 1], prefixes, cum, h, K)
+        res = cat.step(t, W[t - 1], prefixes, cum, h, K, mode)
         if keep_steps:
             steps.append(dict(prefix=prefixes.copy(), cum=cum.copy(), h=h, res=res))
         k = len(res.sel_beam)

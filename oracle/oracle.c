@@ -31,6 +31,12 @@
  * equals p: one contiguous run, found by binary search, already in token
  * order.  A node's number is its index in depth_keys[t].
  *
+ * Two more modes, for comparisons only (orc_step_mode): score-first, where
+ * the softmax denominator covers the whole codebook before the illegal
+ * tokens are dropped ("does filter-first change results" section), and
+ * unconstrained search, where every codebook token is a candidate ("is it
+ * really better" section).
+ *
  * Selection: every candidate of a request is ranked by (cumulative score
  * descending, beam index ascending, token ascending) and the first K are kept
  * in that order; fewer than K candidates keep them all.  The fixed tie-break
@@ -211,7 +217,17 @@ static int cmp_cand(const void* a, const void* b) {
 }
 
 /*
- * One decode step t (1-based) of one request.
+ * One decode step t (1-based) of one request, in one of three modes:
+ *   ORC_FILTER_FIRST (0)  the method: score only the legal tokens, softmax
+ *                         over the legal tokens only ("overall pipeline").
+ *   ORC_SCORE_FIRST (1)   the order the method replaces: every codebook token
+ *                         is scored and the softmax denominator covers all V
+ *                         of them; only then are the illegal tokens dropped
+ *                         ("does filter-first change results" section).
+ *   ORC_UNCONSTRAINED (2) the speed reference: softmax over all V tokens and
+ *                         every token is a candidate; the catalog is not
+ *                         consulted, so a code need not be a real item ("is
+ *                         it really better" section).
  *   W      [V][d]   step-t weights (values as stored, widened to float)
  *   prefix [k_in][t-1] each beam's tokens so far; cum [k_in] its cumulative
  *          log-prob; h [k_in][d] its hidden vector.  Beams are given in rank
@@ -219,30 +235,39 @@ static int cmp_cand(const void* a, const void* b) {
  * All candidates are written to cand_* (beam, token, log-prob, new score) in
  * beam order then token order; at most cap of them; *n_cand gets the full count.
  * The selection (at most K) goes to sel_* in rank order with the node number
- * of the extended prefix (the next row; at t = L the item id); *n_sel its size.
+ * of the extended prefix (the next row; at t = L the item id; -1 when the
+ * extended prefix is not in the catalog, which only the unconstrained mode
+ * produces); *n_sel its size.
  * Returns 0, or 1 on bad arguments, 4 out of memory.
  */
-int orc_step(const orc_catalog* c, int32_t t, const float* W, int32_t d, int32_t k_in,
-             const int32_t* prefix, const double* cum, const float* h, int32_t K, int64_t cap,
-             int32_t* cand_beam, int32_t* cand_token, double* cand_logp, double* cand_score,
-             int64_t* n_cand, int32_t* sel_beam, int32_t* sel_token, double* sel_score,
-             int64_t* sel_node, int32_t* n_sel) {
+int orc_step_mode(const orc_catalog* c, int32_t mode, int32_t t, const float* W, int32_t d,
+                  int32_t k_in, const int32_t* prefix, const double* cum, const float* h,
+                  int32_t K, int64_t cap, int32_t* cand_beam, int32_t* cand_token,
+                  double* cand_logp, double* cand_score, int64_t* n_cand, int32_t* sel_beam,
+                  int32_t* sel_token, double* sel_score, int64_t* sel_node, int32_t* n_sel) {
   if (!c || t < 1 || t > c->L || !W || d < 1 || k_in < 1 || !cum || !h || K < 1) return 1;
+  if (mode < 0 || mode > 2) return 1;
   if (t > 1 && !prefix) return 1;
   const int32_t plen = t - 1;
   int32_t* legal = (int32_t*)malloc((size_t)c->V * sizeof(int32_t));
   double* z = (double*)malloc((size_t)c->V * sizeof(double));
+  double* lp = (double*)malloc((size_t)c->V * sizeof(double));
   int64_t total = 0;
   for (int32_t k = 0; k < k_in; ++k) {
     if (isinf(cum[k]) && cum[k] < 0) continue;
+    if (mode != 0) {  /* at most V candidates per beam */
+      total += c->V;
+      continue;
+    }
     const int64_t n = orc_legal(c, prefix ? prefix + (int64_t)k * plen : NULL, plen, legal, c->V);
     total += (n > 0) ? n : 0;
   }
   orc_cand* all = (orc_cand*)malloc((size_t)(total > 0 ? total : 1) * sizeof(orc_cand));
   int32_t* ext = (int32_t*)malloc((size_t)(t + 1) * sizeof(int32_t));
-  if (!legal || !z || !all || !ext) {
+  if (!legal || !z || !lp || !all || !ext) {
     free(legal);
     free(z);
+    free(lp);
     free(all);
     free(ext);
     return 4;
@@ -251,24 +276,51 @@ int orc_step(const orc_catalog* c, int32_t t, const float* W, int32_t d, int32_t
   for (int32_t k = 0; k < k_in; ++k) {
     if (isinf(cum[k]) && cum[k] < 0) continue;
     const int32_t* pk = prefix ? prefix + (int64_t)k * plen : NULL;
-    const int64_t n = orc_legal(c, pk, plen, legal, c->V);
-    if (n <= 0) continue;
-    /* score only the legal tokens */
     const float* hk = h + (int64_t)k * d;
-    double zmax = -INFINITY;
-    for (int64_t j = 0; j < n; ++j) {
-      const float* w = W + (int64_t)legal[j] * d;
-      double acc = 0.0;
-      for (int32_t i = 0; i < d; ++i) acc += (double)w[i] * (double)hk[i];
-      z[j] = acc;
-      if (acc > zmax) zmax = acc;
+    int64_t n;
+    if (mode == 0) {
+      n = orc_legal(c, pk, plen, legal, c->V);
+      if (n <= 0) continue;
+      /* score only the legal tokens */
+      double zmax = -INFINITY;
+      for (int64_t j = 0; j < n; ++j) {
+        const float* w = W + (int64_t)legal[j] * d;
+        double acc = 0.0;
+        for (int32_t i = 0; i < d; ++i) acc += (double)w[i] * (double)hk[i];
+        z[j] = acc;
+        if (acc > zmax) zmax = acc;
+      }
+      /* log-softmax over the legal tokens only */
+      double s = 0.0;
+      for (int64_t j = 0; j < n; ++j) s += exp(z[j] - zmax);
+      const double lse = zmax + log(s);
+      for (int64_t j = 0; j < n; ++j) lp[j] = z[j] - lse;
+    } else {
+      /* score every token of the codebook: z[v] = W[v] . h */
+      double zmax_all = -INFINITY;
+      for (int32_t v = 0; v < c->V; ++v) {
+        const float* wv = W + (int64_t)v * d;
+        double dot = 0.0;
+        for (int32_t i = 0; i < d; ++i) dot += (double)wv[i] * (double)hk[i];
+        z[v] = dot;
+        if (dot > zmax_all) zmax_all = dot;
+      }
+      /* log-softmax over all V tokens */
+      double s_all = 0.0;
+      for (int32_t v = 0; v < c->V; ++v) s_all += exp(z[v] - zmax_all);
+      const double lse_all = zmax_all + log(s_all);
+      if (mode == 1) {
+        /* then drop the illegal tokens */
+        n = orc_legal(c, pk, plen, legal, c->V);
+        if (n <= 0) continue;
+      } else {
+        n = c->V;
+        for (int32_t v = 0; v < c->V; ++v) legal[v] = v;
+      }
+      for (int64_t j = 0; j < n; ++j) lp[j] = z[legal[j]] - lse_all;
     }
-    /* log-softmax over the legal tokens only */
-    double s = 0.0;
-    for (int64_t j = 0; j < n; ++j) s += exp(z[j] - zmax);
-    const double lse = zmax + log(s);
     for (int64_t j = 0; j < n; ++j) {
-      const double logp = z[j] - lse;
+      const double logp = lp[j];
       const double score = cum[k] + logp;
       if (m_all < cap) {
         if (cand_beam) cand_beam[m_all] = k;
@@ -298,7 +350,19 @@ int orc_step(const orc_catalog* c, int32_t t, const float* W, int32_t d, int32_t
   if (n_sel) *n_sel = keep;
   free(legal);
   free(z);
+  free(lp);
   free(all);
   free(ext);
   return 0;
+}
+
+/* The method's step (filter-first). */
+int orc_step(const orc_catalog* c, int32_t t, const float* W, int32_t d, int32_t k_in,
+             const int32_t* prefix, const double* cum, const float* h, int32_t K, int64_t cap,
+             int32_t* cand_beam, int32_t* cand_token, double* cand_logp, double* cand_score,
+             int64_t* n_cand, int32_t* sel_beam, int32_t* sel_token, double* sel_score,
+             int64_t* sel_node, int32_t* n_sel) {
+  return orc_step_mode(c, 0, t, W, d, k_in, prefix, cum, h, K, cap, cand_beam, cand_token,
+                       cand_logp, cand_score, n_cand, sel_beam, sel_token, sel_score, sel_node,
+                       n_sel);
 }

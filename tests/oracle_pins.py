@@ -200,8 +200,9 @@ def pin_full_product_equals_unconstrained():
         cat = oracle.Catalog(grid.astype(np.int32), V)
         W = weights_of(cfg)
         hid = hidden_fn(cfg)
-        for request in (0, 1):
-            res = oracle.decode(cat, W, hid, request, K=K)
+        for request, mode in [(0, "filter_first"), (1, "filter_first"), (0, "score_first"),
+                              (1, "unconstrained")]:
+            res = oracle.decode(cat, W, hid, request, K=K, mode=mode)
             want_sid, want_score = _numpy_beam_search(V, L, K, W, hid, request)
             n = len(want_score)
             assert np.array_equal(res.sid[:n], want_sid)
@@ -209,6 +210,118 @@ def pin_full_product_equals_unconstrained():
             # item id of a full-product SID is its base-V value (lexicographic rank)
             vals = (want_sid * (V ** np.arange(L - 1, -1, -1))).sum(1)
             assert res.item[:n].tolist() == vals.tolist()
+
+
+def pin_modes_against_scipy_log_softmax():
+    """Score-first and unconstrained log-probs are scipy's log_softmax over the
+    whole codebook (legal tokens only, resp. every token); filter-first is the
+    same scores renormalised over the legal set."""
+    V, d = 16, 12
+    cfg = small_cfg(V=V, d=d, L=3, N=200)
+    sids = random_catalog(V, 3, 200, 11)
+    cat = oracle.Catalog(sids, V)
+    W = weights_of(cfg)
+    hid = hidden_fn(cfg)
+    pre = np.unique(sids[:, :2], axis=0)[:10]
+    cum = np.linspace(-3.0, 0.0, len(pre))
+    cum[3] = -np.inf  # a dead beam contributes nothing in any mode
+    H = hid(0, 3, pre)
+    r = {m: cat.step(3, W[2], pre, cum, H, K=1000, mode=m) for m in oracle.MODES}
+    for k in range(len(pre)):
+        for m in oracle.MODES:
+            if k == 3:
+                assert not np.any(r[m].cand_beam == 3)
+        if k == 3:
+            continue
+        legal = cat.legal(pre[k])
+        full = log_softmax(W[2].astype(np.float64) @ H[k].astype(np.float64))
+        sf, un, ff = (r[m] for m in ("score_first", "unconstrained", "filter_first"))
+        sel = sf.cand_beam == k
+        assert np.array_equal(sf.cand_token[sel], legal)
+        assert np.allclose(sf.cand_logp[sel], full[legal], rtol=0, atol=1e-12)
+        assert np.allclose(sf.cand_score[sel], cum[k] + full[legal], rtol=0, atol=1e-12)
+        sel_u = un.cand_beam == k
+        assert np.array_equal(un.cand_token[sel_u], np.arange(V))
+        assert np.allclose(un.cand_logp[sel_u], full, rtol=0, atol=1e-12)
+        assert abs(math.fsum(np.exp(un.cand_logp[sel_u])) - 1.0) < 1e-12
+        # renormalising the score-first log-probs over the legal set gives filter-first
+        lp_ff = ff.cand_logp[ff.cand_beam == k]
+        assert np.allclose(lp_ff, full[legal] - logsumexp(full[legal]), rtol=0, atol=1e-12)
+    # W = 0: every codebook token has probability 1/V before filtering
+    Z = np.zeros((V, d), np.float32)
+    for m in ("score_first", "unconstrained"):
+        r0 = cat.step(3, Z, pre, np.zeros(len(pre)), H, K=1000, mode=m)
+        assert np.all(np.abs(r0.cand_logp + math.log(V)) <= 1e-15 * math.log(V))
+    # the selection is the best K of the candidates, in the fixed order
+    for m in oracle.MODES:
+        rr = cat.step(3, W[2], pre, cum, H, K=7, mode=m)
+        order = sorted(range(len(rr.cand_score)),
+                       key=lambda i: (-rr.cand_score[i], rr.cand_beam[i], rr.cand_token[i]))[:7]
+        assert rr.sel_beam.tolist() == [int(rr.cand_beam[i]) for i in order]
+        assert rr.sel_token.tolist() == [int(rr.cand_token[i]) for i in order]
+
+
+def _exhaustive_all_v(codes, V, W, hid, request):
+    """Score every code independently: sum over steps of its token's
+    log-softmax over the whole codebook (scipy)."""
+    L = codes.shape[1]
+    out = []
+    for s in codes.tolist():
+        tot = 0.0
+        for t in range(L):
+            h = hid(request, t + 1, np.array([s[:t]], np.int32).reshape(1, t))[0].astype(np.float64)
+            tot += log_softmax(W[t].astype(np.float64) @ h)[s[t]]
+        out.append(tot)
+    return np.array(out)
+
+
+def pin_modes_exhaustive():
+    """Beam covering everything: score-first ranks every catalog item by its
+    summed all-codebook log-probs; unconstrained ranks every one of the V^L
+    codes that way, real items keeping their id and other codes getting -1."""
+    V, L, N, d, seed = 4, 3, 25, 6, 41
+    cfg = small_cfg(V=V, d=d, L=L, N=N, seed=seed)
+    sids = random_catalog(V, L, N, seed)
+    cat = oracle.Catalog(sids, V)
+    W = weights_of(cfg)
+    hid = hidden_fn(cfg)
+    members = {tuple(x): i for i, x in enumerate(sids.tolist())}
+    for request in (0, 2):
+        res = oracle.decode(cat, W, hid, request, K=N, mode="score_first")
+        ex = _exhaustive_all_v(sids, V, W, hid, request)
+        order = np.argsort(-ex, kind="stable")
+        assert [cat.input_row(int(i)) for i in res.item] == order.tolist()
+        assert np.allclose(res.score, ex[order], rtol=0, atol=1e-12)
+        grid = np.stack(np.meshgrid(*[np.arange(V)] * L, indexing="ij"), -1).reshape(-1, L)
+        res = oracle.decode(cat, W, hid, request, K=V ** L, mode="unconstrained")
+        ex = _exhaustive_all_v(grid, V, W, hid, request)
+        order = np.argsort(-ex, kind="stable")
+        assert np.array_equal(res.sid, grid[order])
+        assert np.allclose(res.score, ex[order], rtol=0, atol=1e-12)
+        for it, sid in zip(res.item.tolist(), res.sid.tolist()):
+            if tuple(sid) in members:
+                assert it >= 0 and cat.input_row(it) == members[tuple(sid)]
+            else:
+                assert it == -1
+
+
+def pin_unconstrained_leaves_the_catalog():
+    """On a sparse catalog unconstrained search returns codes that are not
+    items (id -1), while filter-first and score-first return only items."""
+    cfg = small_cfg(V=32, d=16, L=3, N=300, K=16, seed=51)
+    sids = random_catalog(32, 3, 300, 51)
+    cat = oracle.Catalog(sids, 32)
+    W = weights_of(cfg)
+    hid = hidden_fn(cfg)
+    members = set(map(tuple, sids.tolist()))
+    un = oracle.decode(cat, W, hid, 0, K=16, mode="unconstrained")
+    inval = [tuple(x) not in members for x in un.sid.tolist()]
+    assert any(inval)
+    assert all((it == -1) == bad for it, bad in zip(un.item.tolist(), inval))
+    for m in ("filter_first", "score_first"):
+        res = oracle.decode(cat, W, hid, 0, K=16, mode=m)
+        assert np.all(res.item >= 0)
+        assert all(tuple(x) in members for x in res.sid.tolist())
 
 
 def pin_tie_break():

@@ -31,6 +31,13 @@ MUTANTS = {
                         "const int64_t hi = lower_bound_u64(a, n, (p + 1) << c->bits) - 1;"),
     "denominator_sum_wrong": ("for (int64_t j = 0; j < n; ++j) s += exp(z[j] - zmax);",
                               "for (int64_t j = 1; j < n; ++j) s += exp(z[j] - zmax);"),
+    "all_v_max_dropped": ("const double lse_all = zmax_all + log(s_all);",
+                          "const double lse_all = log(s_all);"),
+    "all_v_sum_skips_first": ("for (int32_t v = 0; v < c->V; ++v) s_all += exp(z[v] - zmax_all);",
+                              "for (int32_t v = 1; v < c->V; ++v) s_all += exp(z[v] - zmax_all);"),
+    "score_first_keeps_illegal": ("if (mode == 1) {", "if (mode == 3) {"),
+    "unconstrained_drops_last_token": ("n = c->V;\n", "n = c->V - 1;\n"),
+    "score_first_uses_slot": ("lp[j] = z[legal[j]] - lse_all;", "lp[j] = z[j] - lse_all;"),
     "keep_one_more": ("const int32_t keep = (m_all < K) ? (int32_t)m_all : K;",
                       "const int32_t keep = (m_all < K) ? (int32_t)m_all : K - 1;"),
 }
