@@ -185,6 +185,9 @@ class Workload:
             return "hbm", float(b)
         if kernel == "units":
             return "hbm", float(M * 16)
+        if kernel == "norm":
+            # every live beam's row of V scores read once
+            return "hbm", float(live * cfg.V * 4 + M * 8)
         raise ValueError(kernel)
 
 

@@ -246,6 +246,32 @@ int32_t zgr_plan_choice(const zgr_plan* plan, int32_t t, int32_t* proj, float* u
  * resume a plan exported by zgr_plan_choice without a new warm-up. */
 int32_t zgr_plan_set_choice(zgr_plan* plan, int32_t t, int32_t proj);
 
+/*
+ * Decoding mode of a plan (default ZGR_MODE_FILTER_FIRST), applied by every
+ * later zgr_step / zgr_decode.  The other two are the comparisons of the
+ * ZeroGR description:
+ *   ZGR_MODE_SCORE_FIRST  ("does filter-first change results"): every codebook
+ *       token is scored (full projection at every step, whatever the frozen
+ *       choice), the log-softmax denominator covers all V tokens, and only
+ *       then are the candidates restricted to the legal tokens.  Inputs and
+ *       outputs as in filter-first; cum_out and slot_dbg carry
+ *       log-probabilities normalised over the whole codebook.
+ *   ZGR_MODE_UNCONSTRAINED ("is it really better"): full projection,
+ *       log-softmax over all V tokens, and every token is a candidate of every
+ *       live beam; the index is not read during the steps, so a code need not
+ *       be a catalog item.  row_in >= 0 marks a live beam (its value is not
+ *       used), row_out is 0 for every chosen candidate (-1 = none), and
+ *       slot_dbg has V slots per beam (slot = token).  zgr_decode returns the
+ *       item id of each final code that is a catalog SID and -1 for the
+ *       others (sid_out still holds the code).
+ * Errors: ZGR_E_ARG.
+ */
+#define ZGR_MODE_FILTER_FIRST 0
+#define ZGR_MODE_SCORE_FIRST 1
+#define ZGR_MODE_UNCONSTRAINED 2
+int32_t zgr_plan_set_mode(zgr_plan* plan, int32_t mode);
+int32_t zgr_plan_mode(const zgr_plan* plan, int32_t* mode);
+
 void zgr_plan_free(zgr_plan* plan);
 
 /*
@@ -298,7 +324,8 @@ int32_t zgr_plan_status(zgr_plan* plan, void* stream);
                                    next rows, prefixes (and, on light sparse steps, the
                                    selective projection itself); a request split over several
                                    blocks adds a second, merging dispatch */
-#define ZGR_KERNEL_COUNT 4
+#define ZGR_KERNEL_NORM 4       /* log-sum-exp over the whole codebook (score-first mode) */
+#define ZGR_KERNEL_COUNT 5
 
 /* Per-kernel timing: repeat > 0 turns it on, 0 off; counters are reset.
  * While on, every kernel launch of zgr_step / zgr_decode is issued `repeat`

@@ -26,7 +26,10 @@ ZGR_FMT_AUTO, ZGR_FMT_DENSE, ZGR_FMT_SPARSE = 0, 1, 2
 ZGR_PROJ_AUTO, ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE = 0, 1, 2
 ZGR_UPLOAD_STAGED, ZGR_UPLOAD_DIRECT = 0, 1
 UPLOAD_CODES = {"staged": ZGR_UPLOAD_STAGED, "direct": ZGR_UPLOAD_DIRECT}
-KERNELS = ["units", "selective", "gemm", "request"]
+KERNELS = ["units", "selective", "gemm", "request", "norm"]
+ZGR_MODE_FILTER_FIRST, ZGR_MODE_SCORE_FIRST, ZGR_MODE_UNCONSTRAINED = 0, 1, 2
+MODE_CODES = {"filter_first": ZGR_MODE_FILTER_FIRST, "score_first": ZGR_MODE_SCORE_FIRST,
+              "unconstrained": ZGR_MODE_UNCONSTRAINED}
 
 DTYPE_CODES = {"f32": ZGR_F32, "bf16": ZGR_BF16, "f16": ZGR_F16}
 FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR_FMT_SPARSE}
@@ -106,6 +109,8 @@ def lib() -> ctypes.CDLL:
             "zgr_plan_choice": (_I32, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(ctypes.c_float),
                                        ctypes.POINTER(ctypes.c_float)]),
             "zgr_plan_set_choice": (_I32, [_P, _I32, _I32]),
+            "zgr_plan_set_mode": (_I32, [_P, _I32]),
+            "zgr_plan_mode": (_I32, [_P, ctypes.POINTER(_I32)]),
             "zgr_plan_free": (None, [_P]),
             "zgr_step": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P]),
             "zgr_decode": (_I32, [_P, HIDDEN_FN, _P, _I32, _P, _P, _P, _P]),
@@ -393,6 +398,19 @@ def zgr_plan_choice(plan: Plan, t: int):
 def zgr_plan_set_choice(plan: Plan, t: int, proj):
     code = PROJ_CODES[proj] if isinstance(proj, str) else int(proj)
     _check(lib().zgr_plan_set_choice(plan.handle, t, code))
+
+
+def zgr_plan_set_mode(plan: Plan, mode):
+    """Decoding mode: 'filter_first' (the method), 'score_first' or
+    'unconstrained' (the comparisons), or a ZGR_MODE_* code."""
+    code = MODE_CODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().zgr_plan_set_mode(plan.handle, code))
+
+
+def zgr_plan_mode(plan: Plan) -> str:
+    m = _I32()
+    _check(lib().zgr_plan_mode(plan.handle, ctypes.byref(m)))
+    return {v: k for k, v in MODE_CODES.items()}[m.value]
 
 
 def zgr_plan_free(plan: Plan):

@@ -43,6 +43,8 @@ struct zgr_plan {
   int32_t L = 0, V = 0, d = 0, B = 0, K = 0, dtype = 0;
   std::vector<const void*> W;
   int32_t choice[zgr::kMaxL] = {0};
+  int32_t mode = ZGR_MODE_FILTER_FIRST;
+  zgr::DevTable all_tab{};  // one row, every token legal (unconstrained mode)
   float us_full[zgr::kMaxL], us_sel[zgr::kMaxL];
   int n_cu = 256;
   // HBM scratch
@@ -216,8 +218,9 @@ bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
 int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool heavy_step) {
   if (a.k_in < 2) return 1;
   const HostTable& h = p->idx->host[a.t - 1];
-  const double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
-  const double est_c = a.k_in * std::min<double>(mean_n, h.stride);
+  double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
+  if (a.tab.fmt == kFmtAll) mean_n = p->V;
+  const double est_c = a.k_in * std::min<double>(mean_n, a.tab.stride);
   if (!heavy_step && est_c <= 2048.0) return 1;
   // enough parts to cover the compute units, and enough that a part's
   // candidates (estimated) fit the LDS key array
@@ -233,6 +236,32 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
   const int t = a.t;
   hipError_t e;
   int zmode;
+  if (p->mode != ZGR_MODE_FILTER_FIRST) {
+    // score-first and unconstrained: every token is scored (token-indexed
+    // rows); score-first normalises over the whole codebook and then keeps the
+    // legal tokens, unconstrained keeps every token (the all-legal row, whose
+    // legal rank is the token)
+    const bool unc = p->mode == ZGR_MODE_UNCONSTRAINED;
+    if (unc) a.tab = p->all_tab;
+    a.ldz = p->V;
+    a.plain_z = true;
+    e = prof_launch(p, ZGR_KERNEL_GEMM, t, s, [&] { return launch_full_projection(a, s); });
+    if (e != hipSuccess) return hip_fail(e, "full projection launch");
+    if (!unc) {
+      a.lse_ext = p->lse;
+      e = prof_launch(p, ZGR_KERNEL_NORM, t, s, [&] { return launch_row_lse(a, s); });
+      if (e != hipSuccess) return hip_fail(e, "codebook log-sum-exp launch");
+    }
+    zmode = unc ? 1 : 0;
+    a.parts = request_parts(p, a, true);
+    e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
+    if (e != hipSuccess) return hip_fail(e, "request step launch");
+    if (a.parts > 1) {
+      e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_merge(a, s); });
+      if (e != hipSuccess) return hip_fail(e, "request merge launch");
+    }
+    return ZGR_OK;
+  }
   // z layout: by legal rank on dense steps and on selective sparse steps,
   // token-indexed after a full projection of a sparse step
   if (proj == ZGR_PROJ_FULL) {
@@ -446,9 +475,39 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   }
   A((void**)&p->parent, (size_t)MK * 4);
   A((void**)&p->token, (size_t)MK * 4);
+  // the all-legal row: row_ptr {0, V}, every bit set, rank directory 32 * word
+  const int32_t words = (p->V + 31) / 32;
+  void *all_rp = nullptr, *all_bits = nullptr, *all_rank = nullptr;
+  A(&all_rp, 8);
+  A(&all_bits, (size_t)words * 4);
+  A(&all_rank, (size_t)words * 2);
   if (rc != ZGR_OK) {
     zgr_plan_free(p);
     return rc;
+  }
+  {
+    const int32_t rp_h[2] = {0, p->V};
+    std::vector<uint32_t> bits_h(words, 0xFFFFFFFFu);
+    if (p->V % 32) bits_h[words - 1] = (1u << (p->V % 32)) - 1u;
+    std::vector<uint16_t> rank_h(words);
+    for (int32_t w = 0; w < words; ++w) rank_h[w] = (uint16_t)(32 * w);
+    e = hipMemcpy(all_rp, rp_h, 8, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(all_bits, bits_h.data(), (size_t)words * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(all_rank, rank_h.data(), (size_t)words * 2, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      zgr_plan_free(p);
+      return hip_fail(e, "all-legal row upload");
+    }
+    DevTable& at = p->all_tab;
+    at.fmt = kFmtAll;
+    at.stride = p->V;
+    at.words = words;
+    at.V = p->V;
+    at.rows = 1;
+    at.row_ptr = (const int32_t*)all_rp;
+    at.tok = nullptr;
+    at.bits = (const uint32_t*)all_bits;
+    at.rank = (const uint16_t*)all_rank;
   }
   e = hipMemsetAsync(p->err, 0, 4, s);
   if (e == hipSuccess) e = hipMemsetAsync(p->prefix[0], 0xFF, (size_t)MK * p->L * 4, s);
@@ -507,6 +566,20 @@ int32_t zgr_plan_set_choice(zgr_plan* p, int32_t t, int32_t proj) {
   if (proj != ZGR_PROJ_FULL && proj != ZGR_PROJ_SELECTIVE)
     return fail(ZGR_E_ARG, "zgr_plan_set_choice: proj must be FULL or SELECTIVE");
   p->choice[t - 1] = proj;
+  return ZGR_OK;
+}
+
+int32_t zgr_plan_set_mode(zgr_plan* p, int32_t mode) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_plan_set_mode: null plan");
+  if (mode < ZGR_MODE_FILTER_FIRST || mode > ZGR_MODE_UNCONSTRAINED)
+    return fail(ZGR_E_ARG, "zgr_plan_set_mode: unknown mode");
+  p->mode = mode;
+  return ZGR_OK;
+}
+
+int32_t zgr_plan_mode(const zgr_plan* p, int32_t* mode) {
+  if (!p || !mode) return fail(ZGR_E_ARG, "zgr_plan_mode: null argument");
+  *mode = p->mode;
   return ZGR_OK;
 }
 
@@ -570,7 +643,13 @@ int32_t zgr_decode(zgr_plan* p, zgr_hidden_fn hidden_fn, void* user, int32_t top
   int cur = 0;
   const int32_t rc = decode_impl(p, hidden_fn, user, s, false, nullptr, nullptr, &cur);
   if (rc != ZGR_OK) return rc;
-  hipError_t e = launch_decode_final(p->row[cur], p->cum[cur], p->prefix[cur], p->B, p->K, p->L,
+  hipError_t e = hipSuccess;
+  if (p->mode == ZGR_MODE_UNCONSTRAINED) {
+    // the codes were produced without the filter: look each one up
+    e = launch_lookup_items(p->idx->dev, p->L, p->prefix[cur], p->cum[cur], p->B * p->K, p->row[cur], s);
+    if (e != hipSuccess) return hip_fail(e, "item lookup launch");
+  }
+  e = launch_decode_final(p->row[cur], p->cum[cur], p->prefix[cur], p->B, p->K, p->L,
                                      top_k, item_out, sid_out, score_out, s);
   if (e != hipSuccess) return hip_fail(e, "decode final launch");
   return read_device_flag(p, s);

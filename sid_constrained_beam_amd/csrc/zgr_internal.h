@@ -13,6 +13,9 @@
 namespace zgr {
 
 constexpr int kMaxL = 8;
+// Internal table format: one row in which every codebook token is legal (the
+// unconstrained mode); laid out like a dense row.
+constexpr int32_t kFmtAll = 3;
 
 // One step's table on the host.
 struct HostTable {
@@ -89,6 +92,8 @@ struct StepArgs {
   int32_t* nlegal;      // [M]
   int32_t* unit_start;  // [M + 1]
   float* lse;           // [M] per-beam log-sum-exp over legal tokens
+  float* lse_ext;       // [M] or null: normaliser given to the request kernel (score-first)
+  bool plain_z;         // full projection writes token-indexed rows even on dense steps
   int32_t parts;        // blocks per request in the request kernel (1 = no merge)
   uint64_t* part_keys;  // [B * parts][K] best keys of each part
   int32_t* part_cnt;    // [B * parts]
@@ -106,6 +111,11 @@ constexpr int kSelCapHost = 14336;  // candidates whose keys fit the request ker
 hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s);
 // after launch_request_step with a.parts > 1: the per-request merge of the parts
 hipError_t launch_request_merge(const StepArgs& a, hipStream_t s);
+// score-first: log-sum-exp over all V token-indexed scores of each live beam into a.lse_ext
+hipError_t launch_row_lse(const StepArgs& a, hipStream_t s);
+// item id of each final SID by a walk of the L tables (-1 if not in the catalog)
+hipError_t launch_lookup_items(const DevTable* tabs, int32_t L, const int32_t* prefix, const float* cum,
+                               int32_t n, int32_t* item, hipStream_t s);
 hipError_t launch_decode_init(int32_t* row, float* cum, int32_t B, int32_t K, hipStream_t s);
 hipError_t launch_decode_final(const int32_t* row, const float* cum, const int32_t* prefix,
                                int32_t B, int32_t K, int32_t L, int32_t top_k, int64_t* item_out,

@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     int32_t* __restrict__ part_cnt, int32_t* __restrict__ parent_out,
     int32_t* __restrict__ token_out, int32_t* __restrict__ row_out, float* __restrict__ cum_out,
     const int32_t* __restrict__ prefix_in, int32_t* __restrict__ prefix_out,
-    float* __restrict__ slot_dbg, int32_t* __restrict__ err) {
+    float* __restrict__ slot_dbg, const float* __restrict__ lse_ext, int32_t* __restrict__ err) {
   constexpr int NT = kSelThreads;
   constexpr bool TOKEN_IDX = (MODE == kZToken);
   constexpr bool MERGE = (MODE == kZParts);
@@ -454,7 +454,8 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   const int blo = MERGE ? 0 : min(k_in, part * kp);
   const int nloc = MERGE ? k_in : min(k_in, blo + kp) - blo;
   const int b0 = q * k_in + blo;
-  const bool dense = tab.fmt == ZGR_FMT_DENSE;
+  const bool dense = tab.fmt != ZGR_FMT_SPARSE;
+  const bool all_legal = tab.fmt == kFmtAll;
   const uint32_t S = (uint32_t)tab.stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
@@ -462,6 +463,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   int cnt = 0, items = 0;
   if ((int)threadIdx.x < nloc) {
     int r = row_in[b0 + threadIdx.x];
+    if (all_legal && r > 0) r = 0;  // every live beam has the one all-legal row
     int base = 0;
     if (r >= 0 && r < tab.rows) {
       base = tab.row_ptr[r];
@@ -593,6 +595,22 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
             }
           }
         }
+      } else if (TOKEN_IDX) {
+        // dense, token-indexed scores: walk the row's bitmap words; a set
+        // bit's legal rank is the word's directory entry plus the bits below
+        const int64_t rw = (int64_t)r3 * tab.words;
+        for (int w = lb; w < tab.words; w += LPB) {
+          uint32_t x = tab.bits[rw + w];
+          int j = at + tab.rank[rw + w];
+          while (x) {
+            const int v = (w << 5) + __ffs(x) - 1;
+            x &= x - 1;
+            const float zv = z3[v];
+            acc_lse(zv);
+            if (store) keys[j] = ((uint64_t)__float_as_uint(zv) << 32) | (code0 + (uint32_t)v);
+            ++j;
+          }
+        }
       } else {
         // dense: scores by legal rank; the token of rank j is the j-th set bit
         for (int j0 = lb; j0 < n3; j0 += LPB * U) {
@@ -616,7 +634,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     if (LPB <= 64) {
       for (int o = LPB >> 1; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
       if (lb == 0 && bl3 < nloc) {
-        const float l = m + __logf(s);
+        const float l = lse_ext ? lse_ext[b0 + bl3] : m + __logf(s);
         blse[bl3] = l;
         // best candidate of the beam (cand is monotone in z within a beam)
         if (r3 >= 0) atomicMax(&omax_sh, ord_of(bcum[bl3] + (m - l)));
@@ -633,14 +651,14 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       if ((int)threadIdx.x < nloc) {
         float mm = pm[threadIdx.x * wpb], ss = ps[threadIdx.x * wpb];
         for (int i = 1; i < wpb; ++i) lse_combine(mm, ss, pm[threadIdx.x * wpb + i], ps[threadIdx.x * wpb + i]);
-        const float l = mm + __logf(ss);
+        const float l = lse_ext ? lse_ext[b0 + threadIdx.x] : mm + __logf(ss);
         blse[threadIdx.x] = l;
         if (brow[threadIdx.x] >= 0) atomicMax(&omax_sh, ord_of(bcum[threadIdx.x] + (mm - l)));
       }
     }
   }
   __syncthreads();
-  if (!MERGE && dense && store) {
+  if (!MERGE && dense && store && !TOKEN_IDX) {
     // slot codes of the dense candidates: each (beam, word) pair walks its set
     // bits; a bit's legal rank is the word's directory entry plus the set bits
     // below it
@@ -675,7 +693,8 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
           } else {
             const int64_t w = (int64_t)r * tab.words + (j >> 5);
             const uint32_t x = tab.bits[w];
-            if ((x >> (j & 31)) & 1u) v = zb[tab.rank[w] + __popc(x & ((1u << (j & 31)) - 1u))] - l;
+            if ((x >> (j & 31)) & 1u)
+              v = (TOKEN_IDX ? zb[j] : zb[tab.rank[w] + __popc(x & ((1u << (j & 31)) - 1u))]) - l;
           }
         }
         dbg[j] = v;
@@ -750,7 +769,9 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         while (y) {
           const int v = (i << 5) + __ffs(y) - 1;
           y &= y - 1;
-          fn(make_key(c + (zb[j++] - l), code0 + (uint32_t)v));
+          const float zv = TOKEN_IDX ? zb[v] : zb[j];
+          ++j;
+          fn(make_key(c + (zv - l), code0 + (uint32_t)v));
         }
       }
     }
@@ -887,7 +908,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         // entries of the row before this token: the rank directory gives the
         // count before its word, popcount the rest of the word
         const int64_t w = (int64_t)r * tab.words + (slot >> 5);
-        next = bbase[bl] + tab.rank[w] + __popc(tab.bits[w] & ((1u << (slot & 31)) - 1u));
+        next = all_legal ? 0 : bbase[bl] + tab.rank[w] + __popc(tab.bits[w] & ((1u << (slot & 31)) - 1u));
       }
       parent_out[oi] = b;
       token_out[oi] = token;
@@ -1190,11 +1211,93 @@ __global__ void k_decode_final(const int32_t* row, const float* cum, const int32
   if (i >= B * top_k) return;
   const int q = i / top_k, o = i - q * top_k;
   const int src = q * K + o;
-  const int r = row[src];
-  item_out[i] = r;
+  const bool live = cum[src] != -INFINITY;
+  item_out[i] = live ? row[src] : -1;
   if (score_out) score_out[i] = cum[src];
   if (sid_out)
-    for (int l = 0; l < L; ++l) sid_out[(int64_t)i * L + l] = (r >= 0) ? prefix[(int64_t)src * L + l] : -1;
+    for (int l = 0; l < L; ++l) sid_out[(int64_t)i * L + l] = live ? prefix[(int64_t)src * L + l] : -1;
+}
+
+// Item id of each final beam's SID, found by walking the step tables from the
+// root (sparse rows: binary search among the row's sorted tokens, the entry's
+// position is the next row; dense rows: the bitmap bit, rank directory and
+// popcount).  -1 when the SID is not in the catalog (possible only for codes
+// produced without the filter) or the beam is empty.
+struct TableSet {
+  DevTable t[kMaxL];
+};
+
+__global__ void k_lookup_items(TableSet ts, int32_t L, const int32_t* __restrict__ prefix,
+                               const float* __restrict__ cum, int32_t n, int32_t* __restrict__ item) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int64_t r = 0;
+  if (cum[i] == -INFINITY) r = -1;
+  for (int l = 0; l < L && r >= 0; ++l) {
+    const DevTable& tb = ts.t[l];
+    const int v = prefix[(int64_t)i * L + l];
+    if (v < 0 || v >= tb.V || r >= tb.rows) {
+      r = -1;
+      break;
+    }
+    const int lo0 = tb.row_ptr[r], hi0 = tb.row_ptr[r + 1];
+    if (tb.fmt == ZGR_FMT_SPARSE) {
+      int lo = lo0, hi = hi0;  // first entry with token >= v
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)tb.tok[mid] < v)
+          lo = mid + 1;
+        else
+          hi = mid;
+      }
+      r = (lo < hi0 && (int)tb.tok[lo] == v) ? lo : -1;
+    } else {
+      const int64_t w = r * tb.words + (v >> 5);
+      const uint32_t x = tb.bits[w];
+      r = ((x >> (v & 31)) & 1u) ? lo0 + tb.rank[w] + __popc(x & ((1u << (v & 31)) - 1u)) : -1;
+    }
+  }
+  item[i] = (int32_t)r;
+}
+
+// Log-sum-exp over all V scores of every live beam (the score-first
+// normaliser): one wave per beam row, online max / sum of exp per lane, then
+// a butterfly combine.
+__global__ __launch_bounds__(256) void k_row_lse(const float* __restrict__ z, int64_t ldz, int32_t V,
+                                                 int32_t M, const int32_t* __restrict__ row_in,
+                                                 float* __restrict__ lse) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= M) return;  // wave-uniform
+  if (row_in[b] < 0) {
+    if (lane == 0) lse[b] = -INFINITY;
+    return;
+  }
+  const float* zr = z + (int64_t)b * ldz;
+  float m = -INFINITY, sum = 0.f;
+  auto acc = [&](float v) {
+    if (v > m) {
+      sum = sum * __expf(m - v) + 1.f;
+      m = v;
+    } else {
+      sum += __expf(v - m);
+    }
+  };
+  if ((V & 3) == 0 && (ldz & 3) == 0) {
+    const float4* z4 = (const float4*)zr;
+    for (int i = lane; i < (V >> 2); i += 64) {
+      const float4 q = z4[i];
+      acc(q.x);
+      acc(q.y);
+      acc(q.z);
+      acc(q.w);
+    }
+  } else {
+    for (int i = lane; i < V; i += 64) acc(zr[i]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lse_combine(m, sum, __shfl_xor(m, o), __shfl_xor(sum, o));
+  if (lane == 0) lse[b] = m + __logf(sum);
 }
 
 template <int DT, int D>
@@ -1223,7 +1326,7 @@ hipError_t launch_sel_d(const StepArgs& a, hipStream_t s) {
 template <int DT>
 hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
   const int V = a.tab.V;
-  const int compact = a.tab.fmt == ZGR_FMT_DENSE ? 1 : 0;
+  const int compact = (a.tab.fmt == ZGR_FMT_DENSE && !a.plain_z) ? 1 : 0;
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((V + bn - 1) / bn); };
   // the largest tile that still gives every compute unit two blocks (or one)
   if (tiles(128, 128) >= 2 * a.n_cu) {
@@ -1273,7 +1376,7 @@ hipError_t launch_full_projection(const StepArgs& a, hipStream_t s) {
 #define ZGR_STEP_ARGS                                                                            \
   a.tab, a.t, a.L, a.k_in, a.K, a.row_in, a.cum_in, a.hidden, a.W, a.z, a.ldz, a.parts,            \
       a.part_keys, a.part_cnt, a.parent_out, a.token_out, a.row_out, a.cum_out, a.prefix_in,       \
-      a.prefix_out, a.slot_dbg, a.err
+      a.prefix_out, a.slot_dbg, a.lse_ext, a.err
 
 template <int DT, int D>
 hipError_t launch_scored_step(const StepArgs& a, hipStream_t s) {
@@ -1325,6 +1428,20 @@ hipError_t launch_request_merge(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 #undef ZGR_STEP_ARGS
+
+hipError_t launch_row_lse(const StepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_row_lse, dim3((a.M + 3) / 4), dim3(256), 0, s, a.z, a.ldz, a.tab.V, a.M, a.row_in,
+                     a.lse_ext);
+  return hipGetLastError();
+}
+
+hipError_t launch_lookup_items(const DevTable* tabs, int32_t L, const int32_t* prefix, const float* cum,
+                               int32_t n, int32_t* item, hipStream_t s) {
+  TableSet ts{};
+  for (int l = 0; l < L; ++l) ts.t[l] = tabs[l];
+  hipLaunchKernelGGL(k_lookup_items, dim3((n + 255) / 256), dim3(256), 0, s, ts, L, prefix, cum, n, item);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_init(int32_t* row, float* cum, int32_t B, int32_t K, hipStream_t s) {
   const int n = B * K;

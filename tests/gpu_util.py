@@ -95,21 +95,21 @@ class Setup:
         return zgr.zgr_plan_warmup(self.index, self.W_dev, cfg.dtype, cfg.d, B, K, hs, n_warmup,
                                    force)
 
-    def oracle_decode(self, request, K=None):
+    def oracle_decode(self, request, K=None, mode="filter_first"):
         cfg = self.cfg
-        key = (request, K or cfg.K)
+        key = (request, K or cfg.K, mode)
         if key not in self._decodes:
             def hid(r, t, prefixes):
                 return workload.hidden(cfg, t, np.full(len(prefixes), r, np.int64), prefixes)[1]
             self._decodes[key] = oracle.decode(self.cat, self.W_f32, hid, request, key[1],
-                                               keep_steps=True)
+                                               keep_steps=True, mode=mode)
         return self._decodes[key]
 
 
-def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True):
+def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True, mode="filter_first"):
     """Run zgr_step on given beams.  prefixes [B*k_in, t-1] (rows of dead beams
     ignored), cum float32 [B*k_in] (-inf = dead).  Returns dict of numpy outputs
-    and the inputs used."""
+    and the inputs used.  In the unconstrained mode a live beam's row is 0."""
     import torch
     cfg = setup.cfg
     M = len(cum)
@@ -117,6 +117,9 @@ def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True):
     rows = np.full(M, -1, np.int32)
     for i in range(M):
         if np.isfinite(cum[i]):
+            if mode == "unconstrained":
+                rows[i] = 0
+                continue
             rows[i] = setup.cat.node(prefixes[i, : t - 1]) if t > 1 else 0
             assert rows[i] >= 0
     req = np.repeat(np.asarray(requests, np.int64), k_in)
@@ -131,7 +134,7 @@ def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True):
         row_out=torch.empty(B * K, dtype=torch.int32, device="cuda"),
         cum_out=torch.empty(B * K, dtype=torch.float32, device="cuda"),
     )
-    S = setup.stats[t - 1]["stride"]
+    S = cfg.V if mode == "unconstrained" else setup.stats[t - 1]["stride"]
     dbg = torch.empty(M * S, dtype=torch.float32, device="cuda") if with_dbg is not False else None
     zgr.zgr_step(plan, t, dev["hidden"], dev["row_in"], dev["cum_in"], k_in, dev["parent"],
                  dev["token"], dev["row_out"], dev["cum_out"], dbg)
@@ -150,21 +153,23 @@ def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True):
     return out
 
 
-def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests=None):
-    """Step check against the oracle on identical inputs (all requests, or the
-    listed ones).  Returns the number of requests whose K-th score boundary
-    was ambiguous."""
+def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests=None,
+               mode="filter_first"):
+    """Step check against the oracle (in the same mode) on identical inputs
+    (all requests, or the listed ones).  Returns the number of requests whose
+    K-th score boundary was ambiguous."""
     cfg = setup.cfg
     M = len(cum)
     k_in = M // B
     st = setup.stats[t - 1]
-    dense = st["fmt"] == zgr.ZGR_FMT_DENSE
+    unc = mode == "unconstrained"
+    dense = st["fmt"] == zgr.ZGR_FMT_DENSE or unc  # slot = token
     ambiguous = 0
     for q in (range(B) if requests is None else requests):
         sl = slice(q * k_in, (q + 1) * k_in)
         pq = prefixes[sl, : t - 1] if t > 1 else np.zeros((k_in, 0), np.int32)
         cq = np.asarray(cum[sl], np.float64)
-        res = setup.cat.step(t, setup.W_f32[t - 1], pq, cq, out["h32"][sl], K)
+        res = setup.cat.step(t, setup.W_f32[t - 1], pq, cq, out["h32"][sl], K, mode)
         # (i) legal slots and their log-probs
         if check_dbg and out["dbg"] is not None:
             dbg = out["dbg"][q] if isinstance(out["dbg"], dict) else out["dbg"][sl]
@@ -197,8 +202,11 @@ def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests
             assert key in scores, ("illegal pick", q, key)
             s = scores[key]
             assert abs(cumo[i] - s) <= tol, (q, i, cumo[i], s)
-            ext = np.concatenate([pq[b], [tok[i]]]).astype(np.int32)
-            assert rowo[i] == setup.cat.node(ext), (q, i)
+            if unc:
+                assert rowo[i] == 0, (q, i)
+            else:
+                ext = np.concatenate([pq[b], [tok[i]]]).astype(np.int32)
+                assert rowo[i] == setup.cat.node(ext), (q, i)
             picks.append(s)
         assert len(set(zip(par[:kk].tolist(), tok[:kk].tolist()))) == kk
         picks = np.array(picks)
@@ -214,3 +222,36 @@ def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests
         else:
             ambiguous += 1
     return ambiguous
+
+
+def gpu_trajectory(s, plan, requests, mode="filter_first"):
+    """The GPU's own step-by-step decode; every step checked against the oracle
+    on the GPU's beams.  Returns final (rows, sids, scores) and ambiguity count."""
+    cfg = s.cfg
+    B, K, L = cfg.B, cfg.K, cfg.L
+    tol = TOL[cfg.dtype]
+    prefixes = np.zeros((B, 0), np.int32)
+    cum = np.zeros(B, np.float32)
+    amb = 0
+    out = None
+    for t in range(1, L + 1):
+        out = run_gpu_step(s, plan, t, prefixes, cum, B, K, requests, mode=mode)
+        amb += check_step(s, t, prefixes, cum, out, B, K, tol, mode=mode)
+        par = out["parent"]
+        new = np.full((B * K, t), -1, np.int32)
+        ok = par >= 0
+        if t > 1:
+            new[ok, : t - 1] = prefixes[par[ok]]
+        new[ok, t - 1] = out["token"][ok]
+        prefixes, cum = new, out["cum_out"]
+    return out["row_out"].reshape(B, K), prefixes.reshape(B, K, L), cum.reshape(B, K), amb
+
+
+def oracle_unambiguous(dec, K, tol):
+    for st in dec.steps:
+        sc = np.sort(st["res"].cand_score)[::-1]
+        if len(sc) > K:
+            tau = sc[K - 1]
+            if np.sum(np.abs(sc - tau) <= tol) > 1:
+                return False
+    return True

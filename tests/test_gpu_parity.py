@@ -73,37 +73,8 @@ def test_step_parity_teacher_forced(name, proj):
     print(f"{name} {proj}: ambiguous request-steps {amb}")
 
 
-def gpu_trajectory(s, plan, requests):
-    """The GPU's own step-by-step decode; every step checked against the oracle
-    on the GPU's beams.  Returns final (items, sids, scores) and ambiguity count."""
-    cfg = s.cfg
-    B, K, L = cfg.B, cfg.K, cfg.L
-    tol = gu.TOL[cfg.dtype]
-    prefixes = np.zeros((B, 0), np.int32)
-    cum = np.zeros(B, np.float32)
-    amb = 0
-    out = None
-    for t in range(1, L + 1):
-        out = gu.run_gpu_step(s, plan, t, prefixes, cum, B, K, requests)
-        amb += gu.check_step(s, t, prefixes, cum, out, B, K, tol)
-        par = out["parent"]
-        new = np.full((B * K, t), -1, np.int32)
-        ok = par >= 0
-        if t > 1:
-            new[ok, : t - 1] = prefixes[par[ok]]
-        new[ok, t - 1] = out["token"][ok]
-        prefixes, cum = new, out["cum_out"]
-    return out["row_out"].reshape(B, K), prefixes.reshape(B, K, L), cum.reshape(B, K), amb
-
-
-def oracle_unambiguous(dec, K, tol):
-    for st in dec.steps:
-        sc = np.sort(st["res"].cand_score)[::-1]
-        if len(sc) > K:
-            tau = sc[K - 1]
-            if np.sum(np.abs(sc - tau) <= tol) > 1:
-                return False
-    return True
+gpu_trajectory = gu.gpu_trajectory
+oracle_unambiguous = gu.oracle_unambiguous
 
 
 @pytest.mark.parametrize("proj", ["selective", "full", "model"])
