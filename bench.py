@@ -94,12 +94,19 @@ class Workload:
         self.zgr.copy_to_device(hidden_ptr, bits, stream_ptr)
         return 0
 
+    def set_mode(self, mode):
+        """Switch the plan's decoding mode and record that mode's trajectory."""
+        self.zgr.zgr_plan_set_mode(self.plan, mode)
+        self.mode = mode
+        self._record()
+
     def _record(self):
         """Run the measured requests 0..B-1 step by step and keep each step's inputs."""
         import torch
 
         import workload
         cfg, zgr = self.cfg, self.zgr
+        unc = getattr(self, "mode", "filter_first") == "unconstrained"
         B, K, L = cfg.B, cfg.K, cfg.L
         dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[cfg.dtype]
         self.steps = []
@@ -131,13 +138,19 @@ class Workload:
             prefixes = new
             rows = self.out["row"].clone()
             cum = self.out["cum"].clone()
-        # per-step legal counts of the recorded beams (for the algorithmic work)
+        self.final_sids = prefixes.reshape(B, K, L)
+        self.final_live = np.isfinite(cum.cpu().numpy()).reshape(B, K)
+        # per-step candidate counts of the recorded beams (for the algorithmic
+        # work): the legal counts, or V per live beam without the filter
         for st in self.steps:
             row_ptr = self.tables[st["t"] - 1][0]
             r = st["row"].cpu().numpy()
             live = r >= 0
             n = np.zeros(len(r), np.int64)
-            n[live] = row_ptr[r[live] + 1] - row_ptr[r[live]]
+            if unc:
+                n[live] = cfg.V
+            else:
+                n[live] = row_ptr[r[live] + 1] - row_ptr[r[live]]
             st["n"] = n
             st["M"] = len(r)
             st["live"] = int(live.sum())
@@ -325,6 +338,54 @@ def rebuild_bench(name, reps):
     }), flush=True)
 
 
+def modes_bench(args):
+    """Latency per decode of the method (filter-first) against score-first and
+    unconstrained decoding on one workload and one frozen plan; each mode
+    decodes its own trajectory.  Also: how many of the filter-first items the
+    score-first decode returns, and how many unconstrained codes are items."""
+    import torch
+    torch.cuda.set_device(0)
+    force = args.force.split(",") if args.force else None
+    w = Workload(args.workload, args.plan_warmup, force)
+    cfg = w.cfg
+    stream = torch.cuda.Stream()
+    res, finals = {}, {}
+    for mode in ("filter_first", "score_first", "unconstrained"):
+        w.set_mode(mode)
+        sec, eager_sec, launch = time_decode(w, args, stream)
+        cand = sum(int(st["n"].sum()) for st in w.steps)
+        res[mode] = {"ms": round(sec * 1e3, 4), "eager_ms": round(eager_sec * 1e3, 4),
+                     "launch": launch, "candidates_per_decode": cand}
+        finals[mode] = (w.final_sids.copy(), w.final_live.copy())
+        log(f"[modes] {cfg.name} {mode}: {sec * 1e6:.1f} us per decode ({launch}), {cand} candidates")
+    members = set(map(tuple, w.sids.tolist()))
+    ff_sids, ff_live = finals["filter_first"]
+    sf_sids, sf_live = finals["score_first"]
+    un_sids, un_live = finals["unconstrained"]
+    both = total = 0
+    for q in range(cfg.B):
+        a = {tuple(x) for x in ff_sids[q][ff_live[q]].tolist()}
+        b = {tuple(x) for x in sf_sids[q][sf_live[q]].tolist()}
+        both += len(a & b)
+        total += len(a)
+    un_codes = [tuple(x) for x in un_sids[un_live].tolist()]
+    valid = sum(1 for c in un_codes if c in members)
+    ff = res["filter_first"]["ms"]
+    print(json.dumps({
+        "metric": "latency per decode by decoding mode (ms)",
+        "value": ff, "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: L={cfg.L}, V={cfg.V}, N={cfg.N}, d={cfg.d}, "
+                               f"beam={cfg.K}, batch={cfg.B}, {cfg.dtype}",
+                   "projection": ["full" if c[0] == 1 else "selective" for c in w.choices]},
+        "modes": res,
+        "unconstrained_over_filter_first": round(res["unconstrained"]["ms"] / ff, 3),
+        "score_first_over_filter_first": round(res["score_first"]["ms"] / ff, 3),
+        "score_first_item_overlap": round(both / max(1, total), 4),
+        "unconstrained_codes_in_catalog": round(valid / max(1, len(un_codes)), 4),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -341,6 +402,8 @@ def main():
     ap.add_argument("--rebuild", default=None, metavar="WORKLOAD",
                     help="time the index rebuild pipeline of this workload's catalog instead")
     ap.add_argument("--rebuild-reps", type=int, default=3)
+    ap.add_argument("--modes", action="store_true",
+                    help="time filter-first against score-first and unconstrained decoding instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no "
@@ -349,6 +412,9 @@ def main():
         sys.exit(2)
     if args.rebuild:
         rebuild_bench(args.rebuild, args.rebuild_reps)
+        return
+    if args.modes:
+        modes_bench(args)
         return
     import torch
 
@@ -360,6 +426,16 @@ def main():
 
     # ---- timed region: whole decodes (L steps) over recorded HBM-resident inputs
     stream = torch.cuda.Stream()
+    sec, eager_sec, mode = time_decode(w, args, stream)
+    ms = sec * 1e3
+    log(f"[bench] {mode}: {ms * 1e3:.1f} us per decode (eager {eager_sec * 1e6:.1f} us)")
+    per_kernel_and_line(w, args, stream, sec, eager_sec, mode)
+
+
+def time_decode(w, args, stream):
+    """Seconds per decode: a graph replay of the recorded L steps (checked
+    against eager launches first), and the eager launches themselves."""
+    import torch
     mode = "eager"
     with torch.cuda.stream(stream):
         w.run_decode(stream)
@@ -390,9 +466,15 @@ def main():
         sec = timed(fn, args.steps, args.warmup)
         eager_sec = sec if mode == "eager" else timed(lambda: w.run_decode(stream), args.steps,
                                                       args.warmup)
-    ms = sec * 1e3
-    log(f"[bench] {mode}: {ms * 1e3:.1f} us per decode (eager {eager_sec * 1e6:.1f} us)")
+    return sec, eager_sec, mode
 
+
+def per_kernel_and_line(w, args, stream, sec, eager_sec, mode):
+    import torch
+
+    import sid_constrained_beam_amd as zgr
+    cfg = w.cfg
+    ms = sec * 1e3
     # ---- per-kernel durations: HIP events on the launch stream, eager
     with torch.cuda.stream(stream):
         # every launch repeated 20 times between its two events (the step
