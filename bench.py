@@ -386,6 +386,67 @@ def modes_bench(args):
     }), flush=True)
 
 
+def projections_bench(args):
+    """Per-step latency of the three ways to score a step on the same recorded
+    inputs: the full projection (MFMA over the whole codebook), the padded-slot
+    selective projection (weight rows read in place), and the naive compaction
+    baseline (compact candidate list sized on the host + temporary matrix).
+    Each step is timed as issued (eager, HIP events on the stream), request
+    kernel included, since the naive path cannot be captured (it reads its
+    list size back)."""
+    import torch
+
+    import sid_constrained_beam_amd as zgr
+    import workload
+    torch.cuda.set_device(0)
+    base = workload.CONFIGS[args.workload]
+    if args.batch:
+        workload.CONFIGS[args.workload] = base.scaled(B=args.batch)
+    w = Workload(args.workload, 0, ["selective"] * base.L)
+    cfg = w.cfg
+    stream = torch.cuda.Stream()
+    res = {}
+    with torch.cuda.stream(stream):
+        for proj in ("full", "selective", "naive"):
+            for t in range(1, cfg.L + 1):
+                zgr.zgr_plan_set_choice(w.plan, t, proj)
+            per_step = []
+            for st in w.steps:
+                def one():
+                    zgr.zgr_step(w.plan, st["t"], st["hidden"], st["row"], st["cum"], st["k_in"],
+                                 w.out["parent"], w.out["token"], w.out["row"], w.out["cum"], None,
+                                 stream)
+                for _ in range(args.warmup):
+                    one()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                a.record(stream)
+                for _ in range(args.steps):
+                    one()
+                b.record(stream)
+                b.synchronize()
+                per_step.append(a.elapsed_time(b) / args.steps * 1e3)
+            res[proj] = [round(x, 2) for x in per_step]
+            log(f"[proj] {cfg.name} B={cfg.B} {proj}: " + ", ".join(f"t{i + 1} {x:.1f}us"
+                                                                   for i, x in enumerate(per_step)))
+    cand = [int(st["n"].sum()) for st in w.steps]
+    ratios = {
+        "naive_over_full": [round(n / f, 3) for n, f in zip(res["naive"], res["full"])],
+        "naive_over_selective": [round(n / s_, 3) for n, s_ in zip(res["naive"], res["selective"])],
+        "full_over_selective": [round(f / s_, 3) for f, s_ in zip(res["full"], res["selective"])],
+    }
+    print(json.dumps({
+        "metric": "per-step latency by projection (us): full, padded-slot selective, naive compaction",
+        "value": res["selective"], "unit": "us", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: L={cfg.L}, V={cfg.V}, N={cfg.N}, d={cfg.d}, "
+                               f"beam={cfg.K}, batch={cfg.B}, {cfg.dtype}", "launch": "eager"},
+        "per_step_us": res, "legal_candidates_per_step": cand,
+        "full_scores_per_step": [st["M"] * cfg.V for st in w.steps],
+        **ratios,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +463,9 @@ def main():
     ap.add_argument("--rebuild", default=None, metavar="WORKLOAD",
                     help="time the index rebuild pipeline of this workload's catalog instead")
     ap.add_argument("--rebuild-reps", type=int, default=3)
+    ap.add_argument("--projections", action="store_true",
+                    help="time full / selective / naive-compaction scoring per step instead")
+    ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
     ap.add_argument("--modes", action="store_true",
                     help="time filter-first against score-first and unconstrained decoding instead")
     args = ap.parse_args()
@@ -415,6 +479,9 @@ def main():
         return
     if args.modes:
         modes_bench(args)
+        return
+    if args.projections:
+        projections_bench(args)
         return
     import torch
 

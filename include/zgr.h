@@ -73,6 +73,10 @@ extern "C" {
 #define ZGR_PROJ_AUTO 0       /* decided by warm-up timing (or a cost model without warm-up) */
 #define ZGR_PROJ_FULL 1       /* MFMA projection over the whole codebook, then legal columns */
 #define ZGR_PROJ_SELECTIVE 2  /* score only the legal tokens, weight rows read in place */
+#define ZGR_PROJ_NAIVE 3      /* baseline, never picked by the planner: the legal tokens scored
+                                 through a compact candidate list (sized on the host from a
+                                 device count, so the step synchronises its stream) and a
+                                 temporary [candidates x d] matrix of copied weight rows */
 
 typedef struct zgr_index zgr_index;
 typedef struct zgr_plan zgr_plan;
@@ -242,8 +246,9 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
 int32_t zgr_plan_choice(const zgr_plan* plan, int32_t t, int32_t* proj, float* us_full,
                         float* us_sel);
 
-/* Re-freeze step t's projection (ZGR_PROJ_FULL or ZGR_PROJ_SELECTIVE), e.g. to
- * resume a plan exported by zgr_plan_choice without a new warm-up. */
+/* Re-freeze step t's projection (ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE or the
+ * ZGR_PROJ_NAIVE baseline), e.g. to resume a plan exported by zgr_plan_choice
+ * without a new warm-up. */
 int32_t zgr_plan_set_choice(zgr_plan* plan, int32_t t, int32_t proj);
 
 /*

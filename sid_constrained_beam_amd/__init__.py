@@ -33,8 +33,9 @@ MODE_CODES = {"filter_first": ZGR_MODE_FILTER_FIRST, "score_first": ZGR_MODE_SCO
 
 DTYPE_CODES = {"f32": ZGR_F32, "bf16": ZGR_BF16, "f16": ZGR_F16}
 FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR_FMT_SPARSE}
+ZGR_PROJ_NAIVE = 3
 PROJ_CODES = {None: ZGR_PROJ_AUTO, "auto": ZGR_PROJ_AUTO, "full": ZGR_PROJ_FULL,
-              "selective": ZGR_PROJ_SELECTIVE}
+              "selective": ZGR_PROJ_SELECTIVE, "naive": ZGR_PROJ_NAIVE}
 
 _P = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64

@@ -45,6 +45,11 @@ struct zgr_plan {
   int32_t choice[zgr::kMaxL] = {0};
   int32_t mode = ZGR_MODE_FILTER_FIRST;
   zgr::DevTable all_tab{};  // one row, every token legal (unconstrained mode)
+  // naive compaction baseline: compact list and temporary matrix, grown on demand
+  int32_t* naive_beam = nullptr;
+  int32_t* naive_tok = nullptr;
+  void* naive_tmp = nullptr;
+  int64_t naive_cap = 0;
   float us_full[zgr::kMaxL], us_sel[zgr::kMaxL];
   int n_cu = 256;
   // HBM scratch
@@ -264,7 +269,39 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
   }
   // z layout: by legal rank on dense steps and on selective sparse steps,
   // token-indexed after a full projection of a sparse step
-  if (proj == ZGR_PROJ_FULL) {
+  if (proj == ZGR_PROJ_NAIVE) {
+    a.ldz = a.tab.stride;
+    if ((int64_t)a.M * a.tab.stride >= (int64_t)INT32_MAX)
+      return fail(ZGR_E_SHAPE, "naive projection: candidate list would exceed 2^31 entries");
+    int32_t* start = a.unit_start;  // [M + 1]
+    e = prof_launch(p, ZGR_KERNEL_UNITS, t, s, [&] { return launch_naive_count(a, start, s); });
+    if (e != hipSuccess) return hip_fail(e, "naive count launch");
+    // the list and the temporary matrix are sized from the device count
+    int32_t n = 0;
+    e = hipMemcpyAsync(&n, start + a.M, 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "naive list size read-back");
+    if (n > p->naive_cap) {
+      for (void* x : {(void*)p->naive_beam, (void*)p->naive_tok, p->naive_tmp})
+        if (x) (void)hipFree(x);
+      p->naive_beam = p->naive_tok = nullptr;
+      p->naive_tmp = nullptr;
+      p->naive_cap = 0;
+      e = hipMalloc((void**)&p->naive_beam, (size_t)n * 4);
+      if (e == hipSuccess) e = hipMalloc((void**)&p->naive_tok, (size_t)n * 4);
+      if (e == hipSuccess) e = hipMalloc(&p->naive_tmp, (size_t)n * p->d * elem_size(p->dtype));
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(ZGR_E_NOMEM, "naive projection: temporary matrix of " + std::to_string(n) + " rows");
+      }
+      p->naive_cap = n;
+    }
+    e = prof_launch(p, ZGR_KERNEL_SELECTIVE, t, s, [&] {
+      return launch_naive_score(a, start, n, p->naive_beam, p->naive_tok, p->naive_tmp, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "naive score launch");
+    zmode = 1;
+  } else if (proj == ZGR_PROJ_FULL) {
     a.ldz = p->V;
     e = prof_launch(p, ZGR_KERNEL_GEMM, t, s, [&] { return launch_full_projection(a, s); });
     if (e != hipSuccess) return hip_fail(e, "full projection launch");
@@ -414,8 +451,8 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   if (n_warmup < 0) return fail(ZGR_E_ARG, "zgr_plan_warmup: n_warmup must be >= 0");
   for (int l = 0; l < idx->L; ++l) {
     if (!W_dev[l]) return fail(ZGR_E_ARG, "zgr_plan_warmup: null W_t");
-    if (force && (force[l] < ZGR_PROJ_AUTO || force[l] > ZGR_PROJ_SELECTIVE))
-      return fail(ZGR_E_ARG, "zgr_plan_warmup: force[t] must be AUTO, FULL or SELECTIVE");
+    if (force && (force[l] < ZGR_PROJ_AUTO || force[l] > ZGR_PROJ_NAIVE))
+      return fail(ZGR_E_ARG, "zgr_plan_warmup: force[t] must be AUTO, FULL, SELECTIVE or NAIVE");
     // the slot code beam_rank * S_t + slot must fit 32 bits
     if ((int64_t)K * std::max<int32_t>(1, idx->host[l].stride) >= (int64_t)UINT32_MAX)
       return fail(ZGR_E_SHAPE, "zgr_plan_warmup: K * slot stride too large");
@@ -563,8 +600,8 @@ int32_t zgr_plan_choice(const zgr_plan* p, int32_t t, int32_t* proj, float* us_f
 int32_t zgr_plan_set_choice(zgr_plan* p, int32_t t, int32_t proj) {
   if (!p) return fail(ZGR_E_ARG, "zgr_plan_set_choice: null plan");
   if (t < 1 || t > p->L) return fail(ZGR_E_ARG, "zgr_plan_set_choice: t out of range");
-  if (proj != ZGR_PROJ_FULL && proj != ZGR_PROJ_SELECTIVE)
-    return fail(ZGR_E_ARG, "zgr_plan_set_choice: proj must be FULL or SELECTIVE");
+  if (proj != ZGR_PROJ_FULL && proj != ZGR_PROJ_SELECTIVE && proj != ZGR_PROJ_NAIVE)
+    return fail(ZGR_E_ARG, "zgr_plan_set_choice: proj must be FULL, SELECTIVE or NAIVE");
   p->choice[t - 1] = proj;
   return ZGR_OK;
 }
@@ -611,6 +648,8 @@ void zgr_plan_free(zgr_plan* p) {
   (void)prof_flush(p);
   for (hipEvent_t e : p->pool) (void)hipEventDestroy(e);
   p->pool.clear();
+  for (void* x : {(void*)p->naive_beam, (void*)p->naive_tok, p->naive_tmp})
+    if (x) p->allocations.push_back(x);
   if (!p->allocations.empty()) {
     int cur = -1;
     (void)hipGetDevice(&cur);

@@ -111,6 +111,12 @@ constexpr int kSelCapHost = 14336;  // candidates whose keys fit the request ker
 hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s);
 // after launch_request_step with a.parts > 1: the per-request merge of the parts
 hipError_t launch_request_merge(const StepArgs& a, hipStream_t s);
+// naive compaction baseline: legal counts scanned over all beams into start[0..M]
+hipError_t launch_naive_count(const StepArgs& a, int32_t* start, hipStream_t s);
+// then (n = start[M], read on the host) the compact list, the temporary matrix
+// [n][d] and the row dots scattered into z by legal rank
+hipError_t launch_naive_score(const StepArgs& a, const int32_t* start, int64_t n, int32_t* lbeam,
+                              int32_t* ltok, void* tmp, hipStream_t s);
 // score-first: log-sum-exp over all V token-indexed scores of each live beam into a.lse_ext
 hipError_t launch_row_lse(const StepArgs& a, hipStream_t s);
 // item id of each final SID by a walk of the L tables (-1 if not in the catalog)

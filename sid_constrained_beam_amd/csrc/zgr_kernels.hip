@@ -41,6 +41,8 @@
 // lower beam rank, then the lower slot (slot order = token order).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "zgr_internal.h"
 
 namespace zgr {
@@ -350,6 +352,120 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       const int cnt = lst_count;
       for (int i = grp; i < cnt; i += NG) score(lst[i], lpos[i]);
     }
+  }
+}
+
+// ---------------------------------------------------------------- naive compaction baseline
+//
+// The selective projection organised the way the ZeroGR description says a
+// straightforward implementation does it ("why fewer scores is not faster":
+// all beams' candidates are first packed into one compact list and a
+// temporary matrix is built): a scan of the legal counts over every beam
+// gives each candidate's list position (a beam's position depends on all the
+// beams before it), the list is sized from that count on the host, the
+// candidates' weight rows are copied into a temporary [candidates x d]
+// matrix, each row is dotted with its beam's hidden vector, and the score is
+// scattered back to the beam's slot.  Used only to measure the padded-slot
+// design against it.
+
+// Legal counts of every beam and their exclusive scan (one block).
+__global__ __launch_bounds__(1024) void k_naive_scan(const int32_t* __restrict__ row_in, int32_t M,
+                                                     DevTable tab, int32_t* __restrict__ start,
+                                                     int32_t* __restrict__ err) {
+  __shared__ int sh[16];
+  const int per = (M + 1023) / 1024;
+  const int b0 = threadIdx.x * per, b1 = min(M, b0 + per);
+  auto count = [&](int b) {
+    const int r = row_in[b];
+    if (r >= 0 && r < tab.rows) return tab.row_ptr[r + 1] - tab.row_ptr[r];
+    if (r >= tab.rows) atomicOr(err, 1);
+    return 0;
+  };
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += count(b);
+  int total;
+  int run = block_excl_scan<1024>(mine, sh, &total);
+  for (int b = b0; b < b1; ++b) {
+    start[b] = run;
+    const int r = row_in[b];
+    run += (r >= 0 && r < tab.rows) ? tab.row_ptr[r + 1] - tab.row_ptr[r] : 0;
+  }
+  if (threadIdx.x == 0) start[M] = total;
+}
+
+// The compact list: (beam, token) of every legal candidate at start[b] + its
+// legal rank.  One wave per beam.
+__global__ __launch_bounds__(256) void k_naive_compact(const int32_t* __restrict__ row_in, int32_t M,
+                                                       DevTable tab, const int32_t* __restrict__ start,
+                                                       int32_t* __restrict__ lbeam,
+                                                       int32_t* __restrict__ ltok) {
+  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (b >= M) return;  // wave-uniform
+  const int r = row_in[b];
+  if (r < 0 || r >= tab.rows) return;
+  const int s0 = start[b];
+  if (tab.fmt == ZGR_FMT_SPARSE) {
+    const int base = tab.row_ptr[r], n = tab.row_ptr[r + 1] - base;
+    for (int j = lane; j < n; j += 64) {
+      lbeam[s0 + j] = b;
+      ltok[s0 + j] = tab.tok[base + j];
+    }
+  } else {
+    const int64_t rw = (int64_t)r * tab.words;
+    for (int w = lane; w < tab.words; w += 64) {
+      uint32_t x = tab.bits[rw + w];
+      int j = s0 + tab.rank[rw + w];
+      while (x) {
+        const int v = (w << 5) + __ffs(x) - 1;
+        x &= x - 1;
+        lbeam[j] = b;
+        ltok[j] = v;
+        ++j;
+      }
+    }
+  }
+}
+
+// The temporary matrix: tmp[c] = W[ltok[c]], rows copied in 16-byte pieces.
+__global__ __launch_bounds__(256) void k_naive_gather(const uint4* __restrict__ W, int32_t row_vec,
+                                                      const int32_t* __restrict__ ltok, int64_t n,
+                                                      uint4* __restrict__ tmp) {
+  const int64_t total = n * row_vec;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = i / row_vec, q = i - c * row_vec;
+    tmp[i] = W[(int64_t)ltok[c] * row_vec + q];
+  }
+}
+
+// z of every list entry: its temporary-matrix row dotted with its beam's
+// hidden vector (a group of lanes per entry), scattered to the beam's slot.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_naive_dot(const void* __restrict__ tmp,
+                                                        const void* __restrict__ hidden,
+                                                        const int32_t* __restrict__ lbeam,
+                                                        const int32_t* __restrict__ start, int64_t n,
+                                                        float* __restrict__ z, int64_t ldz) {
+  using Sh = SelShape<DT, D>;
+  constexpr int G = Sh::G, NV = Sh::NV, VEC = Sh::VEC, ES = Sh::ES, NG = Sh::NG;
+  const int gl = threadIdx.x % G, grp = threadIdx.x / G;
+  for (int64_t c = (int64_t)blockIdx.x * NG + grp; c < n; c += (int64_t)gridDim.x * NG) {
+    const int b = lbeam[c];
+    const char* tr = (const char*)tmp + c * D * ES;
+    const char* hb = (const char*)hidden + (int64_t)b * D * ES;
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      float w[VEC], h[VEC];
+      load16<DT>(tr + (int64_t)(q * G + gl) * 16, w);
+      load16<DT>(hb + (int64_t)(q * G + gl) * 16, h);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc = fmaf(w[e], h[e], acc);
+    }
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (gl == 0) z[(int64_t)b * ldz + (c - start[b])] = acc;
   }
 }
 
@@ -1428,6 +1544,60 @@ hipError_t launch_request_merge(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 #undef ZGR_STEP_ARGS
+
+hipError_t launch_naive_count(const StepArgs& a, int32_t* start, hipStream_t s) {
+  hipLaunchKernelGGL(k_naive_scan, dim3(1), dim3(1024), 0, s, a.row_in, a.M, a.tab, start, a.err);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_naive_dot_typed(const StepArgs& a, const void* tmp, const int32_t* lbeam,
+                                  const int32_t* start, int64_t n, hipStream_t s) {
+  using Sh = SelShape<DT, D>;
+  const int64_t want = (n + Sh::NG - 1) / Sh::NG;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)a.n_cu * 16));
+  hipLaunchKernelGGL((k_naive_dot<DT, D>), dim3(grid), dim3(kThreads), 0, s, tmp, a.hidden, lbeam, start,
+                     n, a.z, a.ldz);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_naive_dot_d(const StepArgs& a, const void* tmp, const int32_t* lbeam,
+                              const int32_t* start, int64_t n, hipStream_t s) {
+  switch (a.d) {
+    case 64: return launch_naive_dot_typed<DT, 64>(a, tmp, lbeam, start, n, s);
+    case 128: return launch_naive_dot_typed<DT, 128>(a, tmp, lbeam, start, n, s);
+    case 256: return launch_naive_dot_typed<DT, 256>(a, tmp, lbeam, start, n, s);
+    case 512: return launch_naive_dot_typed<DT, 512>(a, tmp, lbeam, start, n, s);
+    case 768: return launch_naive_dot_typed<DT, 768>(a, tmp, lbeam, start, n, s);
+    case 1024: return launch_naive_dot_typed<DT, 1024>(a, tmp, lbeam, start, n, s);
+    case 2048: return launch_naive_dot_typed<DT, 2048>(a, tmp, lbeam, start, n, s);
+    case 4096: return launch_naive_dot_typed<DT, 4096>(a, tmp, lbeam, start, n, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_naive_score(const StepArgs& a, const int32_t* start, int64_t n, int32_t* lbeam,
+                              int32_t* ltok, void* tmp, hipStream_t s) {
+  hipLaunchKernelGGL(k_naive_compact, dim3((a.M + 3) / 4), dim3(256), 0, s, a.row_in, a.M, a.tab, start,
+                     lbeam, ltok);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n == 0) return e;
+  const int es = a.dtype == ZGR_F32 ? 4 : 2;
+  const int row_vec = a.d * es / 16;
+  const int64_t vecs = n * row_vec;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((vecs + 255) / 256, (int64_t)a.n_cu * 16));
+  hipLaunchKernelGGL(k_naive_gather, dim3(grid), dim3(256), 0, s, (const uint4*)a.W, row_vec, ltok, n,
+                     (uint4*)tmp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (a.dtype) {
+    case ZGR_F32: return launch_naive_dot_d<ZGR_F32>(a, tmp, lbeam, start, n, s);
+    case ZGR_BF16: return launch_naive_dot_d<ZGR_BF16>(a, tmp, lbeam, start, n, s);
+    case ZGR_F16: return launch_naive_dot_d<ZGR_F16>(a, tmp, lbeam, start, n, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_row_lse(const StepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_row_lse, dim3((a.M + 3) / 4), dim3(256), 0, s, a.z, a.ldz, a.tab.V, a.M, a.row_in,

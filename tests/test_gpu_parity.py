@@ -56,7 +56,7 @@ def oracle_inputs(s, requests, t):
     return prefixes, cum
 
 
-@pytest.mark.parametrize("proj", ["selective", "full"])
+@pytest.mark.parametrize("proj", ["selective", "full", "naive"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_step_parity_teacher_forced(name, proj):
     s = setup_of(name)
@@ -77,7 +77,7 @@ gpu_trajectory = gu.gpu_trajectory
 oracle_unambiguous = gu.oracle_unambiguous
 
 
-@pytest.mark.parametrize("proj", ["selective", "full", "model"])
+@pytest.mark.parametrize("proj", ["selective", "full", "model", "naive"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_parity(name, proj):
     import torch
@@ -270,3 +270,24 @@ def test_profiled_launches_keep_results():
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
     with pytest.raises(zgr.ZgrError):
         zgr.zgr_plan_profile(plan, -1)
+
+
+def test_naive_baseline_matches_padded_slots():
+    """The compaction baseline scores the same candidates as the padded-slot
+    selective path: identical legal sets and selections, scores equal up to
+    the summation order (both reduce the same products over one weight row)."""
+    import torch
+    s = setup_of("n1e6_v2048")
+    cfg = s.cfg
+    outs = {}
+    for proj in ("selective", "naive"):
+        plan = s.plan(force=[proj] * cfg.L)
+        item = torch.empty(cfg.B * cfg.K, dtype=torch.int64, device="cuda")
+        sc = torch.empty(cfg.B * cfg.K, dtype=torch.float32, device="cuda")
+        zgr.zgr_decode(plan, s.hidden_source(0), cfg.K, item, None, sc)
+        outs[proj] = (item.cpu().numpy(), sc.cpu().numpy())
+        assert plan.choice(2)[0] == zgr.PROJ_CODES[proj]
+    same = np.mean(outs["selective"][0] == outs["naive"][0])
+    assert same > 0.99, same
+    ok = np.isfinite(outs["selective"][1])
+    assert np.allclose(outs["selective"][1][ok], outs["naive"][1][ok], atol=1e-4, rtol=0)
