@@ -181,7 +181,7 @@ class Workload:
         n = st["n"]
         M, live = st["M"], st["live"]
         tab = self.stats[st["t"] - 1]
-        dense = tab["fmt"] == 1
+        dense = tab["fmt"] != 2
         cand = int(n.sum())
         gather = cand * (cfg.d * es + (0 if dense else 2) + 4) + live * (cfg.d * es + 8)
         if kernel == "selective":
@@ -447,6 +447,107 @@ def projections_bench(args):
     }), flush=True)
 
 
+def index_bytes_report(names):
+    """Bytes of each workload's filter index (host build only; no GPU): the
+    per-step tables as built, and the same tables in other encodings, from
+    the built index's per-step rows (R_t) and entries (nnz_t):
+      as_built          formats as chosen (dense: bitmap + rank directory;
+                        sparse: sorted tokens, the position is the next row)
+      bitmap_only       dense rows without the rank directory
+      dense_next_matrix dense rows as an int32 next-row matrix [R_t][V]
+      all_sparse / all_dense_bitmap   one format for every step
+      explicit_successor  every step as sorted tokens plus an explicit int32
+                        next row per entry and an int64 item id per last-step
+                        entry: the layout without the implicit-position rule"""
+    import sid_constrained_beam_amd as zgr
+    import workload
+    out = []
+    for name in names:
+        cfg = workload.CONFIGS[name]
+        t0 = time.time()
+        sids = workload.catalog(cfg)
+        idx, _ = zgr.zgr_index_build_host(sids, cfg.V, cfg.fmt, want_rank=False)
+        words = (cfg.V + 31) // 32
+        per = []
+        tot = dict(as_built=0, bitmap_only=0, dense_next_matrix=0, all_sparse=0, all_dense_bitmap=0,
+                   explicit_successor=0)
+        for t in range(1, cfg.L + 1):
+            st = idx.stats(t)
+            R, nnz = st["rows"], st["nnz"]
+            rp = (R + 1) * 4
+            dense = st["fmt"] != zgr.ZGR_FMT_SPARSE
+            e = dict(as_built=st["bytes"],
+                     bitmap_only=rp + (R * words * 4 if dense else nnz * 2),
+                     dense_next_matrix=rp + (R * cfg.V * 4 if dense else nnz * 2),
+                     all_sparse=rp + nnz * 2,
+                     all_dense_bitmap=rp + R * words * 6,
+                     explicit_successor=rp + nnz * 2 + nnz * (8 if t == cfg.L else 4))
+            for k in tot:
+                tot[k] += e[k]
+            per.append(dict(t=t, rows=R, nnz=nnz, fmt="S" if not dense else "D", **e))
+        del idx
+        rec = dict(workload=name, items=cfg.N, L=cfg.L, V=cfg.V, steps=per, total=tot,
+                   saving_vs_explicit_successor=round(1 - tot["as_built"] / tot["explicit_successor"], 4),
+                   saving_vs_dense_next_matrix=round(1 - tot["as_built"] / tot["dense_next_matrix"], 4))
+        log(f"[bytes] {name}: {tot} ({time.time() - t0:.1f}s)")
+        out.append(rec)
+        print(json.dumps(rec), flush=True)
+    return out
+
+
+def encodings_bench(args):
+    """Decode latency with dense steps stored as the bitmap + rank directory
+    against the int32 next-row matrix, same plan choices, same inputs."""
+    import torch
+
+    import sid_constrained_beam_amd as zgr
+    import workload
+    torch.cuda.set_device(0)
+    base = workload.CONFIGS[args.workload]
+    force = args.force.split(",") if args.force else None
+    w = Workload(args.workload, args.plan_warmup, force)
+    fmts = ["S" if st["fmt"] == zgr.ZGR_FMT_SPARSE else "D" for st in w.stats]
+    choice = ["full" if c[0] == 1 else "selective" for c in w.choices]
+    stream = torch.cuda.Stream()
+    res = {}
+    for enc in ("bitmap", "next_matrix"):
+        if enc == "next_matrix":
+            w.plan.free()
+            w.index.free()
+            workload.CONFIGS[args.workload] = base.scaled(fmt=["N" if f == "D" else f for f in fmts])
+            w = Workload(args.workload, 0, choice)
+        sec, eager_sec, launch = time_decode(w, args, stream)
+        with torch.cuda.stream(stream):
+            zgr.zgr_plan_profile(w.plan, 20)
+            for _ in range(3):
+                w.run_decode(stream)
+            torch.cuda.synchronize()
+        kern = {}
+        for kname in zgr.KERNELS:
+            for st in w.steps:
+                n, kms = zgr.zgr_plan_profile_read(w.plan, kname, st["t"])
+                if n:
+                    kern[f"t{st['t']}_{kname}_us"] = round(kms / n * 1e3, 2)
+        zgr.zgr_plan_profile(w.plan, 0)
+        res[enc] = {"ms": round(sec * 1e3, 4), "launch": launch,
+                    "index_bytes": int(sum(st["bytes"] for st in w.stats)),
+                    "dense_step_bytes": int(sum(st["bytes"] for st in w.stats
+                                                if st["fmt"] != zgr.ZGR_FMT_SPARSE)),
+                    "kernels": kern}
+        log(f"[enc] {args.workload} {enc}: {sec * 1e6:.1f} us per decode; {res[enc]}")
+    cfg = w.cfg
+    print(json.dumps({
+        "metric": "latency per decode by dense-table encoding (ms)",
+        "value": res["bitmap"]["ms"], "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: L={cfg.L}, V={cfg.V}, N={cfg.N}, d={cfg.d}, "
+                               f"beam={cfg.K}, batch={cfg.B}, {cfg.dtype}",
+                   "formats": fmts, "projection": choice},
+        "encodings": res,
+        "next_matrix_over_bitmap": round(res["next_matrix"]["ms"] / res["bitmap"]["ms"], 3),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -466,6 +567,10 @@ def main():
     ap.add_argument("--projections", action="store_true",
                     help="time full / selective / naive-compaction scoring per step instead")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--index-bytes", default=None, metavar="WORKLOADS",
+                    help="comma list: report index bytes per encoding (host only) instead")
+    ap.add_argument("--encodings", action="store_true",
+                    help="time bitmap against next-row-matrix dense tables instead")
     ap.add_argument("--modes", action="store_true",
                     help="time filter-first against score-first and unconstrained decoding instead")
     args = ap.parse_args()
@@ -474,8 +579,14 @@ def main():
                                    "multi-GPU mode (requests would shard across GPUs with no "
                                    "exchange, see the design notes)", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.index_bytes:
+        index_bytes_report(args.index_bytes.split(","))
+        return
     if args.rebuild:
         rebuild_bench(args.rebuild, args.rebuild_reps)
+        return
+    if args.encodings:
+        encodings_bench(args)
         return
     if args.modes:
         modes_bench(args)

@@ -69,6 +69,10 @@ extern "C" {
 #define ZGR_FMT_AUTO 0    /* smaller of the two encodings */
 #define ZGR_FMT_DENSE 1   /* bitmap per row over the codebook, slot = token */
 #define ZGR_FMT_SPARSE 2  /* sorted legal tokens per row, slot = position */
+#define ZGR_FMT_DENSE_NEXT 3 /* dense rows stored as an int32 next-row matrix [rows][V]
+                                (-1 = not legal) instead of the bitmap: the same results and
+                                slots as DENSE at 32 times its bytes; never picked by AUTO,
+                                kept to measure the two encodings against each other */
 
 #define ZGR_PROJ_AUTO 0       /* decided by warm-up timing (or a cost model without warm-up) */
 #define ZGR_PROJ_FULL 1       /* MFMA projection over the whole codebook, then legal columns */
@@ -85,7 +89,7 @@ typedef struct zgr_plan zgr_plan;
 typedef struct {
   int64_t rows;    /* R_t: distinct prefixes of length t-1 */
   int64_t nnz;     /* legal (row, token) pairs = rows of table t+1 (N at t = L) */
-  int32_t fmt;     /* ZGR_FMT_DENSE or ZGR_FMT_SPARSE */
+  int32_t fmt;     /* ZGR_FMT_DENSE, ZGR_FMT_SPARSE or ZGR_FMT_DENSE_NEXT */
   int32_t stride;  /* S_t: slots per beam (max legal count of a row; V when dense) */
   int64_t bytes;   /* device bytes of this table */
   int32_t max_legal;  /* largest legal count of any row */
@@ -186,10 +190,11 @@ int32_t zgr_index_times(const zgr_index* idx, zgr_build_times* out);
 /* Device copies of table t (valid while idx lives; NULL where the table's
  * format has no such array): row_ptr int32 [rows+1], tok uint16 [nnz]
  * (sparse), bits uint32 [rows][ceil(V/32)] and rank uint16 [rows][ceil(V/32)]
- * (dense; set bits of the row before each word).  Errors: ZGR_E_ARG,
- * ZGR_E_STATE (not uploaded). */
+ * (dense; set bits of the row before each word), next int32 [rows][V]
+ * (DENSE_NEXT).  Errors: ZGR_E_ARG, ZGR_E_STATE (not uploaded). */
 int32_t zgr_index_device_table(const zgr_index* idx, int32_t t, const void** row_ptr,
-                               const void** tok, const void** bits, const void** rank);
+                               const void** tok, const void** bits, const void** rank,
+                               const void** next);
 
 /* Per-step statistics, t in 1..L.  Errors: ZGR_E_ARG. */
 int32_t zgr_index_stats(const zgr_index* idx, int32_t t, zgr_step_stats* out);

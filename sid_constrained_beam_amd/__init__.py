@@ -22,7 +22,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "zgr.h")
 ZGR_OK, ZGR_E_ARG, ZGR_E_DUP_SID, ZGR_E_TOKEN_RANGE, ZGR_E_SHAPE = 0, 1, 2, 3, 4
 ZGR_E_NOMEM, ZGR_E_HIP, ZGR_E_STATE, ZGR_E_CALLBACK, ZGR_E_DEVICE = 5, 6, 7, 8, 9
 ZGR_F32, ZGR_BF16, ZGR_F16 = 0, 1, 2
-ZGR_FMT_AUTO, ZGR_FMT_DENSE, ZGR_FMT_SPARSE = 0, 1, 2
+ZGR_FMT_AUTO, ZGR_FMT_DENSE, ZGR_FMT_SPARSE, ZGR_FMT_DENSE_NEXT = 0, 1, 2, 3
 ZGR_PROJ_AUTO, ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE = 0, 1, 2
 ZGR_UPLOAD_STAGED, ZGR_UPLOAD_DIRECT = 0, 1
 UPLOAD_CODES = {"staged": ZGR_UPLOAD_STAGED, "direct": ZGR_UPLOAD_DIRECT}
@@ -32,7 +32,8 @@ MODE_CODES = {"filter_first": ZGR_MODE_FILTER_FIRST, "score_first": ZGR_MODE_SCO
               "unconstrained": ZGR_MODE_UNCONSTRAINED}
 
 DTYPE_CODES = {"f32": ZGR_F32, "bf16": ZGR_BF16, "f16": ZGR_F16}
-FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR_FMT_SPARSE}
+FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR_FMT_SPARSE,
+             "N": ZGR_FMT_DENSE_NEXT}
 ZGR_PROJ_NAIVE = 3
 PROJ_CODES = {None: ZGR_PROJ_AUTO, "auto": ZGR_PROJ_AUTO, "full": ZGR_PROJ_FULL,
               "selective": ZGR_PROJ_SELECTIVE, "naive": ZGR_PROJ_NAIVE}
@@ -98,7 +99,8 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(BuildTimes), ctypes.POINTER(_P), _P]),
             "zgr_index_times": (_I32, [_P, ctypes.POINTER(BuildTimes)]),
             "zgr_index_device_table": (_I32, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
-                                              ctypes.POINTER(_P), ctypes.POINTER(_P)]),
+                                              ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                              ctypes.POINTER(_P)]),
             "zgr_index_stats": (_I32, [_P, _I32, ctypes.POINTER(StepStats)]),
             "zgr_index_host_table": (_I32, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                             ctypes.POINTER(_P)]),
@@ -281,8 +283,8 @@ def zgr_index_times(index: Index) -> dict:
 
 
 def zgr_index_device_table(index: Index, t: int):
-    """Device pointers of table t: (row_ptr, tok, bits, rank), 0 where absent."""
-    ptrs = [_P() for _ in range(4)]
+    """Device pointers of table t: (row_ptr, tok, bits, rank, next), 0 where absent."""
+    ptrs = [_P() for _ in range(5)]
     _check(lib().zgr_index_device_table(index.handle, t, *[ctypes.byref(p) for p in ptrs]))
     return tuple(p.value or 0 for p in ptrs)
 

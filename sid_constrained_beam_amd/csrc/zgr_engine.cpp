@@ -237,7 +237,7 @@ int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool heavy_step) {
 
 // Enqueue one step with the given projection.
 int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
-  const bool dense = a.tab.fmt == ZGR_FMT_DENSE;
+  const bool dense = a.tab.fmt == ZGR_FMT_DENSE || a.tab.fmt == ZGR_FMT_DENSE_NEXT;
   const int t = a.t;
   hipError_t e;
   int zmode;

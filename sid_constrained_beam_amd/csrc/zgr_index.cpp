@@ -27,6 +27,15 @@
 
 namespace {
 
+// Bytes of a table in HBM: row_ptr, then the sorted tokens (sparse), the
+// bitmap and its rank directory (dense), or the next-row matrix.
+int64_t table_device_bytes(const zgr::HostTable& h, int32_t words) {
+  const int64_t rp = (h.rows + 1) * 4;
+  if (h.fmt == ZGR_FMT_SPARSE) return rp + h.nnz * 2;
+  if (h.fmt == ZGR_FMT_DENSE_NEXT) return rp + h.rows * (int64_t)h.stride * 4;
+  return rp + h.rows * (int64_t)words * 6;
+}
+
 using Clock = std::chrono::steady_clock;
 double ms_since(Clock::time_point t0) {
   return std::chrono::duration<double, std::milli>(Clock::now() - t0).count();
@@ -172,8 +181,8 @@ int32_t build_host(const int32_t* sids, int64_t N, int32_t L, int32_t V, const i
   if (bits * L > 64) return fail(ZGR_E_SHAPE, "zgr_index_build_host: ceil(log2 V) * L > 64");
   if (fmt) {
     for (int l = 0; l < L; ++l)
-      if (fmt[l] < ZGR_FMT_AUTO || fmt[l] > ZGR_FMT_SPARSE)
-        return fail(ZGR_E_ARG, "zgr_index_build_host: fmt[t] must be AUTO, DENSE or SPARSE");
+      if (fmt[l] < ZGR_FMT_AUTO || fmt[l] > ZGR_FMT_DENSE_NEXT)
+        return fail(ZGR_E_ARG, "zgr_index_build_host: fmt[t] must be AUTO, DENSE, SPARSE or DENSE_NEXT");
   }
   const int T = pick_threads(opts ? opts->host_threads : 0, N);
   zgr_build_times tm{};
@@ -355,15 +364,24 @@ int32_t build_host(const int32_t* sids, int64_t N, int32_t L, int32_t V, const i
     const int32_t want = fmt ? fmt[l] : ZGR_FMT_AUTO;
     h.fmt = (want == ZGR_FMT_AUTO) ? (dense_bytes < sparse_bytes ? ZGR_FMT_DENSE : ZGR_FMT_SPARSE)
                                    : want;
-    h.stride = (h.fmt == ZGR_FMT_DENSE) ? V : h.max_legal;
-    if (h.fmt == ZGR_FMT_DENSE) {
+    const bool next_matrix = h.fmt == ZGR_FMT_DENSE_NEXT;
+    h.stride = (h.fmt != ZGR_FMT_SPARSE) ? V : h.max_legal;
+    if (h.fmt != ZGR_FMT_SPARSE) {
       try {
         h.bits.assign((size_t)h.rows * words, 0u);
         h.rank.resize((size_t)h.rows * words);
+        if (next_matrix) h.next.assign((size_t)h.rows * V, -1);
       } catch (...) {
         delete idx;
         return fail(ZGR_E_NOMEM, "zgr_index_build_host: host allocation");
       }
+      if (next_matrix)
+        // the alternative dense encoding: every (row, token) cell holds the
+        // entry's next row, -1 where the token is not legal
+        par_chunks(Tr, h.rows, [&](int64_t lo, int64_t hi, int) {
+          for (int64_t q = lo; q < hi; ++q)
+            for (int32_t j = h.row_ptr[q]; j < h.row_ptr[q + 1]; ++j) h.next[q * V + h.tok[j]] = j;
+        });
       // Bitmap, then the rank directory: set bits of the row before each word
       // (a dense entry's next row is row_ptr[r] + rank + popcount below the
       // token inside its word).
@@ -384,8 +402,7 @@ int32_t build_host(const int32_t* sids, int64_t N, int32_t L, int32_t V, const i
   tm.encode_ms = ms_since(t0);
   for (int l = 0; l < L; ++l) {
     const HostTable& h = idx->host[l];
-    tm.device_bytes += (int64_t)h.row_ptr.size() * 4 +
-                       (h.fmt == ZGR_FMT_DENSE ? (int64_t)h.bits.size() * 6 : h.nnz * 2);
+    tm.device_bytes += table_device_bytes(h, words);
   }
   tm.build_ms = ms_since(t_all);
   static uint64_t gen_counter = 0;
@@ -439,13 +456,15 @@ int32_t upload_index(zgr_index* idx, void* stream, const zgr_build_opts* opts, z
     void** dst;
   };
   std::vector<Piece> pieces;
-  void* ptrs[kMaxL][4] = {};
+  void* ptrs[kMaxL][5] = {};
   size_t total = 0;
   for (int l = 0; l < idx->L; ++l) {
     const HostTable& h = idx->host[l];
     pieces.push_back({h.row_ptr.data(), h.row_ptr.size() * 4, &ptrs[l][0]});
     if (h.fmt == ZGR_FMT_SPARSE) {
       pieces.push_back({h.tok.data(), h.tok.size() * 2, &ptrs[l][1]});
+    } else if (h.fmt == ZGR_FMT_DENSE_NEXT) {
+      pieces.push_back({h.next.data(), h.next.size() * 4, &ptrs[l][4]});
     } else {
       pieces.push_back({h.bits.data(), h.bits.size() * 4, &ptrs[l][2]});
       pieces.push_back({h.rank.data(), h.rank.size() * 2, &ptrs[l][3]});
@@ -542,6 +561,7 @@ int32_t upload_index(zgr_index* idx, void* stream, const zgr_build_opts* opts, z
     d.tok = (const uint16_t*)ptrs[l][1];
     d.bits = (const uint32_t*)ptrs[l][2];
     d.rank = (const uint16_t*)ptrs[l][3];
+    d.next = (const int32_t*)ptrs[l][4];
   }
   idx->on_device = true;
   if (times) *times = tm;
@@ -609,7 +629,8 @@ extern "C" int32_t zgr_index_times(const zgr_index* idx, zgr_build_times* out) {
 }
 
 extern "C" int32_t zgr_index_device_table(const zgr_index* idx, int32_t t, const void** row_ptr,
-                                          const void** tok, const void** bits, const void** rank) {
+                                          const void** tok, const void** bits, const void** rank,
+                                          const void** next) {
   using namespace zgr;
   if (!idx) return fail(ZGR_E_ARG, "zgr_index_device_table: null index");
   if (t < 1 || t > idx->L) return fail(ZGR_E_ARG, "zgr_index_device_table: t out of range");
@@ -619,6 +640,7 @@ extern "C" int32_t zgr_index_device_table(const zgr_index* idx, int32_t t, const
   if (tok) *tok = d.tok;
   if (bits) *bits = d.bits;
   if (rank) *rank = d.rank;
+  if (next) *next = d.next;
   return ZGR_OK;
 }
 
@@ -634,7 +656,7 @@ extern "C" int32_t zgr_index_stats(const zgr_index* idx, int32_t t, zgr_step_sta
   out->stride = h.stride;
   out->max_legal = h.max_legal;
   out->reserved = 0;
-  out->bytes = (h.rows + 1) * 4 + (h.fmt == ZGR_FMT_DENSE ? h.rows * words * 6 : h.nnz * 2);
+  out->bytes = table_device_bytes(h, (int32_t)words);
   return ZGR_OK;
 }
 
@@ -646,7 +668,7 @@ extern "C" int32_t zgr_index_host_table(const zgr_index* idx, int32_t t, const i
   const HostTable& h = idx->host[t - 1];
   if (row_ptr) *row_ptr = h.row_ptr.data();
   if (tok) *tok = h.tok.data();
-  if (bits) *bits = h.fmt == ZGR_FMT_DENSE ? h.bits.data() : nullptr;
+  if (bits) *bits = h.fmt != ZGR_FMT_SPARSE ? h.bits.data() : nullptr;
   return ZGR_OK;
 }
 

@@ -15,7 +15,7 @@ namespace zgr {
 constexpr int kMaxL = 8;
 // Internal table format: one row in which every codebook token is legal (the
 // unconstrained mode); laid out like a dense row.
-constexpr int32_t kFmtAll = 3;
+constexpr int32_t kFmtAll = 4;
 
 // One step's table on the host.
 struct HostTable {
@@ -28,6 +28,7 @@ struct HostTable {
   std::vector<uint16_t> tok;     // [nnz]
   std::vector<uint32_t> bits;    // dense: [rows][words]
   std::vector<uint16_t> rank;    // dense: [rows][words] set bits of the row before each word
+  std::vector<int32_t> next;     // next-row matrix encoding: [rows][V], -1 = not legal
 };
 
 // One step's table in HBM (plain pointers, passed to kernels by value).
@@ -41,6 +42,7 @@ struct DevTable {
   const uint16_t* tok;   // sparse only
   const uint32_t* bits;  // dense only
   const uint16_t* rank;  // dense only: [rows][words] set bits of the row before each word
+  const int32_t* next;   // next-row matrix encoding only: [rows][V], -1 = not legal
 };
 
 }  // namespace zgr

@@ -210,6 +210,58 @@ __device__ bool radix_narrow(RadixSel& s, int shift, const int* hist, int* sh) {
   return done;
 }
 
+// ---------------------------------------------------------------- dense rows
+//
+// A dense row is read one 32-token word at a time: the word's legal bits and
+// the row's legal count before the word (legal rank of its first set bit).
+// With the bitmap encoding both are stored (bitmap + rank directory).  With
+// the next-row matrix encoding they come from the word's 32 cells: a cell
+// >= 0 is a legal token, and its value minus the row's base is its legal
+// rank (a row's entries are numbered consecutively in token order).
+struct DWord {
+  uint32_t bits;
+  int rank;
+};
+
+__device__ __forceinline__ bool is_dense(int fmt) { return fmt != ZGR_FMT_SPARSE; }
+
+// NX selects the encoding at compile time, so the bitmap instantiations of
+// every kernel carry none of the next-row matrix code (nor its registers).
+template <bool NX>
+__device__ __forceinline__ DWord dense_word(const DevTable& tab, int64_t r, int w) {
+  if constexpr (!NX) {
+    const int64_t i = r * tab.words + w;
+    return {tab.bits[i], (int)tab.rank[i]};
+  } else {
+    const int32_t* nx = tab.next + r * (int64_t)tab.V + (w << 5);
+    const int nk = min(32, tab.V - (w << 5));
+    uint32_t b = 0;
+    int first = -1;
+    if (nk == 32 && (tab.V & 3) == 0) {
+      // highest quad first, so `first` ends at the word's lowest legal token
+      for (int q = 7; q >= 0; --q) {
+        const int4 v = ((const int4*)nx)[q];
+        const int c[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 3; k >= 0; --k)
+          if (c[k] >= 0) {
+            b |= 1u << (4 * q + k);
+            first = c[k];
+          }
+      }
+    } else {
+      for (int k = nk - 1; k >= 0; --k) {
+        const int v = nx[k];
+        if (v >= 0) {
+          b |= 1u << k;
+          first = v;
+        }
+      }
+    }
+    return {b, first >= 0 ? first - tab.row_ptr[r] : 0};
+  }
+}
+
 // ---------------------------------------------------------------- k_units
 
 constexpr int kUnitsCache = 16384;
@@ -236,7 +288,7 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
     }
     if (record) nlegal[b] = n;
     if (n == 0) return 0;
-    return tab.fmt == ZGR_FMT_DENSE ? dense_units : (n + kSparseTile - 1) / kSparseTile;
+    return is_dense(tab.fmt) ? dense_units : (n + kSparseTile - 1) / kSparseTile;
   };
   int mine = 0;
   for (int b = b0; b < b1; ++b) {
@@ -273,7 +325,7 @@ struct SelShape {
   static_assert(D * ES % (16 * G) == 0, "hidden size must split into 16-byte lane chunks");
 };
 
-template <int DT, int D>
+template <int DT, int D, bool NX>
 __global__ __launch_bounds__(kThreads) void k_score_selective(
     const int32_t* __restrict__ unit_start, int32_t M, DevTable tab,
     const int32_t* __restrict__ row_in, const void* __restrict__ hidden,
@@ -334,8 +386,9 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       const int nw = min(kDenseTile / 32, tab.words - w0);
       __syncthreads();  // previous unit's readers are done with lst
       if (threadIdx.x < 64) {
-        const uint32_t word = (lane < nw) ? tab.bits[(int64_t)r * tab.words + w0 + lane] : 0u;
-        int rk = (lane < nw) ? (int)tab.rank[(int64_t)r * tab.words + w0 + lane] : 0;
+        const DWord dw = (lane < nw) ? dense_word<NX>(tab, r, w0 + lane) : DWord{0u, 0};
+        const uint32_t word = dw.bits;
+        int rk = dw.rank;
         const int pc = __popc(word);
         const int incl = wave_incl_scan(pc);
         int pos = incl - pc;
@@ -412,10 +465,10 @@ __global__ __launch_bounds__(256) void k_naive_compact(const int32_t* __restrict
       ltok[s0 + j] = tab.tok[base + j];
     }
   } else {
-    const int64_t rw = (int64_t)r * tab.words;
     for (int w = lane; w < tab.words; w += 64) {
-      uint32_t x = tab.bits[rw + w];
-      int j = s0 + tab.rank[rw + w];
+      const DWord dw = tab.next ? dense_word<true>(tab, r, w) : dense_word<false>(tab, r, w);
+      uint32_t x = dw.bits;
+      int j = s0 + dw.rank;
       while (x) {
         const int v = (w << 5) + __ffs(x) - 1;
         x &= x - 1;
@@ -535,7 +588,7 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
 // every dense step; after a full projection of a sparse step they are
 // token-indexed (kZToken).  On dense rows the token of rank j is the row's
 // j-th set bit; the rank directory gives each word's first rank.
-template <int MODE, int DT, int D>
+template <int MODE, int DT, int D, bool NX>
 __global__ __launch_bounds__(kSelThreads) void k_request_step(
     DevTable tab, int32_t t, int32_t L, int32_t k_in, int32_t K, const int32_t* __restrict__ row_in,
     const float* __restrict__ cum_in, const void* __restrict__ hidden, const void* __restrict__ W,
@@ -714,10 +767,10 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       } else if (TOKEN_IDX) {
         // dense, token-indexed scores: walk the row's bitmap words; a set
         // bit's legal rank is the word's directory entry plus the bits below
-        const int64_t rw = (int64_t)r3 * tab.words;
         for (int w = lb; w < tab.words; w += LPB) {
-          uint32_t x = tab.bits[rw + w];
-          int j = at + tab.rank[rw + w];
+          const DWord dw = dense_word<NX>(tab, r3, w);
+          uint32_t x = dw.bits;
+          int j = at + dw.rank;
           while (x) {
             const int v = (w << 5) + __ffs(x) - 1;
             x &= x - 1;
@@ -782,8 +835,9 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       const int bl = u / tab.words, w = u - bl * tab.words;
       const int r = brow[bl];
       if (r < 0) continue;
-      uint32_t x = tab.bits[(int64_t)r * tab.words + w];
-      int j = cpre[bl] + tab.rank[(int64_t)r * tab.words + w];
+      const DWord dw = dense_word<NX>(tab, r, w);
+      uint32_t x = dw.bits;
+      int j = cpre[bl] + dw.rank;
       const uint32_t code0 = (uint32_t)(blo + bl) * S + (uint32_t)(w << 5);
       while (x) {
         const int k = __ffs(x) - 1;
@@ -807,10 +861,10 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
           if (!dense) {
             if (j < n) v = (TOKEN_IDX ? zb[tab.tok[bbase[bl] + j]] : zb[j]) - l;
           } else {
-            const int64_t w = (int64_t)r * tab.words + (j >> 5);
-            const uint32_t x = tab.bits[w];
+            const DWord dw = dense_word<NX>(tab, r, j >> 5);
+            const uint32_t x = dw.bits;
             if ((x >> (j & 31)) & 1u)
-              v = (TOKEN_IDX ? zb[j] : zb[tab.rank[w] + __popc(x & ((1u << (j & 31)) - 1u))]) - l;
+              v = (TOKEN_IDX ? zb[j] : zb[dw.rank + __popc(x & ((1u << (j & 31)) - 1u))]) - l;
           }
         }
         dbg[j] = v;
@@ -880,8 +934,9 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         const float zv = TOKEN_IDX ? zb[tab.tok[bbase[bl] + i]] : zb[i];
         fn(make_key(c + (zv - l), code0 + (uint32_t)i));
       } else {
-        uint32_t y = tab.bits[(int64_t)r * tab.words + i];
-        int j = tab.rank[(int64_t)r * tab.words + i];
+        const DWord dw = dense_word<NX>(tab, r, i);
+        uint32_t y = dw.bits;
+        int j = dw.rank;
         while (y) {
           const int v = (i << 5) + __ffs(y) - 1;
           y &= y - 1;
@@ -1021,10 +1076,10 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         token = tab.tok[next];
       } else {
         token = slot;
-        // entries of the row before this token: the rank directory gives the
-        // count before its word, popcount the rest of the word
-        const int64_t w = (int64_t)r * tab.words + (slot >> 5);
-        next = all_legal ? 0 : bbase[bl] + tab.rank[w] + __popc(tab.bits[w] & ((1u << (slot & 31)) - 1u));
+        // entries of the row before this token: the count before its word,
+        // then popcount within the word
+        const DWord dw = dense_word<NX>(tab, r, slot >> 5);
+        next = all_legal ? 0 : bbase[bl] + dw.rank + __popc(dw.bits & ((1u << (slot & 31)) - 1u));
       }
       parent_out[oi] = b;
       token_out[oi] = token;
@@ -1065,7 +1120,7 @@ constexpr int kLdsRow = kTileKBytes + 16;  // padded row pitch in bytes
 // dead beams are skipped.  The tile's rows, bitmap words and rank entries are
 // loaded into LDS before the k loop so the epilogue does not wait on them.
 // compact == 0: full rows, column = token.
-template <int DT, int BM, int BN>
+template <int DT, int BM, int BN, bool NX>
 __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A,
                                                       const void* __restrict__ Bm,
                                                       float* __restrict__ C, int32_t M, int32_t N,
@@ -1098,8 +1153,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
       for (int k = 0; k < TW; ++k) {
         const int wd = (n0 >> 5) + k;
         const bool ok = r >= 0 && r < tab.rows && wd < tab.words;
-        tbits[i * TW + k] = ok ? tab.bits[(int64_t)r * tab.words + wd] : 0u;
-        trank[i * TW + k] = ok ? (int)tab.rank[(int64_t)r * tab.words + wd] : 0;
+        const DWord dw = ok ? dense_word<NX>(tab, r, wd) : DWord{0u, 0};
+        tbits[i * TW + k] = dw.bits;
+        trank[i * TW + k] = dw.rank;
       }
     }
   }
@@ -1228,7 +1284,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
 // hidden size, operands streamed from global memory with 16-byte loads (the
 // four 16-lane groups of a wave cover 64 contiguous bytes of each row).  The
 // k order inside a 64-byte chunk is permuted identically for both operands.
-template <int DT>
+template <int DT, bool NX>
 __global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict__ A,
                                                          const void* __restrict__ Bm,
                                                          float* __restrict__ C, int32_t M,
@@ -1296,8 +1352,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict_
     r = (r >= 0 && r < tab.rows) ? r : -1;
     const bool ok = r >= 0 && tn < tab.words;
     trow[threadIdx.x] = r;
-    tbits[threadIdx.x] = ok ? tab.bits[(int64_t)r * tab.words + tn] : 0u;
-    trank[threadIdx.x] = ok ? (int)tab.rank[(int64_t)r * tab.words + tn] : 0;
+    const DWord dw = ok ? dense_word<NX>(tab, r, tn) : DWord{0u, 0};
+    tbits[threadIdx.x] = dw.bits;
+    trank[threadIdx.x] = dw.rank;
   }
   __syncthreads();
   const int bit = (wave & 1) * 16 + l16;
@@ -1368,9 +1425,9 @@ __global__ void k_lookup_items(TableSet ts, int32_t L, const int32_t* __restrict
       }
       r = (lo < hi0 && (int)tb.tok[lo] == v) ? lo : -1;
     } else {
-      const int64_t w = r * tb.words + (v >> 5);
-      const uint32_t x = tb.bits[w];
-      r = ((x >> (v & 31)) & 1u) ? lo0 + tb.rank[w] + __popc(x & ((1u << (v & 31)) - 1u)) : -1;
+      const DWord dw = tb.next ? dense_word<true>(tb, r, v >> 5) : dense_word<false>(tb, r, v >> 5);
+      const uint32_t x = dw.bits;
+      r = ((x >> (v & 31)) & 1u) ? lo0 + dw.rank + __popc(x & ((1u << (v & 31)) - 1u)) : -1;
     }
   }
   item[i] = (int32_t)r;
@@ -1419,8 +1476,12 @@ __global__ __launch_bounds__(256) void k_row_lse(const float* __restrict__ z, in
 template <int DT, int D>
 hipError_t launch_sel_typed(const StepArgs& a, hipStream_t s) {
   const int grid = a.n_cu * 8;
-  hipLaunchKernelGGL((k_score_selective<DT, D>), dim3(grid), dim3(kThreads), 0, s, a.unit_start, a.M,
-                     a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
+  if (a.tab.next)
+    hipLaunchKernelGGL((k_score_selective<DT, D, true>), dim3(grid), dim3(kThreads), 0, s, a.unit_start,
+                       a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
+  else
+    hipLaunchKernelGGL((k_score_selective<DT, D, false>), dim3(grid), dim3(kThreads), 0, s, a.unit_start,
+                       a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
   return hipGetLastError();
 }
 
@@ -1439,20 +1500,20 @@ hipError_t launch_sel_d(const StepArgs& a, hipStream_t s) {
   }
 }
 
-template <int DT>
+template <int DT, bool NX>
 hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
   const int V = a.tab.V;
-  const int compact = (a.tab.fmt == ZGR_FMT_DENSE && !a.plain_z) ? 1 : 0;
+  const int compact = ((a.tab.fmt == ZGR_FMT_DENSE || a.tab.fmt == ZGR_FMT_DENSE_NEXT) && !a.plain_z) ? 1 : 0;
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((V + bn - 1) / bn); };
   // the largest tile that still gives every compute unit two blocks (or one)
   if (tiles(128, 128) >= 2 * a.n_cu) {
-    hipLaunchKernelGGL((k_gemm_nt<DT, 128, 128>), dim3(tiles(128, 128)), dim3(kThreads), 0, s, a.hidden,
+    hipLaunchKernelGGL((k_gemm_nt<DT, 128, 128, NX>), dim3(tiles(128, 128)), dim3(kThreads), 0, s, a.hidden,
                        a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   } else if (tiles(64, 64) >= a.n_cu) {
-    hipLaunchKernelGGL((k_gemm_nt<DT, 64, 64>), dim3(tiles(64, 64)), dim3(kThreads), 0, s, a.hidden,
+    hipLaunchKernelGGL((k_gemm_nt<DT, 64, 64, NX>), dim3(tiles(64, 64)), dim3(kThreads), 0, s, a.hidden,
                        a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   } else {
-    hipLaunchKernelGGL(k_gemm_small<DT>, dim3(tiles(32, 32)), dim3(kThreads), 0, s, a.hidden, a.W, a.z,
+    hipLaunchKernelGGL((k_gemm_small<DT, NX>), dim3(tiles(32, 32)), dim3(kThreads), 0, s, a.hidden, a.W, a.z,
                        a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   }
   return hipGetLastError();
@@ -1481,10 +1542,11 @@ hipError_t launch_selective_score(const StepArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_full_projection(const StepArgs& a, hipStream_t s) {
+  const bool nx = a.tab.next != nullptr && !a.plain_z;  // only the compact epilogue reads the table
   switch (a.dtype) {
-    case ZGR_F32: return launch_proj_typed<ZGR_F32>(a, s);
-    case ZGR_BF16: return launch_proj_typed<ZGR_BF16>(a, s);
-    case ZGR_F16: return launch_proj_typed<ZGR_F16>(a, s);
+    case ZGR_F32: return nx ? launch_proj_typed<ZGR_F32, true>(a, s) : launch_proj_typed<ZGR_F32, false>(a, s);
+    case ZGR_BF16: return nx ? launch_proj_typed<ZGR_BF16, true>(a, s) : launch_proj_typed<ZGR_BF16, false>(a, s);
+    case ZGR_F16: return nx ? launch_proj_typed<ZGR_F16, true>(a, s) : launch_proj_typed<ZGR_F16, false>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1496,7 +1558,7 @@ hipError_t launch_full_projection(const StepArgs& a, hipStream_t s) {
 
 template <int DT, int D>
 hipError_t launch_scored_step(const StepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_request_step<kZScore, DT, D>), dim3(a.B * a.parts), dim3(kSelThreads), 0, s,
+  hipLaunchKernelGGL((k_request_step<kZScore, DT, D, false>), dim3(a.B * a.parts), dim3(kSelThreads), 0, s,
                      ZGR_STEP_ARGS);
   return hipGetLastError();
 }
@@ -1527,20 +1589,32 @@ hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s) {
       default: return hipErrorInvalidValue;
     }
   } else if (zmode == kZToken) {
-    hipLaunchKernelGGL((k_request_step<kZToken, ZGR_F32, 64>), grid, dim3(kSelThreads), 0, s,
-                       ZGR_STEP_ARGS);
+    if (a.tab.next)
+      hipLaunchKernelGGL((k_request_step<kZToken, ZGR_F32, 64, true>), grid, dim3(kSelThreads), 0, s,
+                         ZGR_STEP_ARGS);
+    else
+      hipLaunchKernelGGL((k_request_step<kZToken, ZGR_F32, 64, false>), grid, dim3(kSelThreads), 0, s,
+                         ZGR_STEP_ARGS);
     e = hipGetLastError();
   } else {
-    hipLaunchKernelGGL((k_request_step<kZSlot, ZGR_F32, 64>), grid, dim3(kSelThreads), 0, s,
-                       ZGR_STEP_ARGS);
+    if (a.tab.next)
+      hipLaunchKernelGGL((k_request_step<kZSlot, ZGR_F32, 64, true>), grid, dim3(kSelThreads), 0, s,
+                         ZGR_STEP_ARGS);
+    else
+      hipLaunchKernelGGL((k_request_step<kZSlot, ZGR_F32, 64, false>), grid, dim3(kSelThreads), 0, s,
+                         ZGR_STEP_ARGS);
     e = hipGetLastError();
   }
   return e;
 }
 
 hipError_t launch_request_merge(const StepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_request_step<kZParts, ZGR_F32, 64>), dim3(a.B), dim3(kSelThreads), 0, s,
-                     ZGR_STEP_ARGS);
+  if (a.tab.next)
+    hipLaunchKernelGGL((k_request_step<kZParts, ZGR_F32, 64, true>), dim3(a.B), dim3(kSelThreads), 0, s,
+                       ZGR_STEP_ARGS);
+  else
+    hipLaunchKernelGGL((k_request_step<kZParts, ZGR_F32, 64, false>), dim3(a.B), dim3(kSelThreads), 0, s,
+                       ZGR_STEP_ARGS);
   return hipGetLastError();
 }
 #undef ZGR_STEP_ARGS

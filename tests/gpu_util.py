@@ -163,7 +163,7 @@ def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests
     k_in = M // B
     st = setup.stats[t - 1]
     unc = mode == "unconstrained"
-    dense = st["fmt"] == zgr.ZGR_FMT_DENSE or unc  # slot = token
+    dense = st["fmt"] != zgr.ZGR_FMT_SPARSE or unc  # slot = token
     ambiguous = 0
     for q in (range(B) if requests is None else requests):
         sl = slice(q * k_in, (q + 1) * k_in)

@@ -43,7 +43,7 @@ def test_index_argument_errors():
                 np.array([[0, 1], [2, 3], [0, 1]], np.int32), 4)
     assert "0" in e.detail and "2" in e.detail
     _expect(zgr.ZGR_E_SHAPE, zgr.zgr_index_build_host, np.zeros((1, 5), np.int32), 65536)  # 80 bits
-    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, ok, 4, [3, 0])    # bad fmt code
+    _expect(zgr.ZGR_E_ARG, zgr.zgr_index_build_host, ok, 4, [4, 0])    # bad fmt code
     L = zgr.lib()
     h = ctypes.c_void_p()
     assert L.zgr_index_build_host(None, 2, 2, 4, None, None, ctypes.byref(h)) == zgr.ZGR_E_ARG

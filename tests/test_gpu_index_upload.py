@@ -14,6 +14,7 @@ CATALOGS = {
     "n1e4_v256": (CONFIGS["n1e4_v256"], None),
     "n1e8_v16384_small": (CONFIGS["n1e8_v16384"].scaled(N=400_000), None),
     "n1e6_v2048_all_dense": (CONFIGS["n1e6_v2048"].scaled(N=50_000), ["D", "D", "D"]),
+    "n1e6_v2048_next_matrix": (CONFIGS["n1e6_v2048"].scaled(N=50_000), ["N", "N", "S"]),
 }
 OPTIONS = [
     dict(),                                          # defaults: automatic threads, staged
@@ -58,14 +59,23 @@ def test_device_tables_match_host(name, opt):
         st = idx.stats(t)
         assert st == ref.stats(t)
         row_ptr, tok, bits = ref.host_table(t)
-        d_rp, d_tok, d_bits, d_rank = zgr.zgr_index_device_table(idx, t)
+        d_rp, d_tok, d_bits, d_rank, d_next = zgr.zgr_index_device_table(idx, t)
         assert np.array_equal(device_array(d_rp, row_ptr.shape, np.int32, stream), row_ptr)
         total += row_ptr.nbytes
         if st["fmt"] == zgr.ZGR_FMT_SPARSE:
-            assert d_bits == 0 and d_rank == 0
+            assert d_bits == 0 and d_rank == 0 and d_next == 0
             assert np.array_equal(device_array(d_tok, tok.shape, np.uint16, stream), tok)
             total += tok.nbytes
+        elif st["fmt"] == zgr.ZGR_FMT_DENSE_NEXT:
+            assert d_tok == 0 and d_bits == 0 and d_rank == 0
+            # cell (row, token) = the entry's next row, -1 where not legal
+            want = np.full((st["rows"], cfg.V), -1, np.int32)
+            rows_of = np.repeat(np.arange(st["rows"]), np.diff(row_ptr))
+            want[rows_of, tok.astype(np.int64)] = np.arange(st["nnz"], dtype=np.int32)
+            assert np.array_equal(device_array(d_next, want.shape, np.int32, stream), want)
+            total += want.nbytes
         else:
+            assert d_next == 0
             assert d_tok == 0
             assert np.array_equal(device_array(d_bits, bits.shape, np.uint32, stream), bits)
             pc = np.unpackbits(bits.view(np.uint8), axis=1, bitorder="little").reshape(

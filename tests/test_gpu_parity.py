@@ -291,3 +291,36 @@ def test_naive_baseline_matches_padded_slots():
     assert same > 0.99, same
     ok = np.isfinite(outs["selective"][1])
     assert np.allclose(outs["selective"][1][ok], outs["naive"][1][ok], atol=1e-4, rtol=0)
+
+
+NEXT_CASES = {
+    "n1e6_v2048": ["N", "N", "S"],
+    "n1e7_v2048_small": ["N", "N", "S", "S"],
+    "n5e7_v1024_dense_small": ["N", "N", "S", "S"],
+}
+
+
+@pytest.mark.parametrize("proj", ["selective", "full"])
+@pytest.mark.parametrize("name", list(NEXT_CASES))
+def test_next_row_matrix_encoding(name, proj):
+    """Dense steps stored as an int32 next-row matrix instead of the bitmap:
+    every step passes the oracle check, and the outputs equal the bitmap
+    encoding's bit for bit (only the table decode differs)."""
+    import torch
+    base = setup_of(name)
+    cfg = base.cfg.scaled(fmt=NEXT_CASES[name])
+    s = gu.Setup(cfg)
+    for t in range(1, cfg.L + 1):
+        want = zgr.ZGR_FMT_DENSE_NEXT if cfg.fmt[t - 1] == "N" else zgr.ZGR_FMT_SPARSE
+        assert s.stats[t - 1]["fmt"] == want
+    plan = s.plan(force=[proj] * cfg.L)
+    gu.gpu_trajectory(s, plan, list(range(cfg.B)))
+    bitmap = gu.Setup(cfg.scaled(fmt=["D" if f == "N" else f for f in cfg.fmt]), with_oracle=False)
+    outs = []
+    for setup in (s, bitmap):
+        p = setup.plan(force=[proj] * cfg.L)
+        item = torch.empty(cfg.B * cfg.K, dtype=torch.int64, device="cuda")
+        sc = torch.empty(cfg.B * cfg.K, dtype=torch.float32, device="cuda")
+        zgr.zgr_decode(p, setup.hidden_source(0), cfg.K, item, None, sc)
+        outs.append((item.cpu().numpy(), sc.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])

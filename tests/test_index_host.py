@@ -40,7 +40,7 @@ def check_against_oracle(sids, V, fmt=None, sample=None, seed=0, threads=0):
         counts = np.diff(row_ptr)
         assert counts.min() >= 1  # every row leads to at least one item
         assert st["max_legal"] == counts.max()
-        if st["fmt"] == zgr.ZGR_FMT_DENSE:
+        if st["fmt"] in (zgr.ZGR_FMT_DENSE, zgr.ZGR_FMT_DENSE_NEXT):
             assert st["stride"] == V
             assert bits is not None and bits.shape == (st["rows"], (V + 31) // 32)
             # bitmap rows hold exactly the sorted legal tokens
@@ -96,7 +96,7 @@ def test_slot_example_layout():
     assert np.diff(row_ptr).tolist() == g["legal_counts"]
 
 
-@pytest.mark.parametrize("fmt", [None, "D", "S"])
+@pytest.mark.parametrize("fmt", [None, "D", "S", "N"])
 @pytest.mark.parametrize("V,L,N,seed", [(4, 3, 40, 1), (16, 4, 900, 2), (300, 2, 5000, 3), (2, 6, 50, 4)])
 def test_random_catalogs(V, L, N, seed, fmt):
     rng = np.random.default_rng(seed)
@@ -144,7 +144,7 @@ def test_chunked_layout_matches_oracle(V, L, N, seed, threads):
     check_against_oracle(_random_sids(V, L, N, seed), V, threads=threads)
 
 
-@pytest.mark.parametrize("fmt", [None, "D", "S"])
+@pytest.mark.parametrize("fmt", [None, "D", "S", "N"])
 def test_layout_independent_of_threads(fmt):
     cfg = workload.CONFIGS["n1e4_v256"]
     sids = workload.catalog(cfg)
@@ -196,3 +196,21 @@ def test_presorted_catalog(threads):
     with pytest.raises(zgr.ZgrError) as e:
         zgr.zgr_index_build_host(dup, cfg.V, threads=threads)
     assert e.value.status == zgr.ZGR_E_DUP_SID and "rows 49 and 50" in e.value.detail
+
+
+def test_encoding_bytes():
+    """Device bytes per table: sparse 2 B per entry, bitmap 6 B per 32 tokens
+    of a row (bits + rank directory), next-row matrix 4 B per (row, token);
+    all plus the row offsets."""
+    cfg = workload.CONFIGS["n1e4_v256"]
+    sids = workload.catalog(cfg)
+    words = (cfg.V + 31) // 32
+    for f in ("D", "S", "N"):
+        idx, _ = zgr.zgr_index_build_host(sids, cfg.V, [f] * cfg.L)
+        for t in range(1, cfg.L + 1):
+            st = idx.stats(t)
+            rp = (st["rows"] + 1) * 4
+            want = {"S": rp + st["nnz"] * 2, "D": rp + st["rows"] * words * 6,
+                    "N": rp + st["rows"] * cfg.V * 4}[f]
+            assert st["bytes"] == want
+            assert st["stride"] == (st["max_legal"] if f == "S" else cfg.V)

@@ -95,7 +95,7 @@ class Config:
     K: int
     B: int
     dtype: str
-    fmt: Optional[List[str]] = None  # per-step table format override ("D"/"S"), None = automatic
+    fmt: Optional[List[str]] = None  # per-step table format ("D"/"S"/"N"), None = automatic
     seed_cat: int = 1000
     seed_w: int = 2000
     seed_h: int = 3000
