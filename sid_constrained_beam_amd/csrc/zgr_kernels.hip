@@ -628,6 +628,31 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   const uint32_t S = (uint32_t)tab.stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
+  // 0. loads whose addresses are known before the beams' rows: the first
+  //    round of this thread's phase-3 score loads (rank-indexed rows; the row
+  //    stride keeps them in bounds, values past a beam's legal count are
+  //    never used), and the merge's part counts and first keys.  They overlap
+  //    the row lookups below instead of following them.
+  constexpr int U = 8;  // phase-3 loads issued together per thread
+  int LPB = 1;          // phase-3 threads per beam
+  while (LPB < NT && LPB * 2 * max(nloc, 1) <= NT) LPB *= 2;
+  float zpf[U];
+  if constexpr (MODE == kZSlot) {
+    const int bl = threadIdx.x / LPB, lbb = threadIdx.x - bl * LPB;
+    const float* zz = z + (int64_t)(b0 + (bl < nloc ? bl : 0)) * ldz;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = lbb + u * LPB;
+      zpf[u] = (bl < nloc && j < ldz) ? zz[j] : 0.f;
+    }
+  }
+  int mcnt = 0;
+  uint64_t mkey0 = 0;
+  if constexpr (MERGE) {
+    if ((int)threadIdx.x < P) mcnt = part_cnt[q * P + threadIdx.x];
+    if ((int)threadIdx.x < P * K) mkey0 = part_keys[(int64_t)q * P * K + threadIdx.x];
+  }
+
   // 1. the block's beams
   int cnt = 0, items = 0;
   if ((int)threadIdx.x < nloc) {
@@ -723,10 +748,23 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     __syncthreads();
   }
 
+  // Dense rank-indexed scores get their slot codes after phase 3 (below):
+  // LPW lanes share a (beam, word) pair, each walking its own 32/LPW bits.
+  // LPW grows while the pairs leave threads idle, so a full row at the first
+  // step needs no long serial walks.  The first round's bitmap words are
+  // loaded now so that phase 3 hides their latency.
+  const bool code_pass = !MERGE && dense && store && !TOKEN_IDX;
+  const int pairs = nloc * tab.words;
+  int LPW = 1;
+  while (LPW < 32 && pairs * LPW * 2 <= NT) LPW *= 2;
+  DWord dwpf{0u, 0};
+  if (code_pass && (int)threadIdx.x < pairs * LPW) {
+    const int pr = threadIdx.x / LPW, bl = pr / tab.words, w = pr - bl * tab.words;
+    if (brow[bl] >= 0) dwpf = dense_word<NX>(tab, brow[bl], w);
+  }
+
   // 3. legal-only log-sum-exp of every beam, LPB threads per beam
   if constexpr (!MERGE) {
-    int LPB = 1;
-    while (LPB < NT && LPB * 2 * max(nloc, 1) <= NT) LPB *= 2;
     const int bl3 = threadIdx.x / LPB, lb = threadIdx.x - bl3 * LPB;
     const int r3 = (bl3 < nloc) ? brow[bl3] : -1;
     const float* z3 = z + (int64_t)(b0 + (bl3 < nloc ? bl3 : 0)) * ldz;
@@ -742,7 +780,6 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         s += __expf(zv - m);
       }
     };
-    constexpr int U = 8;  // loads issued together per thread
     if (r3 >= 0) {
       if (MODE == kZScore && store) {
         // the projection left the scores in keys[]
@@ -753,7 +790,8 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             const int j = j0 + u * LPB;
-            if (j < n3) zv[u] = TOKEN_IDX ? z3[tab.tok[bbase[bl3] + j]] : z3[j];
+            if (j < n3)
+              zv[u] = TOKEN_IDX ? z3[tab.tok[bbase[bl3] + j]] : (MODE == kZSlot && j0 == lb) ? zpf[u] : z3[j];
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) {
@@ -787,7 +825,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             const int j = j0 + u * LPB;
-            if (j < n3) zv[u] = z3[j];
+            if (j < n3) zv[u] = (MODE == kZSlot && j0 == lb) ? zpf[u] : z3[j];
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) {
@@ -827,18 +865,20 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     }
   }
   __syncthreads();
-  if (!MERGE && dense && store && !TOKEN_IDX) {
-    // slot codes of the dense candidates: each (beam, word) pair walks its set
-    // bits; a bit's legal rank is the word's directory entry plus the set bits
-    // below it
-    for (int u = threadIdx.x; u < nloc * tab.words; u += NT) {
-      const int bl = u / tab.words, w = u - bl * tab.words;
+  if (code_pass) {
+    // a bit's legal rank is the word's count before it plus the set bits below it
+    const int nb = 32 / LPW;
+    const uint32_t sub_mask = (nb == 32) ? 0xFFFFFFFFu : ((1u << nb) - 1u);
+    for (int u = threadIdx.x; u < pairs * LPW; u += NT) {
+      const int pr = u / LPW, sub = u - pr * LPW;
+      const int bl = pr / tab.words, w = pr - bl * tab.words;
       const int r = brow[bl];
       if (r < 0) continue;
-      const DWord dw = dense_word<NX>(tab, r, w);
-      uint32_t x = dw.bits;
-      int j = cpre[bl] + dw.rank;
-      const uint32_t code0 = (uint32_t)(blo + bl) * S + (uint32_t)(w << 5);
+      const DWord dw = (u == (int)threadIdx.x) ? dwpf : dense_word<NX>(tab, r, w);
+      const int lo = sub * nb;  // <= 31
+      uint32_t x = (dw.bits >> lo) & sub_mask;
+      int j = cpre[bl] + dw.rank + __popc(dw.bits & ((1u << lo) - 1u));
+      const uint32_t code0 = (uint32_t)(blo + bl) * S + (uint32_t)((w << 5) + lo);
       while (x) {
         const int k = __ffs(x) - 1;
         x &= x - 1;
@@ -875,16 +915,17 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
 
   if constexpr (MERGE) {
     // the parts' keys (already final) into LDS, in part order
-    int c = 0;
-    if ((int)threadIdx.x < P) c = part_cnt[q * P + threadIdx.x];
-    const int exp_ = block_excl_scan<NT>(c, sh, &C);
-    if ((int)threadIdx.x < P) pre[threadIdx.x] = exp_;
+    const int exp_ = block_excl_scan<NT>(mcnt, sh, &C);
+    if ((int)threadIdx.x < P) {
+      pre[threadIdx.x] = exp_;
+      cpre[threadIdx.x] = mcnt;  // part counts (the merge has no per-beam candidates)
+    }
     __syncthreads();
     uint32_t o = 0;
     for (int f = threadIdx.x; f < P * K; f += NT) {
       const int pi = f / K, i = f - pi * K;
-      if (i < part_cnt[q * P + pi]) {
-        const uint64_t kk = part_keys[(int64_t)(q * P + pi) * K + i];
+      if (i < cpre[pi]) {
+        const uint64_t kk = (f == (int)threadIdx.x) ? mkey0 : part_keys[(int64_t)(q * P + pi) * K + i];
         keys[pre[pi] + i] = kk;
         o = max(o, (uint32_t)(kk >> 32));
       }
@@ -981,9 +1022,21 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         const uint64_t k = i < C ? keys[i] : 0ull;
         const int bn = i < C ? bin_of(k) : kDistBins;
         if (__ballot(bn <= bstar) == 0) continue;  // wave-uniform: nothing to keep here
-        const int a1 = wave_alloc(bn < bstar ? 1 : 0, &pos);
+        // one wave scan for both appends: selected keys in the low half,
+        // boundary keys in the high half (at most 64 of each per wave)
+        const int inc = (bn < bstar ? 1 : 0) | (bn == bstar ? (1 << 16) : 0);
+        const int incl = wave_incl_scan(inc);
+        const int tot = __shfl(incl, 63);
+        int b1 = 0, b2 = 0;
+        if (lane == 63) {
+          if (tot & 0xFFFF) b1 = atomicAdd(&pos, tot & 0xFFFF);
+          if (tot >> 16) b2 = atomicAdd(&pos2, tot >> 16);
+        }
+        b1 = __shfl(b1, 63);
+        b2 = __shfl(b2, 63);
+        const int ex = incl - inc;
+        const int a1 = b1 + (ex & 0xFFFF), a2 = b2 + (ex >> 16);
         if (bn < bstar && a1 < kMaxK) sel[a1] = k;
-        const int a2 = wave_alloc(bn == bstar ? 1 : 0, &pos2);
         if (bn == bstar && a2 < kBoundary) bnd[a2] = k;
       }
     } else {
@@ -1051,15 +1104,23 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     return;
   }
 
-  // 5. sorted position of a selected key = number of selected keys above it
-  uint64_t mine = 0;
-  int rank = 0;
-  if ((int)threadIdx.x < nsel) {
-    mine = sel[threadIdx.x];
-    for (int j = 0; j < nsel; ++j) rank += sel[j] > mine ? 1 : 0;
+  // 5. sorted position of a selected key = number of selected keys above it;
+  //    G = NT / nsel lanes (a power of two, within one wave) share a key,
+  //    each counting over a strided part of the selection
+  {
+    int G = 1;
+    while (G < 64 && G * 2 * max(nsel, 1) <= NT) G *= 2;
+    const int i = threadIdx.x / G, g = threadIdx.x - i * G;
+    uint64_t mine = 0;
+    int rank = 0;
+    if (i < nsel) {
+      mine = sel[i];
+      for (int j = g; j < nsel; j += G) rank += sel[j] > mine ? 1 : 0;
+    }
+    for (int o = G >> 1; o >= 1; o >>= 1) rank += __shfl_xor(rank, o);
+    __syncthreads();
+    if (i < nsel && g == 0) keys[rank] = mine;
   }
-  __syncthreads();
-  if ((int)threadIdx.x < nsel) keys[rank] = mine;
   __syncthreads();
   for (int o = threadIdx.x; o < K; o += NT) {
     const int64_t oi = (int64_t)q * K + o;
@@ -1134,7 +1195,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   constexpr int TW = BN / 32;                                     // bitmap words per tile row
   __shared__ __attribute__((aligned(16))) char As[BM * kLdsRow];
   __shared__ __attribute__((aligned(16))) char Bs[BN * kLdsRow];
-  __shared__ int trow[BM];
   __shared__ uint32_t tbits[BM * TW];
   __shared__ int trank[BM * TW];
   const int nbm = (M + BM - 1) / BM;
@@ -1145,17 +1205,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   const char* Ab = (const char*)A;
   const char* Bb = (const char*)Bm;
   const int64_t rowbytes = (int64_t)D * ES;
-  if (compact) {
-    for (int i = threadIdx.x; i < BM; i += kThreads) {
-      const int gm = m0 + i;
-      const int r = gm < M ? row_in[gm] : -1;
-      trow[i] = (r >= 0 && r < tab.rows) ? r : -1;
+  // compact epilogue: the tile rows' bitmap words and ranks are loaded into
+  // registers now (thread i < BM owns tile row i) and reach LDS only after
+  // the k loop, so their two dependent loads overlap the product
+  static_assert(BM <= kThreads, "one tile row per thread");
+  DWord pdw[TW];
+#pragma unroll
+  for (int k = 0; k < TW; ++k) pdw[k] = DWord{0u, 0};
+  if (compact && (int)threadIdx.x < BM) {
+    const int gm = m0 + threadIdx.x;
+    const int r = gm < M ? row_in[gm] : -1;
+    if (r >= 0 && r < tab.rows) {
+#pragma unroll
       for (int k = 0; k < TW; ++k) {
         const int wd = (n0 >> 5) + k;
-        const bool ok = r >= 0 && r < tab.rows && wd < tab.words;
-        const DWord dw = ok ? dense_word<NX>(tab, r, wd) : DWord{0u, 0};
-        tbits[i * TW + k] = dw.bits;
-        trank[i * TW + k] = dw.rank;
+        if (wd < tab.words) pdw[k] = dense_word<NX>(tab, r, wd);
       }
     }
   }
@@ -1262,6 +1326,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
       }
     return;
   }
+  if ((int)threadIdx.x < BM) {
+#pragma unroll
+    for (int k = 0; k < TW; ++k) {
+      tbits[threadIdx.x * TW + k] = pdw[k].bits;
+      trank[threadIdx.x * TW + k] = pdw[k].rank;
+    }
+  }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < IB; ++i)
 #pragma unroll
@@ -1280,45 +1352,58 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
 // ---------------------------------------------------------------- k_gemm_small (MFMA 16x16)
 
 // Full projection for few beams (the first step has one beam per request):
-// 32x32 output tiles per block, one 16x16 MFMA tile per wave over the whole
-// hidden size, operands streamed from global memory with 16-byte loads (the
-// four 16-lane groups of a wave cover 64 contiguous bytes of each row).  The
-// k order inside a 64-byte chunk is permuted identically for both operands.
+// 32x32 output tiles per block, one 16x16 MFMA tile per wave, operands
+// streamed from global memory with 16-byte loads (the four 16-lane groups of
+// a wave cover 64 contiguous bytes of each row).  The k order inside a 64-byte
+// chunk is permuted identically for both operands.  Few blocks run, so each
+// tile is split over two wave groups by halves of the hidden size (summed
+// through LDS) and a wave keeps 8 chunks of loads in flight; the compact
+// epilogue's row lookups are issued before the product.
+constexpr int kSmallThreads = 512;
+
 template <int DT, bool NX>
-__global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict__ A,
-                                                         const void* __restrict__ Bm,
-                                                         float* __restrict__ C, int32_t M,
-                                                         int32_t N, int32_t D, int64_t ldc,
-                                                         int32_t compact, DevTable tab,
-                                                         const int32_t* __restrict__ row_in) {
-  __shared__ int trow[32];
+__global__ __launch_bounds__(kSmallThreads) void k_gemm_small(const void* __restrict__ A,
+                                                              const void* __restrict__ Bm,
+                                                              float* __restrict__ C, int32_t M,
+                                                              int32_t N, int32_t D, int64_t ldc,
+                                                              int32_t compact, DevTable tab,
+                                                              const int32_t* __restrict__ row_in) {
   __shared__ uint32_t tbits[32];
   __shared__ int trank[32];
+  __shared__ f32x4 part[4][64];
   constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
-  constexpr int U = 4;
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tw = wave & 3, ks = wave >> 2;  // tile quarter, k half
   const int nbn = (N + 31) / 32;
   const int tm = blockIdx.x / nbn, tn = blockIdx.x - tm * nbn;
   const int l16 = lane & 15, g = lane >> 4;
-  const int m = tm * 32 + (wave >> 1) * 16 + l16;
-  const int n = tn * 32 + (wave & 1) * 16 + l16;
+  const int m = tm * 32 + (tw >> 1) * 16 + l16;
+  const int n = tn * 32 + (tw & 1) * 16 + l16;
   const int64_t rowbytes = (int64_t)D * ES;
+  const int nch = (int)(rowbytes / 64);
+  const int c0 = ks * (nch / 2), c1 = ks ? nch : nch / 2;
+  DWord pdw{0u, 0};
+  if (compact && threadIdx.x < 32) {
+    const int gm = tm * 32 + threadIdx.x;
+    const int r = gm < M ? row_in[gm] : -1;
+    if (r >= 0 && r < tab.rows && tn < tab.words) pdw = dense_word<NX>(tab, r, tn);
+  }
   const char* ap = (const char*)A + (int64_t)min(m, M - 1) * rowbytes + g * 16;
   const char* bp = (const char*)Bm + (int64_t)min(n, N - 1) * rowbytes + g * 16;
-  const int nch = (int)(rowbytes / 64);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < nch; c += U) {
+  for (int c = c0; c < c1; c += U) {
     uint4 a[U], b[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c + u < nch) {
+      if (c + u < c1) {
         a[u] = *(const uint4*)(ap + (int64_t)(c + u) * 64);
         b[u] = *(const uint4*)(bp + (int64_t)(c + u) * 64);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (c + u >= nch) break;
+      if (c + u >= c1) break;
       if constexpr (DT == ZGR_F32) {
         const f32x4 av = __builtin_bit_cast(f32x4, a[u]);
         const f32x4 bv = __builtin_bit_cast(f32x4, b[u]);
@@ -1333,12 +1418,23 @@ __global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict_
       }
     }
   }
+  // the second k half hands its partial tile to the first
+  if (ks) part[tw][lane] = acc;
+  if (compact && threadIdx.x < 32) {
+    tbits[threadIdx.x] = pdw.bits;
+    trank[threadIdx.x] = pdw.rank;
+  }
+  __syncthreads();
+  if (ks) return;
+  const f32x4 o = part[tw][lane];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) acc[v] += o[v];
   // 16x16 accumulator layout: lane -> column l16, register v -> row 4*g + v
   if (!compact) {
     if (n < N) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = tm * 32 + (wave >> 1) * 16 + 4 * g + v;
+        const int row = tm * 32 + (tw >> 1) * 16 + 4 * g + v;
         if (row < M) C[(int64_t)row * ldc + n] = acc[v];
       }
     }
@@ -1346,21 +1442,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_small(const void* __restrict_
   }
   // dense table: legal columns only, at their legal rank (the block's 32
   // columns are one bitmap word)
-  if (threadIdx.x < 32) {
-    const int gm = tm * 32 + threadIdx.x;
-    int r = gm < M ? row_in[gm] : -1;
-    r = (r >= 0 && r < tab.rows) ? r : -1;
-    const bool ok = r >= 0 && tn < tab.words;
-    trow[threadIdx.x] = r;
-    const DWord dw = ok ? dense_word<NX>(tab, r, tn) : DWord{0u, 0};
-    tbits[threadIdx.x] = dw.bits;
-    trank[threadIdx.x] = dw.rank;
-  }
-  __syncthreads();
-  const int bit = (wave & 1) * 16 + l16;
+  const int bit = (tw & 1) * 16 + l16;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int rl = (wave >> 1) * 16 + 4 * g + v;
+    const int rl = (tw >> 1) * 16 + 4 * g + v;
     const uint32_t x = tbits[rl];
     if ((x >> bit) & 1u)
       C[(int64_t)(tm * 32 + rl) * ldc + trank[rl] + __popc(x & ((1u << bit) - 1u))] = acc[v];
@@ -1513,7 +1598,7 @@ hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_gemm_nt<DT, 64, 64, NX>), dim3(tiles(64, 64)), dim3(kThreads), 0, s, a.hidden,
                        a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   } else {
-    hipLaunchKernelGGL((k_gemm_small<DT, NX>), dim3(tiles(32, 32)), dim3(kThreads), 0, s, a.hidden, a.W, a.z,
+    hipLaunchKernelGGL((k_gemm_small<DT, NX>), dim3(tiles(32, 32)), dim3(kSmallThreads), 0, s, a.hidden, a.W, a.z,
                        a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   }
   return hipGetLastError();

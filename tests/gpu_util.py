@@ -50,10 +50,10 @@ def to_device_bits(bits, dtype):
 class Setup:
     """One workload on the GPU and in the oracle."""
 
-    def __init__(self, cfg, with_oracle=True):
+    def __init__(self, cfg, with_oracle=True, sids=None):
         import torch
         self.cfg = cfg
-        self.sids = workload.catalog(cfg)
+        self.sids = workload.catalog(cfg) if sids is None else np.ascontiguousarray(sids, np.int32)
         fmt = cfg.fmt
         self.index, self.rank = zgr.zgr_index_upload(self.sids, cfg.V, fmt)
         self.W_bits, self.W_f32 = [], []
