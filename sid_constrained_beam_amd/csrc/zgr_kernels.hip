@@ -533,6 +533,10 @@ constexpr int kMaxK = 1024;
 // sub-bins per octave (monotone in the distance; 1728 bins used).
 constexpr int kDistBins = 2 * kSelThreads;
 constexpr int kBoundary = kDistBins / 2;  // boundary keys resolved by rank counting
+// At most this many stored keys: every key is ranked directly (the number of
+// keys above it), which yields the sorted selection in one pass.  The pass
+// moves 8 C^2 bytes through LDS, so it only pays for small C.
+constexpr int kSmallSel = 128;
 
 __device__ __forceinline__ int dist_bin(uint32_t d) {
   if (d < 64u) return (int)d;
@@ -944,13 +948,19 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   // Log-scaled histogram of each key's distance below the best key's ord:
   // bins above the boundary bin are taken whole, the boundary bin is resolved
   // exactly among its own keys.
+  // Few stored keys skip the histogram: each is ranked directly below.
   auto bin_of = [&](uint64_t k) { return dist_bin(omax - (uint32_t)(k >> 32)); };
-  for (int i = threadIdx.x; i < kDistBins; i += NT) dhist[i] = 0;
-  __syncthreads();
-  if (MERGE) {
-    if (C > K)
-      for (int i = threadIdx.x; i < C; i += NT) atomicAdd(&dhist[bin_of(keys[i])], 1);
+  const bool small = store && C <= kSmallSel;
+  const bool histo = C > K && !small;
+  if (histo) {
+    for (int i = threadIdx.x; i < kDistBins; i += NT) dhist[i] = 0;
     __syncthreads();
+  }
+  if (MERGE) {
+    if (histo) {
+      for (int i = threadIdx.x; i < C; i += NT) atomicAdd(&dhist[bin_of(keys[i])], 1);
+      __syncthreads();
+    }
   } else if (store) {
     for (int i = threadIdx.x; i < C; i += NT) {
       const uint64_t e = keys[i];
@@ -958,7 +968,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       const int bl = (int)(code / S) - blo;
       const uint64_t k = make_key(bcum[bl] + (__uint_as_float((uint32_t)(e >> 32)) - blse[bl]), code);
       keys[i] = k;
-      if (C > K) atomicAdd(&dhist[bin_of(k)], 1);
+      if (histo) atomicAdd(&dhist[bin_of(k)], 1);
     }
     __syncthreads();
   }
@@ -989,7 +999,31 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     }
   };
   const int nsel = min(C, K);
-  if (C <= K) {
+  if (small) {
+    // rank of a key = number of keys above it (keys are distinct); G lanes
+    // share a key, each counting over a strided part; the K best land in
+    // sel[] already in order
+    int G = 1;
+    while (G < 64 && G * 2 * max(C, 1) <= NT) G *= 2;
+    const int per = NT / G;
+    for (int i0 = 0; i0 < C; i0 += per) {
+      const int i = i0 + (int)threadIdx.x / G, g = (int)threadIdx.x % G;
+      const uint64_t mine = i < C ? keys[i] : 0ull;
+      int rank = 0;
+      if (i < C)
+        for (int j0 = g; j0 < C; j0 += 8 * G) {
+          // eight independent LDS reads in flight: the reads are
+          // unconditional (clamped index), the bound applies to the count
+          uint64_t kk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) kk[u] = keys[min(j0 + u * G, C - 1)];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) rank += (j0 + u * G < C && kk[u] > mine) ? 1 : 0;
+        }
+      for (int o = G >> 1; o >= 1; o >>= 1) rank += __shfl_xor(rank, o);
+      if (i < C && g == 0 && rank < K) sel[rank] = mine;
+    }
+  } else if (C <= K) {
     for (int i = threadIdx.x; i < C; i += NT) sel[i] = keys[i];  // C <= K <= kSelCap: stored
   } else {
     if (!store) {
@@ -1098,7 +1132,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   __syncthreads();
 
   if (!MERGE && P > 1) {
-    // a part: its best keys go to the merge unsorted
+    // a part: its best keys go to the merge (in any order)
     for (int i = threadIdx.x; i < nsel; i += NT) part_keys[(int64_t)blockIdx.x * K + i] = sel[i];
     if (threadIdx.x == 0) part_cnt[blockIdx.x] = nsel;
     return;
@@ -1106,8 +1140,34 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
 
   // 5. sorted position of a selected key = number of selected keys above it;
   //    G = NT / nsel lanes (a power of two, within one wave) share a key,
-  //    each counting over a strided part of the selection
-  {
+  //    each counting over a strided part of the selection (the direct ranking
+  //    above already left them in order).  Rank counting moves 8 nsel^2 bytes
+  //    through LDS, so more than 256 keys go through a bitonic network in
+  //    place instead.
+  const bool in_order = small;
+  const bool bitonic = !in_order && nsel > 256;
+  const uint64_t* sorted = (in_order || bitonic) ? sel : keys;
+  if (bitonic) {
+    int n2 = 1;
+    while (n2 < nsel) n2 <<= 1;  // <= kMaxK
+    for (int i = nsel + threadIdx.x; i < n2; i += NT) sel[i] = 0ull;  // padding sorts last
+    __syncthreads();
+    for (int k2 = 2; k2 <= n2; k2 <<= 1)
+      for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+        for (int i = threadIdx.x; i < n2; i += NT) {
+          const int l = i ^ j2;
+          if (l > i) {
+            const uint64_t x = sel[i], y = sel[l];
+            // descending where (i & k2) == 0, so the last round is descending
+            if (((i & k2) == 0) ? (x < y) : (x > y)) {
+              sel[i] = y;
+              sel[l] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+  } else if (!in_order) {
     int G = 1;
     while (G < 64 && G * 2 * max(nsel, 1) <= NT) G *= 2;
     const int i = threadIdx.x / G, g = threadIdx.x - i * G;
@@ -1120,12 +1180,12 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     for (int o = G >> 1; o >= 1; o >>= 1) rank += __shfl_xor(rank, o);
     __syncthreads();
     if (i < nsel && g == 0) keys[rank] = mine;
+    __syncthreads();
   }
-  __syncthreads();
   for (int o = threadIdx.x; o < K; o += NT) {
     const int64_t oi = (int64_t)q * K + o;
     if (o < nsel) {
-      const uint64_t key = keys[o];
+      const uint64_t key = sorted[o];
       const uint32_t code = 0xFFFFFFFFu - (uint32_t)key;
       const int bl = (int)(code / S);
       const int slot = (int)(code - (uint32_t)bl * S);
