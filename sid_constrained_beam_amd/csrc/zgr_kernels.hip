@@ -632,24 +632,11 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   const uint32_t S = (uint32_t)tab.stride;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
-  // 0. loads whose addresses are known before the beams' rows: the first
-  //    round of this thread's phase-3 score loads (rank-indexed rows; the row
-  //    stride keeps them in bounds, values past a beam's legal count are
-  //    never used), and the merge's part counts and first keys.  They overlap
-  //    the row lookups below instead of following them.
+  // 0. the merge's part counts and first keys: their addresses are known
+  //    before the beams' rows, so they overlap the row lookups below
   constexpr int U = 8;  // phase-3 loads issued together per thread
   int LPB = 1;          // phase-3 threads per beam
   while (LPB < NT && LPB * 2 * max(nloc, 1) <= NT) LPB *= 2;
-  float zpf[U];
-  if constexpr (MODE == kZSlot) {
-    const int bl = threadIdx.x / LPB, lbb = threadIdx.x - bl * LPB;
-    const float* zz = z + (int64_t)(b0 + (bl < nloc ? bl : 0)) * ldz;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = lbb + u * LPB;
-      zpf[u] = (bl < nloc && j < ldz) ? zz[j] : 0.f;
-    }
-  }
   int mcnt = 0;
   uint64_t mkey0 = 0;
   if constexpr (MERGE) {
@@ -795,7 +782,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
           for (int u = 0; u < U; ++u) {
             const int j = j0 + u * LPB;
             if (j < n3)
-              zv[u] = TOKEN_IDX ? z3[tab.tok[bbase[bl3] + j]] : (MODE == kZSlot && j0 == lb) ? zpf[u] : z3[j];
+              zv[u] = TOKEN_IDX ? z3[tab.tok[bbase[bl3] + j]] : z3[j];
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) {
@@ -829,7 +816,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             const int j = j0 + u * LPB;
-            if (j < n3) zv[u] = (MODE == kZSlot && j0 == lb) ? zpf[u] : z3[j];
+            if (j < n3) zv[u] = z3[j];
           }
 #pragma unroll
           for (int u = 0; u < U; ++u) {
