@@ -311,8 +311,10 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     zmode = 2;
   } else {
     a.ldz = a.tab.stride;
-    e = prof_launch(p, ZGR_KERNEL_UNITS, t, s, [&] { return launch_units(a, s); });
-    if (e != hipSuccess) return hip_fail(e, "unit count launch");
+    if (!dense) {  // dense rows all have the same tiles: no unit scan needed
+      e = prof_launch(p, ZGR_KERNEL_UNITS, t, s, [&] { return launch_units(a, s); });
+      if (e != hipSuccess) return hip_fail(e, "unit count launch");
+    }
     e = prof_launch(p, ZGR_KERNEL_SELECTIVE, t, s, [&] { return launch_selective_score(a, s); });
     if (e != hipSuccess) return hip_fail(e, "selective score launch");
     zmode = 1;

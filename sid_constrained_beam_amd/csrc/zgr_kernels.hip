@@ -13,22 +13,26 @@
 // read in place: no compacted candidate list and no temporary matrix.
 //
 // Kernels of a step:
-//   k_units            per beam: legal count n_b and its number of work units;
-//                      an exclusive scan over the M beams (not over candidates:
-//                      slot addresses never depend on other beams).
+//   k_units            sparse steps, per beam: legal count n_b and its number
+//                      of work units; an exclusive scan over the M beams (not
+//                      over candidates: slot addresses never depend on other
+//                      beams).
 //   k_score_selective  persistent grid over (beam, tile) units: each unit
-//                      reads the beam's legal tokens (sparse: tok[row_ptr[r]+j];
-//                      dense: set bits of the row's bitmap) and computes
-//                      z = W_t[token] . h_beam with the weight row read in place
-//                      by a group of lanes (16-byte loads), h kept in registers,
-//                      a lane-group shuffle reduction, z stored at the slot
-//                      (sparse: rank j; dense: the token's legal rank).
+//                      reads the beam's legal tokens (sparse: tok[row_ptr[r]+j],
+//                      a contiguous range of units per block; dense: set bits
+//                      of a 1024-token tile of the row's bitmap, tiles split
+//                      over the XCDs so each XCD's L2 holds its tiles' weight
+//                      rows) and computes z = W_t[token] . h_beam with the
+//                      weight row read in place by a group of lanes (16-byte
+//                      loads), h kept in registers, a lane-group shuffle
+//                      reduction, z stored at the slot (sparse: rank j; dense:
+//                      the token's legal rank).
 //   k_gemm_nt          full projection Z = H . W_t^T on MFMA (fp32, bf16, f16
 //                      inputs; fp32 accumulate), Z row = beam, column = token;
 //   k_gemm_small       the same product for few beams (first step): 16x16 MFMA.
 //   k_request_step     one block per request: legal-only log-sum-exp of each
 //                      beam, cand = cum + (z - lse) for every legal candidate,
-//                      the best K by an LDS radix select, rank sort, decode
+//                      the best K by an LDS distance histogram, rank sort, decode
 //                      (parent, token, cum) and advance: next row = row_ptr[r]
 //                      + slot (sparse: the position is the next row) or
 //                      row_ptr[r] + rank directory + popcount (dense); prefix
@@ -338,53 +342,87 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
   const int gl = threadIdx.x % G;   // lane within the candidate group
   const int grp = threadIdx.x / G;  // group within the block
   const int lane = threadIdx.x & 63;
-  const int total = unit_start[M];
   const char* Wb = (const char*)W;
-  for (int u = blockIdx.x; u < total; u += gridDim.x) {
-    // beam owning unit u: the last b with unit_start[b] <= u
-    int lo = 0, hi = M;
+  float h[NV * VEC];  // this lane's share of the unit's hidden vector
+  auto load_h = [&](int b) {
+    const char* hb = (const char*)hidden + (int64_t)b * D * ES;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) load16<DT>(hb + (int64_t)(c * G + gl) * 16, &h[c * VEC]);
+  };
+  auto score = [&](float* zb, int token, int slot) {
+    const char* wr = Wb + (int64_t)token * D * ES;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      float w[VEC];
+      load16<DT>(wr + (int64_t)(c * G + gl) * 16, w);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc = fmaf(w[e], h[c * VEC + e], acc);
+    }
+#pragma unroll
+    for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    if (gl == 0) zb[slot] = acc;
+  };
+
+  if (tab.fmt == ZGR_FMT_SPARSE) {
+    // units (a beam's run of up to kSparseTile candidates) in one contiguous
+    // range per block: one search for the first unit's beam, then the beam
+    // advances with the unit index
+    const int total = unit_start[M];
+    const int chunk = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int u0 = (int)blockIdx.x * chunk, u1 = min(total, u0 + chunk);
+    if (u0 >= u1) return;
+    int lo = 0, hi = M;  // the last b with unit_start[b] <= u0
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (unit_start[mid] <= u)
+      if (unit_start[mid] <= u0)
         lo = mid;
       else
         hi = mid;
     }
-    const int b = lo;
-    const int tile = u - unit_start[b];
-    const int r = row_in[b];
-    // this lane's share of h_b, widened to float, kept in registers
-    float h[NV * VEC];
-    const char* hb = (const char*)hidden + (int64_t)b * D * ES;
-#pragma unroll
-    for (int c = 0; c < NV; ++c) load16<DT>(hb + (int64_t)(c * G + gl) * 16, &h[c * VEC]);
-    float* zb = z + (int64_t)b * ldz;
-    auto score = [&](int token, int slot) {
-      const char* wr = Wb + (int64_t)token * D * ES;
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < NV; ++c) {
-        float w[VEC];
-        load16<DT>(wr + (int64_t)(c * G + gl) * 16, w);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc = fmaf(w[e], h[c * VEC + e], acc);
-      }
-#pragma unroll
-      for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-      if (gl == 0) zb[slot] = acc;
-    };
-    if (tab.fmt == ZGR_FMT_SPARSE) {
+    int b = lo, next = unit_start[b + 1];
+    for (int u = u0; u < u1; ++u) {
+      while (next <= u) next = unit_start[++b + 1];
+      const int tile = u - unit_start[b];
+      const int r = row_in[b];
+      load_h(b);
+      float* zb = z + (int64_t)b * ldz;
       const int base = tab.row_ptr[r];
       const int n = tab.row_ptr[r + 1] - base;
       const int j0 = tile * kSparseTile, j1 = min(n, j0 + kSparseTile);
-      for (int j = j0 + grp; j < j1; j += NG) score(tab.tok[base + j], j);
-    } else {
-      // compact this tile's set bits into an LDS token list (a local, per-tile
-      // list; slots stay token-addressed)
-      const int v0 = tile * kDenseTile;
+      for (int j = j0 + grp; j < j1; j += NG) score(zb, tab.tok[base + j], j);
+    }
+    return;
+  }
+
+  // Dense rows: every live beam has the same tiles of kDenseTile tokens, so
+  // (tile, beam) pairs are enumerated directly.  With at least 8 tiles, the
+  // blocks of one XCD (blocks are dealt to the 8 XCDs in turn) take only the
+  // tiles of their own residue, one tile at a time, so the weight rows a
+  // tile gathers stay in that XCD's L2 instead of every XCD streaming all of
+  // W_t.
+  const int tiles = (tab.V + kDenseTile - 1) / kDenseTile;
+  const bool by_xcd = tiles >= 8 && (gridDim.x & 7) == 0;
+  const int stride_b = by_xcd ? (int)gridDim.x / 8 : (int)gridDim.x;
+  const int first_b = by_xcd ? (int)blockIdx.x / 8 : (int)blockIdx.x;
+  const int t_step = by_xcd ? 8 : 1;
+  const int t_first = by_xcd ? (int)blockIdx.x % 8 : 0;
+  for (int tile = t_first; tile < tiles; tile += t_step) {
+    // without the XCD split, pairs run over (tile, beam) in one flat range
+    const int nb = by_xcd ? M : M * tiles;
+    for (int pb = first_b; pb < nb; pb += stride_b) {
+      const int b = by_xcd ? pb : pb % M;
+      const int tl = by_xcd ? tile : pb / M;
+      const int r = row_in[b];
+      if (r < 0 || r >= tab.rows) continue;  // the request kernel reports bad rows
+      load_h(b);
+      float* zb = z + (int64_t)b * ldz;
+      // this tile's set bits as an LDS token list with their legal ranks
+      // (z of a dense row is stored by legal rank)
+      const int v0 = tl * kDenseTile;
       const int w0 = v0 >> 5;
       const int nw = min(kDenseTile / 32, tab.words - w0);
-      __syncthreads();  // previous unit's readers are done with lst
+      __syncthreads();  // previous pair's readers are done with lst
       if (threadIdx.x < 64) {
         const DWord dw = (lane < nw) ? dense_word<NX>(tab, r, w0 + lane) : DWord{0u, 0};
         const uint32_t word = dw.bits;
@@ -397,14 +435,15 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
           const int k = __ffs(x) - 1;
           x &= x - 1;
           lst[pos] = (uint16_t)(v0 + lane * 32 + k);
-          lpos[pos++] = rk++;  // z of a dense row is stored by legal rank
+          lpos[pos++] = rk++;
         }
         if (lane == 63) lst_count = incl;
       }
       __syncthreads();
       const int cnt = lst_count;
-      for (int i = grp; i < cnt; i += NG) score(lst[i], lpos[i]);
+      for (int i = grp; i < cnt; i += NG) score(zb, lst[i], lpos[i]);
     }
+    if (!by_xcd) break;  // the flat range covered every tile
   }
 }
 
