@@ -302,10 +302,13 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     if (e != hipSuccess) return hip_fail(e, "naive score launch");
     zmode = 1;
   } else if (proj == ZGR_PROJ_FULL) {
-    a.ldz = p->V;
+    // dense rows and tiled sparse steps: legal columns only, by legal rank /
+    // slot; the few-beam kernel on a sparse step writes token-indexed rows
+    const bool slot = dense || full_projection_slot_layout(a);
+    a.ldz = (slot && !dense) ? a.tab.stride : p->V;
     e = prof_launch(p, ZGR_KERNEL_GEMM, t, s, [&] { return launch_full_projection(a, s); });
     if (e != hipSuccess) return hip_fail(e, "full projection launch");
-    zmode = dense ? 1 : 0;
+    zmode = slot ? 1 : 0;
   } else if (!dense && light_sparse_step(p, a)) {
     a.ldz = a.tab.stride;
     zmode = 2;

@@ -106,6 +106,9 @@ struct StepArgs {
 hipError_t launch_units(const StepArgs& a, hipStream_t s);
 hipError_t launch_selective_score(const StepArgs& a, hipStream_t s);
 hipError_t launch_full_projection(const StepArgs& a, hipStream_t s);
+// true when the full projection of this step writes sparse rows by slot
+// (legal columns only, ldz = stride) rather than token-indexed rows (ldz = V)
+bool full_projection_slot_layout(const StepArgs& a);
 // zmode: 0 = z token-indexed, 1 = z slot-indexed, 2 = score inside the request kernel.
 // With a.parts > 1 each request is split over a.parts blocks, then merged.
 constexpr int kMaxParts = 32;

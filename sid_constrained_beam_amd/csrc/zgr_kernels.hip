@@ -1267,7 +1267,12 @@ constexpr int kLdsRow = kTileKBytes + 16;  // padded row pitch in bytes
 // dead beams are skipped.  The tile's rows, bitmap words and rank entries are
 // loaded into LDS before the k loop so the epilogue does not wait on them.
 // compact == 0: full rows, column = token.
-template <int DT, int BM, int BN, bool NX>
+// SP: sparse table (compact == 2): the tile is staged in LDS after the k
+// loop and only the rows' legal columns are written, at their slot (the
+// token's position in the row), so the scores of a sparse step take the
+// same layout as under the selective projection; each row's first token in
+// the tile's column range is found before the product.
+template <int DT, int BM, int BN, bool NX, bool SP>
 __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A,
                                                       const void* __restrict__ Bm,
                                                       float* __restrict__ C, int32_t M, int32_t N,
@@ -1279,8 +1284,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   constexpr int WM = BM / 2, WN = BN / 2, IB = WM / 32, JB = WN / 32;
   constexpr int NA = BM * 8 / kThreads, NB = BN * 8 / kThreads;  // 16-byte chunks per thread
   constexpr int TW = BN / 32;                                     // bitmap words per tile row
-  __shared__ __attribute__((aligned(16))) char As[BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) char Bs[BN * kLdsRow];
+  constexpr int STAGE = (BM + BN) * kLdsRow;
+  constexpr int CTILE = SP ? BM * (BN + 1) * 4 : 0;  // staged output tile (sparse epilogue)
+  __shared__ __attribute__((aligned(16))) char smem[STAGE > CTILE ? STAGE : CTILE];
+  char* As = smem;
+  char* Bs = smem + BM * kLdsRow;
   __shared__ uint32_t tbits[BM * TW];
   __shared__ int trank[BM * TW];
   const int nbm = (M + BM - 1) / BM;
@@ -1298,7 +1306,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   DWord pdw[TW];
 #pragma unroll
   for (int k = 0; k < TW; ++k) pdw[k] = DWord{0u, 0};
-  if (compact && (int)threadIdx.x < BM) {
+  int sp_base = 0, sp_n = 0, sp_lo = 0;  // sparse: the row's entries, first one in the tile
+  if (compact == 1 && (int)threadIdx.x < BM) {
     const int gm = m0 + threadIdx.x;
     const int r = gm < M ? row_in[gm] : -1;
     if (r >= 0 && r < tab.rows) {
@@ -1306,6 +1315,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
       for (int k = 0; k < TW; ++k) {
         const int wd = (n0 >> 5) + k;
         if (wd < tab.words) pdw[k] = dense_word<NX>(tab, r, wd);
+      }
+    }
+  }
+  if constexpr (SP) {
+    if ((int)threadIdx.x < BM) {
+      const int gm = m0 + threadIdx.x;
+      const int r = gm < M ? row_in[gm] : -1;
+      if (r >= 0 && r < tab.rows) {
+        sp_base = tab.row_ptr[r];
+        sp_n = tab.row_ptr[r + 1] - sp_base;
+        int lo = 0, hi = sp_n;  // first entry with token >= n0
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)tab.tok[sp_base + mid] < n0)
+            lo = mid + 1;
+          else
+            hi = mid;
+        }
+        sp_lo = lo;
       }
     }
   }
@@ -1398,6 +1426,43 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
     }
   }
   // 32x32 accumulator layout: lane -> column l32, register v -> row 8*(v/4) + 4*half + v%4
+  if constexpr (SP) {
+    float* Ct = (float*)smem;
+    __syncthreads();  // every wave is done reading the staged operands
+#pragma unroll
+    for (int i = 0; i < IB; ++i)
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int col = wn * WN + j * 32 + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          Ct[rl * (BN + 1) + col] = acc[i][j][v];
+        }
+      }
+    __syncthreads();
+    if ((int)threadIdx.x < BM && sp_lo < sp_n) {
+      float* zrow = C + (int64_t)(m0 + threadIdx.x) * ldc;
+      const float* crow = Ct + threadIdx.x * (BN + 1);
+      for (int j0 = sp_lo; j0 < sp_n; j0 += 8) {
+        int tk[8];  // eight token loads in flight (clamped, unconditional)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tk[u] = tab.tok[sp_base + min(j0 + u, sp_n - 1)];
+        bool done = false;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int jj = j0 + u;
+          if (jj >= sp_n || tk[u] >= n0 + BN) {
+            done = true;
+          } else if (!done) {
+            zrow[jj] = crow[tk[u] - n0];
+          }
+        }
+        if (done) break;
+      }
+    }
+    return;
+  }
   if (!compact) {
 #pragma unroll
     for (int i = 0; i < IB; ++i)
@@ -1674,23 +1739,40 @@ hipError_t launch_sel_d(const StepArgs& a, hipStream_t s) {
 template <int DT, bool NX>
 hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
   const int V = a.tab.V;
-  const int compact = ((a.tab.fmt == ZGR_FMT_DENSE || a.tab.fmt == ZGR_FMT_DENSE_NEXT) && !a.plain_z) ? 1 : 0;
+  const bool dense = a.tab.fmt == ZGR_FMT_DENSE || a.tab.fmt == ZGR_FMT_DENSE_NEXT;
+  const int compact = a.plain_z ? 0 : (dense ? 1 : (full_projection_slot_layout(a) ? 2 : 0));
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((V + bn - 1) / bn); };
+#define ZGR_GEMM(BM_, BN_, SP_)                                                                    \
+  hipLaunchKernelGGL((k_gemm_nt<DT, BM_, BN_, NX, SP_>), dim3(tiles(BM_, BN_)), dim3(kThreads), 0, s, \
+                     a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in)
   // the largest tile that still gives every compute unit two blocks (or one)
   if (tiles(128, 128) >= 2 * a.n_cu) {
-    hipLaunchKernelGGL((k_gemm_nt<DT, 128, 128, NX>), dim3(tiles(128, 128)), dim3(kThreads), 0, s, a.hidden,
-                       a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
+    if (compact == 2)
+      ZGR_GEMM(128, 128, true);
+    else
+      ZGR_GEMM(128, 128, false);
   } else if (tiles(64, 64) >= a.n_cu) {
-    hipLaunchKernelGGL((k_gemm_nt<DT, 64, 64, NX>), dim3(tiles(64, 64)), dim3(kThreads), 0, s, a.hidden,
-                       a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
+    if (compact == 2)
+      ZGR_GEMM(64, 64, true);
+    else
+      ZGR_GEMM(64, 64, false);
   } else {
     hipLaunchKernelGGL((k_gemm_small<DT, NX>), dim3(tiles(32, 32)), dim3(kSmallThreads), 0, s, a.hidden, a.W, a.z,
                        a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   }
+#undef ZGR_GEMM
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool full_projection_slot_layout(const StepArgs& a) {
+  // sparse step, filter-first, and enough beams for the tiled kernels (the
+  // few-beam kernel writes token-indexed rows)
+  const bool sparse = a.tab.fmt == ZGR_FMT_SPARSE;
+  const int64_t t64 = (int64_t)((a.M + 63) / 64) * ((a.tab.V + 63) / 64);
+  return sparse && !a.plain_z && t64 >= a.n_cu;
+}
 
 bool supported_hidden_size(int d) {
   return d == 64 || d == 128 || d == 256 || d == 512 || d == 768 || d == 1024 || d == 2048 ||
