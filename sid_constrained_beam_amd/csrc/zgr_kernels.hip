@@ -396,13 +396,15 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
   }
 
   // Dense rows: every live beam has the same tiles of kDenseTile tokens, so
-  // (tile, beam) pairs are enumerated directly.  With at least 8 tiles, the
-  // blocks of one XCD (blocks are dealt to the 8 XCDs in turn) take only the
-  // tiles of their own residue, one tile at a time, so the weight rows a
-  // tile gathers stay in that XCD's L2 instead of every XCD streaming all of
-  // W_t.
+  // (tile, beam) pairs are enumerated directly.  With at least 8 tiles and
+  // enough beams to keep every block busy, the blocks of one XCD (blocks are
+  // dealt to the 8 XCDs in turn) take only the tiles of their own residue,
+  // one tile at a time, so the weight rows a tile gathers stay in that XCD's
+  // L2 instead of every XCD streaming all of W_t.  Otherwise one flat range
+  // with a beam's tiles side by side (neighbouring blocks share its bitmap
+  // row and hidden vector).
   const int tiles = (tab.V + kDenseTile - 1) / kDenseTile;
-  const bool by_xcd = tiles >= 8 && (gridDim.x & 7) == 0;
+  const bool by_xcd = tiles >= 8 && (gridDim.x & 7) == 0 && M >= (int)gridDim.x / 8;
   const int stride_b = by_xcd ? (int)gridDim.x / 8 : (int)gridDim.x;
   const int first_b = by_xcd ? (int)blockIdx.x / 8 : (int)blockIdx.x;
   const int t_step = by_xcd ? 8 : 1;
@@ -411,8 +413,8 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
     // without the XCD split, pairs run over (tile, beam) in one flat range
     const int nb = by_xcd ? M : M * tiles;
     for (int pb = first_b; pb < nb; pb += stride_b) {
-      const int b = by_xcd ? pb : pb % M;
-      const int tl = by_xcd ? tile : pb / M;
+      const int b = by_xcd ? pb : pb / tiles;  // flat range: a beam's tiles side by side
+      const int tl = by_xcd ? tile : pb % tiles;
       const int r = row_in[b];
       if (r < 0 || r >= tab.rows) continue;  // the request kernel reports bad rows
       load_h(b);
