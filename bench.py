@@ -352,10 +352,11 @@ def modes_bench(args):
     res, finals = {}, {}
     for mode in ("filter_first", "score_first", "unconstrained"):
         w.set_mode(mode)
-        sec, eager_sec, launch = time_decode(w, args, stream)
+        sec, times, launch = time_decode(w, args, stream)
         cand = sum(int(st["n"].sum()) for st in w.steps)
-        res[mode] = {"ms": round(sec * 1e3, 4), "eager_ms": round(eager_sec * 1e3, 4),
-                     "launch": launch, "candidates_per_decode": cand}
+        res[mode] = {"ms": round(sec * 1e3, 4), "launch": launch,
+                     "ms_by_launch": {k: round(v * 1e3, 4) for k, v in times.items()},
+                     "candidates_per_decode": cand}
         finals[mode] = (w.final_sids.copy(), w.final_live.copy())
         log(f"[modes] {cfg.name} {mode}: {sec * 1e6:.1f} us per decode ({launch}), {cand} candidates")
     members = set(map(tuple, w.sids.tolist()))
@@ -407,7 +408,7 @@ def projections_bench(args):
     stream = torch.cuda.Stream()
     res = {}
     with torch.cuda.stream(stream):
-        for proj in ("full", "selective", "naive"):
+        for proj in args.proj_kinds.split(","):
             for t in range(1, cfg.L + 1):
                 zgr.zgr_plan_set_choice(w.plan, t, proj)
             per_step = []
@@ -430,11 +431,10 @@ def projections_bench(args):
             log(f"[proj] {cfg.name} B={cfg.B} {proj}: " + ", ".join(f"t{i + 1} {x:.1f}us"
                                                                    for i, x in enumerate(per_step)))
     cand = [int(st["n"].sum()) for st in w.steps]
-    ratios = {
-        "naive_over_full": [round(n / f, 3) for n, f in zip(res["naive"], res["full"])],
-        "naive_over_selective": [round(n / s_, 3) for n, s_ in zip(res["naive"], res["selective"])],
-        "full_over_selective": [round(f / s_, 3) for f, s_ in zip(res["full"], res["selective"])],
-    }
+    ratios = {}
+    for a_, b_ in (("naive", "full"), ("naive", "selective"), ("full", "selective")):
+        if a_ in res and b_ in res:
+            ratios[f"{a_}_over_{b_}"] = [round(x / y, 3) for x, y in zip(res[a_], res[b_])]
     print(json.dumps({
         "metric": "per-step latency by projection (us): full, padded-slot selective, naive compaction",
         "value": res["selective"], "unit": "us", "higher_is_better": False, "n_gpus": 1,
@@ -516,7 +516,7 @@ def encodings_bench(args):
             w.index.free()
             workload.CONFIGS[args.workload] = base.scaled(fmt=["N" if f == "D" else f for f in fmts])
             w = Workload(args.workload, 0, choice)
-        sec, eager_sec, launch = time_decode(w, args, stream)
+        sec, _, launch = time_decode(w, args, stream)
         with torch.cuda.stream(stream):
             zgr.zgr_plan_profile(w.plan, 20)
             for _ in range(3):
@@ -567,6 +567,8 @@ def main():
     ap.add_argument("--projections", action="store_true",
                     help="time full / selective / naive-compaction scoring per step instead")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
+    ap.add_argument("--proj-kinds", default="full,selective,naive",
+                    help="with --projections: comma list of the projections to time")
     ap.add_argument("--index-bytes", default=None, metavar="WORKLOADS",
                     help="comma list: report index bytes per encoding (host only) instead")
     ap.add_argument("--encodings", action="store_true",
@@ -604,15 +606,17 @@ def main():
 
     # ---- timed region: whole decodes (L steps) over recorded HBM-resident inputs
     stream = torch.cuda.Stream()
-    sec, eager_sec, mode = time_decode(w, args, stream)
-    ms = sec * 1e3
-    log(f"[bench] {mode}: {ms * 1e3:.1f} us per decode (eager {eager_sec * 1e6:.1f} us)")
-    per_kernel_and_line(w, args, stream, sec, eager_sec, mode)
+    sec, times, mode = time_decode(w, args, stream)
+    log("[bench] " + ", ".join(f"{k}: {v * 1e6:.1f} us per decode" for k, v in times.items())
+        + f" (value: {mode})")
+    per_kernel_and_line(w, args, stream, sec, times, mode)
 
 
 def time_decode(w, args, stream):
-    """Seconds per decode: a graph replay of the recorded L steps (checked
-    against eager launches first), and the eager launches themselves."""
+    """Seconds per decode, timed two ways: a graph replay of the recorded L
+    steps (checked against eager launches first) and the eager launches
+    themselves, back to back on one stream.  Returns the faster time, both
+    times by launch style, and the style of the faster one."""
     import torch
     mode = "eager"
     with torch.cuda.stream(stream):
@@ -640,14 +644,14 @@ def time_decode(w, args, stream):
             except Exception as e:  # noqa: BLE001 - fall back to eager timing, and say so
                 log(f"[bench] graph capture unavailable ({e}); timing eager launches")
                 mode = "eager"
-        fn = graph.replay if mode == "graph" else (lambda: w.run_decode(stream))
-        sec = timed(fn, args.steps, args.warmup)
-        eager_sec = sec if mode == "eager" else timed(lambda: w.run_decode(stream), args.steps,
-                                                      args.warmup)
-    return sec, eager_sec, mode
+        times = {"eager": timed(lambda: w.run_decode(stream), args.steps, args.warmup)}
+        if mode == "graph":
+            times["graph"] = timed(graph.replay, args.steps, args.warmup)
+    best = min(times, key=times.get)
+    return times[best], times, best
 
 
-def per_kernel_and_line(w, args, stream, sec, eager_sec, mode):
+def per_kernel_and_line(w, args, stream, sec, times, mode):
     import torch
 
     import sid_constrained_beam_amd as zgr
@@ -724,7 +728,7 @@ def per_kernel_and_line(w, args, stream, sec, eager_sec, mode):
                    "projection": ["full" if c[0] == 1 else "selective" for c in w.choices]},
         "candidates_per_s": round(cand_per_decode / sec, 1),
         "candidates_per_decode": cand_per_decode,
-        "eager_ms": round(eager_sec * 1e3, 4),
+        "ms_by_launch": {k: round(v * 1e3, 4) for k, v in times.items()},
         "hbm_gbs_algorithmic": round(hbm_bytes / sec / 1e9, 1),
         "roofline": roofline,
     }

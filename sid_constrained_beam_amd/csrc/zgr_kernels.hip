@@ -54,6 +54,9 @@ namespace zgr {
 namespace {
 
 constexpr int kThreads = 256;
+// Selective scoring: candidates a lane group scores at once when a row takes
+// at most 6 loads per lane (a power of two)
+constexpr int kSelU = 2;
 constexpr int kWaves = kThreads / 64;
 
 // ---------------------------------------------------------------- element helpers
@@ -325,15 +328,39 @@ struct SelShape {
   // lanes per candidate: a power of two (shuffle groups), at most one wave
   static constexpr int G = RAW < 1 ? 1 : (RAW > 64 ? 64 : pow2_floor(RAW));
   static constexpr int NV = D * ES / (16 * G);         // 16-byte loads per lane per row
-  static constexpr int NG = kThreads / G;              // candidates in flight per block
+  static constexpr int NG = kThreads / G;              // lane groups per block
+  // candidates a lane group scores at once (their row loads in flight together)
+  static constexpr int U = NV <= 6 ? (kSelU < G ? kSelU : G) : 1;
   static_assert(D * ES % (16 * G) == 0, "hidden size must split into 16-byte lane chunks");
 };
+
+// Sums of U candidates' partial dot products over a group of G lanes (U a
+// power of two, U <= G): U - 1 shuffles halve the vector (each lane keeps
+// the half that its partner does not), then a butterfly over the remaining
+// G / U lanes.  Lane gl ends with the sum of candidate gl / (G / U).
+template <int G, int U>
+__device__ __forceinline__ float group_sum_multi(float (&acc)[U], int gl) {
+#pragma unroll
+  for (int n = U, o = G / 2; n > 1; n >>= 1, o >>= 1) {
+    const bool hi = (gl & o) != 0;
+#pragma unroll
+    for (int i = 0; i < n / 2; ++i) {
+      const float send = hi ? acc[i] : acc[i + n / 2];
+      const float keep = hi ? acc[i + n / 2] : acc[i];
+      acc[i] = keep + __shfl_xor(send, o);
+    }
+  }
+  float v = acc[0];
+#pragma unroll
+  for (int o = G / (2 * U); o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
 
 template <int DT, int D, bool NX>
 __global__ __launch_bounds__(kThreads) void k_score_selective(
     const int32_t* __restrict__ unit_start, int32_t M, DevTable tab,
     const int32_t* __restrict__ row_in, const void* __restrict__ hidden,
-    const void* __restrict__ W, float* __restrict__ z, int64_t ldz) {
+    const void* __restrict__ W, float* __restrict__ z, int64_t ldz, int32_t tt) {
   using S = SelShape<DT, D>;
   constexpr int G = S::G, NV = S::NV, VEC = S::VEC, NG = S::NG, ES = S::ES;
   __shared__ uint16_t lst[kDenseTile];
@@ -349,19 +376,30 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
 #pragma unroll
     for (int c = 0; c < NV; ++c) load16<DT>(hb + (int64_t)(c * G + gl) * 16, &h[c * VEC]);
   };
-  auto score = [&](float* zb, int token, int slot) {
-    const char* wr = Wb + (int64_t)token * D * ES;
-    float acc = 0.f;
+  // U candidates of one beam per lane group: tok(u) gives candidate u's token
+  // (callers clamp it to a real candidate, so every load is in bounds), and
+  // slot(u) its z index; only the first nvalid are stored
+  constexpr int U = S::U;
+  auto score_u = [&](float* zb, auto&& tok, auto&& slot, int nvalid) {
+    const char* wr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) wr[u] = Wb + (int64_t)tok(u) * D * ES;
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = 0.f;
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      float w[VEC];
-      load16<DT>(wr + (int64_t)(c * G + gl) * 16, w);
+      float w[U][VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc = fmaf(w[e], h[c * VEC + e], acc);
+      for (int u = 0; u < U; ++u) load16<DT>(wr[u] + (int64_t)(c * G + gl) * 16, w[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[u] = fmaf(w[u][e], h[c * VEC + e], acc[u]);
     }
-#pragma unroll
-    for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-    if (gl == 0) zb[slot] = acc;
+    const float v = group_sum_multi<G, U>(acc, gl);
+    const int mine = gl / (G / U);
+    if (gl % (G / U) == 0 && mine < nvalid) zb[slot(mine)] = v;
   };
 
   if (tab.fmt == ZGR_FMT_SPARSE) {
@@ -390,20 +428,26 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       const int base = tab.row_ptr[r];
       const int n = tab.row_ptr[r + 1] - base;
       const int j0 = tile * kSparseTile, j1 = min(n, j0 + kSparseTile);
-      for (int j = j0 + grp; j < j1; j += NG) score(zb, tab.tok[base + j], j);
+      for (int j = j0 + grp; j < j1; j += NG * U) {
+        const int nv = min(U, (j1 - j + NG - 1) / NG);
+        score_u(
+            zb, [&](int u) { return (int)tab.tok[base + min(j + u * NG, j1 - 1)]; },
+            [&](int u) { return j + u * NG; }, nv);
+      }
     }
     return;
   }
 
-  // Dense rows: every live beam has the same tiles of kDenseTile tokens, so
-  // (tile, beam) pairs are enumerated directly.  With at least 8 tiles and
-  // enough beams to keep every block busy, the blocks of one XCD (blocks are
-  // dealt to the 8 XCDs in turn) take only the tiles of their own residue,
-  // one tile at a time, so the weight rows a tile gathers stay in that XCD's
-  // L2 instead of every XCD streaming all of W_t.  Otherwise one flat range
-  // with a beam's tiles side by side (neighbouring blocks share its bitmap
-  // row and hidden vector).
-  const int tiles = (tab.V + kDenseTile - 1) / kDenseTile;
+  // Dense rows: every live beam has the same tiles of tt tokens (a multiple
+  // of 32, at most kDenseTile; the host sizes a tile's weight rows to a
+  // fraction of one XCD's L2), so (tile, beam) pairs are enumerated
+  // directly.  With at least 8 tiles and enough beams to keep every block
+  // busy, the blocks of one XCD (blocks are dealt to the 8 XCDs in turn) take
+  // only the tiles of their own residue, one tile at a time, so the weight
+  // rows a tile gathers stay in that XCD's L2 instead of every XCD streaming
+  // all of W_t.  Otherwise one flat range with a beam's tiles side by side
+  // (neighbouring blocks share its bitmap row and hidden vector).
+  const int tiles = (tab.V + tt - 1) / tt;
   const bool by_xcd = tiles >= 8 && (gridDim.x & 7) == 0 && M >= (int)gridDim.x / 8;
   const int stride_b = by_xcd ? (int)gridDim.x / 8 : (int)gridDim.x;
   const int first_b = by_xcd ? (int)blockIdx.x / 8 : (int)blockIdx.x;
@@ -421,9 +465,9 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       float* zb = z + (int64_t)b * ldz;
       // this tile's set bits as an LDS token list with their legal ranks
       // (z of a dense row is stored by legal rank)
-      const int v0 = tl * kDenseTile;
+      const int v0 = tl * tt;
       const int w0 = v0 >> 5;
-      const int nw = min(kDenseTile / 32, tab.words - w0);
+      const int nw = min(tt >> 5, tab.words - w0);
       __syncthreads();  // previous pair's readers are done with lst
       if (threadIdx.x < 64) {
         const DWord dw = (lane < nw) ? dense_word<NX>(tab, r, w0 + lane) : DWord{0u, 0};
@@ -443,7 +487,12 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       }
       __syncthreads();
       const int cnt = lst_count;
-      for (int i = grp; i < cnt; i += NG) score(zb, lst[i], lpos[i]);
+      for (int i = grp; i < cnt; i += NG * U) {
+        const int nv = min(U, (cnt - i + NG - 1) / NG);
+        score_u(
+            zb, [&](int u) { return (int)lst[min(i + u * NG, cnt - 1)]; },
+            [&](int u) { return lpos[i + u * NG]; }, nv);
+      }
     }
     if (!by_xcd) break;  // the flat range covered every tile
   }
@@ -1711,15 +1760,45 @@ __global__ __launch_bounds__(256) void k_row_lse(const float* __restrict__ z, in
   if (lane == 0) lse[b] = m + __logf(sum);
 }
 
+// Tokens per dense selective tile: the tile's weight rows take at most
+// kSelTileBytes (one XCD's L2).  Smaller tiles keep the rows in L2 but add
+// (tile, beam) pairs, each with its own barrier, bitmap decode and hidden
+// vector load; at d = 1024 fp32 a quarter-L2 tile measured 17% slower and a
+// sixteenth 2.3x slower.
+constexpr int64_t kSelTileBytes = 1 << 22;
+
+int32_t dense_tile_tokens(int32_t d, int32_t dtype) {
+  const int64_t row = (int64_t)d * (dtype == ZGR_F32 ? 4 : 2);
+  int tt = kDenseTile;
+  while (tt > 64 && tt * row > kSelTileBytes) tt >>= 1;
+  return tt;
+}
+
+// Resident blocks per CU of a kernel (registers and LDS decide), so that a
+// persistent grid is exactly one wave of blocks: a block that has to wait for
+// another to finish would start its equal share of the work only then.
+template <typename Kernel>
+int resident_blocks_per_cu(Kernel kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    n = 1;
+  }
+  return n;
+}
+
 template <int DT, int D>
 hipError_t launch_sel_typed(const StepArgs& a, hipStream_t s) {
-  const int grid = a.n_cu * 8;
-  if (a.tab.next)
-    hipLaunchKernelGGL((k_score_selective<DT, D, true>), dim3(grid), dim3(kThreads), 0, s, a.unit_start,
-                       a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
-  else
-    hipLaunchKernelGGL((k_score_selective<DT, D, false>), dim3(grid), dim3(kThreads), 0, s, a.unit_start,
-                       a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
+  const int32_t tt = dense_tile_tokens(D, DT);
+  if (a.tab.next) {
+    static const int per_cu = resident_blocks_per_cu(k_score_selective<DT, D, true>, kThreads);
+    hipLaunchKernelGGL((k_score_selective<DT, D, true>), dim3(a.n_cu * per_cu), dim3(kThreads), 0, s,
+                       a.unit_start, a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz, tt);
+  } else {
+    static const int per_cu = resident_blocks_per_cu(k_score_selective<DT, D, false>, kThreads);
+    hipLaunchKernelGGL((k_score_selective<DT, D, false>), dim3(a.n_cu * per_cu), dim3(kThreads), 0, s,
+                       a.unit_start, a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz, tt);
+  }
   return hipGetLastError();
 }
 
