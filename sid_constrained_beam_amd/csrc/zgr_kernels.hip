@@ -276,38 +276,53 @@ constexpr int kUnitsCache = 16384;
 // Per beam: legal count n_b and its work units (sparse: ceil(n_b / 64)
 // candidates; dense: ceil(V / 1024) token tiles), then the exclusive scan of
 // units over the M beams into unit_start[0..M] (unit_start[M] = total).
+// The counts are read coalesced with kUnitsInFlight beams' row lookups in
+// flight per thread; the scan then runs over contiguous chunks per thread.
+constexpr int kUnitsInFlight = 8;
 __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_in, int32_t M,
                                                 DevTable tab, int32_t* __restrict__ nlegal,
                                                 int32_t* __restrict__ unit_start,
                                                 int32_t* __restrict__ err) {
   __shared__ int ucache[kUnitsCache];
   __shared__ int sh[16];
-  const int per = (M + 1023) / 1024;
-  const int b0 = threadIdx.x * per, b1 = min(M, b0 + per);
+  constexpr int R = kUnitsInFlight;
   const int dense_units = (tab.V + kDenseTile - 1) / kDenseTile;
-  auto units_of = [&](int b, bool record) -> int {
-    const int r = row_in[b];
-    int n = 0;
-    if (r >= 0 && r < tab.rows) {
-      n = tab.row_ptr[r + 1] - tab.row_ptr[r];
-    } else if (r >= tab.rows && record) {
-      atomicOr(err, 1);
-    }
-    if (record) nlegal[b] = n;
+  auto units_of_n = [&](int n) {
     if (n == 0) return 0;
     return is_dense(tab.fmt) ? dense_units : (n + kSparseTile - 1) / kSparseTile;
   };
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int u = units_of(b, true);
-    if (b < kUnitsCache) ucache[b] = u;
-    mine += u;
+  for (int c = threadIdx.x; c < M; c += 1024 * R) {
+    int r[R], lo[R], hi[R];
+#pragma unroll
+    for (int u = 0; u < R; ++u) r[u] = row_in[min(c + u * 1024, M - 1)];
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int rr = (r[u] >= 0 && r[u] < tab.rows) ? r[u] : 0;
+      lo[u] = tab.row_ptr[rr];
+      hi[u] = tab.row_ptr[rr + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int b = c + u * 1024;
+      if (b < M) {
+        if (r[u] >= tab.rows) atomicOr(err, 1);
+        const int n = (r[u] >= 0 && r[u] < tab.rows) ? hi[u] - lo[u] : 0;
+        nlegal[b] = n;
+        if (b < kUnitsCache) ucache[b] = units_of_n(n);
+      }
+    }
   }
+  __syncthreads();  // beams past the LDS cache are read back from nlegal
+  auto units_at = [&](int b) { return b < kUnitsCache ? ucache[b] : units_of_n(nlegal[b]); };
+  const int per = (M + 1023) / 1024;
+  const int b0 = min(M, (int)threadIdx.x * per), b1 = min(M, b0 + per);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += units_at(b);
   int total;
   int run = block_excl_scan<1024>(mine, sh, &total);
   for (int b = b0; b < b1; ++b) {
     unit_start[b] = run;
-    run += (b < kUnitsCache) ? ucache[b] : units_of(b, false);
+    run += units_at(b);
   }
   if (threadIdx.x == 0) unit_start[M] = total;
 }
@@ -1323,6 +1338,41 @@ constexpr int kLdsRow = kTileKBytes + 16;  // padded row pitch in bytes
 // token's position in the row), so the scores of a sparse step take the
 // same layout as under the selective projection; each row's first token in
 // the tile's column range is found before the product.
+// Tile order of the tiled GEMM.  Blocks are dealt to the 8 XCDs in turn;
+// with at least 8 row blocks, XCD x takes the row blocks tm = x (mod 8) and
+// walks them in groups of up to 16, every column tile of a group with the
+// group's row blocks side by side, so the blocks an XCD runs at once share
+// their hidden rows and weight rows in its L2 (consecutive blocks on
+// different XCDs would each stream the same hidden rows).  Blocks padding the
+// last group of an XCD have no tile (tm = -1).
+struct GemmOrder {
+  int nbm, nbn, gm, nlr_pad;
+  __host__ __device__ GemmOrder(int M, int N, int BM, int BN) {
+    nbm = (M + BM - 1) / BM;
+    nbn = (N + BN - 1) / BN;
+    const int nlr = (nbm + 7) / 8;
+    gm = nlr < 16 ? nlr : 16;
+    nlr_pad = (nlr + gm - 1) / gm * gm;
+  }
+  __host__ __device__ bool by_xcd() const { return nbm >= 8; }
+  __host__ __device__ int64_t blocks() const {
+    return by_xcd() ? (int64_t)8 * nlr_pad * nbn : (int64_t)nbm * nbn;
+  }
+  __device__ void tile(int bid, int& tm, int& tn) const {
+    if (!by_xcd()) {
+      tm = bid % nbm;
+      tn = bid / nbm;
+      return;
+    }
+    const int x = bid & 7, j = bid >> 3;
+    const int tmi = j % gm, rest = j / gm;
+    tn = rest % nbn;
+    const int lr = (rest / nbn) * gm + tmi;
+    tm = lr * 8 + x;
+    if (tm >= nbm) tm = -1;
+  }
+};
+
 template <int DT, int BM, int BN, bool NX, bool SP>
 __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A,
                                                       const void* __restrict__ Bm,
@@ -1342,8 +1392,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   char* Bs = smem + BM * kLdsRow;
   __shared__ uint32_t tbits[BM * TW];
   __shared__ int trank[BM * TW];
-  const int nbm = (M + BM - 1) / BM;
-  const int tm = blockIdx.x % nbm, tn = blockIdx.x / nbm;
+  int tm, tn;
+  GemmOrder(M, N, BM, BN).tile((int)blockIdx.x, tm, tn);
+  if (tm < 0) return;  // padding block (before any barrier)
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -1824,7 +1875,8 @@ hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
   const int compact = a.plain_z ? 0 : (dense ? 1 : (full_projection_slot_layout(a) ? 2 : 0));
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((V + bn - 1) / bn); };
 #define ZGR_GEMM(BM_, BN_, SP_)                                                                    \
-  hipLaunchKernelGGL((k_gemm_nt<DT, BM_, BN_, NX, SP_>), dim3(tiles(BM_, BN_)), dim3(kThreads), 0, s, \
+  hipLaunchKernelGGL((k_gemm_nt<DT, BM_, BN_, NX, SP_>), dim3(GemmOrder(a.M, V, BM_, BN_).blocks()), \
+                     dim3(kThreads), 0, s,                                                          \
                      a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in)
   // the largest tile that still gives every compute unit two blocks (or one)
   if (tiles(128, 128) >= 2 * a.n_cu) {
