@@ -1064,9 +1064,15 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     }
     __syncthreads();
   }
-  // without room in LDS, keys are recomputed from z in every pass
+  // without room in LDS, keys are recomputed from z in every pass; on dense
+  // rows LPE threads share a bitmap word (each walks 32 / LPE of its bits)
+  // while that leaves no thread idle
+  int LPE = 1;
+  if (dense)
+    while (LPE < 32 && T * LPE * 2 <= NT) LPE *= 2;
   auto enumerate = [&](auto&& fn) {
-    for (int f = threadIdx.x; f < T; f += NT) {
+    for (int f2 = threadIdx.x; f2 < T * LPE; f2 += NT) {
+      const int f = f2 / LPE, sub = f2 - f * LPE;
       const int bl = beam_of(pre, f), i = f - pre[bl];
       const int b = b0 + bl;
       const int r = brow[bl];
@@ -1078,10 +1084,11 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         fn(make_key(c + (zv - l), code0 + (uint32_t)i));
       } else {
         const DWord dw = dense_word<NX>(tab, r, i);
-        uint32_t y = dw.bits;
-        int j = dw.rank;
+        const int nb = 32 / LPE, lo = sub * nb;  // this thread's bits [lo, lo + nb)
+        uint32_t y = (dw.bits >> lo) & (nb == 32 ? 0xFFFFFFFFu : ((1u << nb) - 1u));
+        int j = dw.rank + __popc(dw.bits & ((1u << lo) - 1u));
         while (y) {
-          const int v = (i << 5) + __ffs(y) - 1;
+          const int v = (i << 5) + lo + __ffs(y) - 1;
           y &= y - 1;
           const float zv = TOKEN_IDX ? zb[v] : zb[j];
           ++j;
