@@ -519,15 +519,16 @@ def encodings_bench(args):
         sec, _, launch = time_decode(w, args, stream)
         with torch.cuda.stream(stream):
             zgr.zgr_plan_profile(w.plan, 20)
-            for _ in range(3):
+            n_dec = 3
+            for _ in range(n_dec):
                 w.run_decode(stream)
             torch.cuda.synchronize()
-        kern = {}
+        kern = {}  # microseconds per step (all launches of the kernel in that step)
         for kname in zgr.KERNELS:
             for st in w.steps:
                 n, kms = zgr.zgr_plan_profile_read(w.plan, kname, st["t"])
                 if n:
-                    kern[f"t{st['t']}_{kname}_us"] = round(kms / n * 1e3, 2)
+                    kern[f"t{st['t']}_{kname}_us"] = round(kms / n_dec * 1e3, 2)
         zgr.zgr_plan_profile(w.plan, 0)
         res[enc] = {"ms": round(sec * 1e3, 4), "launch": launch,
                     "index_bytes": int(sum(st["bytes"] for st in w.stats)),
@@ -662,7 +663,8 @@ def per_kernel_and_line(w, args, stream, sec, times, mode):
         # every launch repeated 20 times between its two events (the step
         # kernels are idempotent), so the events' own cost is amortised
         zgr.zgr_plan_profile(w.plan, 20)
-        for _ in range(max(1, args.steps // 10)):
+        n_dec = max(1, args.steps // 10)
+        for _ in range(n_dec):
             w.run_decode(stream)
         torch.cuda.synchronize()
     per = {}
@@ -673,14 +675,17 @@ def per_kernel_and_line(w, args, stream, sec, times, mode):
             n, kms = zgr.zgr_plan_profile_read(w.plan, kname, st["t"])
             if n == 0:
                 continue
+            # u is the step's work; a step may take several launches of one
+            # kernel (a request split over blocks, then its merge)
             b, u = w.work(kname, st)
             bound = b
             tot_ms += kms
             launches += n
-            units += u * n
-            log(f"[bench]   t{st['t']} {kname:15s} {kms / n * 1e3:8.2f} us/launch  "
-                f"{'GB/s' if b == 'hbm' else 'TFLOP/s'} "
-                f"{(u / (kms / n * 1e-3)) / (1e9 if b == 'hbm' else 1e12):9.1f}  "
+            units += u * n_dec
+            step_s = kms / n_dec * 1e-3
+            log(f"[bench]   t{st['t']} {kname:15s} {step_s * 1e6:8.2f} us/step ({n // n_dec} launch"
+                f"{'es' if n > n_dec else ''})  {'GB/s' if b == 'hbm' else 'TFLOP/s'} "
+                f"{(u / step_s) / (1e9 if b == 'hbm' else 1e12):9.1f}  "
                 f"cand {int(st['n'].sum())}")
         if launches:
             per[kname] = dict(ms=tot_ms, launches=launches, units=units, bound=bound)
@@ -689,7 +694,8 @@ def per_kernel_and_line(w, args, stream, sec, times, mode):
     dom = max(per, key=lambda k: per[k]["ms"])
     d = per[dom]
     avg_s = d["ms"] / d["launches"] * 1e-3
-    achieved_per_s = d["units"] / d["launches"] / avg_s
+    # the class's algorithmic work over its total time (per launch: both / launches)
+    achieved_per_s = d["units"] / (d["ms"] * 1e-3)
     if d["bound"] == "hbm":
         achieved, peak, unit = achieved_per_s / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
