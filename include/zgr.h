@@ -233,9 +233,11 @@ typedef int32_t (*zgr_hidden_fn)(void* user, int32_t t, int32_t B, int32_t k_in,
  *   W_dev   L device pointers, W_t row-major [V][d] of dtype (kept, not copied;
  *           must outlive the plan).
  *   force   host int32 [L] of ZGR_PROJ_* or NULL (all AUTO).
- *   n_warmup  warm-up decodes; for every AUTO step both projections are timed
- *           with HIP events on each, and the one with the lower median wins
- *           (an exact tie picks selective).  With n_warmup = 0 or no callback,
+ *   n_warmup  warm-up decodes; in each, every AUTO step runs both projections
+ *           twice, interleaved, and the second run of each is timed with HIP
+ *           events (so the device is not waiting on host launches and both
+ *           see warm caches); the one with the lower median over the decodes
+ *           wins (an exact tie picks selective).  With n_warmup = 0 or no callback,
  *           AUTO steps use a bandwidth/MFMA cost model instead.
  *   hidden_fn, user  source of warm-up hidden vectors (may be NULL if no timing).
  * Limits: d % 64 == 0, d <= 4096; 1 <= K <= 1024; B >= 1; B*K < 2^31.

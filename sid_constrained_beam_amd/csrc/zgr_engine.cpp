@@ -348,8 +348,12 @@ int32_t read_device_flag(zgr_plan* p, hipStream_t s) {
 }
 
 // One decode (all L steps).  When time_opts is set, every AUTO step is run
-// with both projections, each timed with HIP events; the later run's outputs
-// carry the decode forward.
+// with both projections twice, interleaved (full, selective, full,
+// selective), and the second pair is timed with HIP events: by then the
+// stream holds queued work, so neither timing includes the device waiting on
+// the host to enqueue its launches, and each option finds the caches as the
+// other one left them.  A step only reads its inputs and overwrites its
+// outputs, so the last run's outputs carry the decode forward.
 int32_t decode_impl(zgr_plan* p, zgr_hidden_fn fn, void* user, hipStream_t s, bool time_opts,
                     std::vector<float>* t_full, std::vector<float>* t_sel, int* final_buf) {
   hipError_t e = launch_decode_init(p->row[0], p->cum[0], p->B, p->K, s);
@@ -373,8 +377,10 @@ int32_t decode_impl(zgr_plan* p, zgr_hidden_fn fn, void* user, hipStream_t s, bo
                            p->prefix[1 - cur]);
     if (time_opts && p->choice[t - 1] == ZGR_PROJ_AUTO) {
       float ms_full = 0.f, ms_sel = 0.f;
-      (void)hipEventRecord(ev[0], s);
       rc = run_step(p, a, ZGR_PROJ_FULL, s);
+      if (rc == ZGR_OK) rc = run_step(p, a, ZGR_PROJ_SELECTIVE, s);
+      (void)hipEventRecord(ev[0], s);
+      if (rc == ZGR_OK) rc = run_step(p, a, ZGR_PROJ_FULL, s);
       (void)hipEventRecord(ev[1], s);
       if (rc == ZGR_OK) rc = run_step(p, a, ZGR_PROJ_SELECTIVE, s);
       (void)hipEventRecord(ev[2], s);
