@@ -235,11 +235,31 @@ def read_traffic(kernel_name, workload):
         return None
 
 
+def _oracle_request(cat, w, r):
+    """One request decoded by the oracle; returns the seconds spent in its
+    steps (hidden-vector generation excluded)."""
+    import workload
+    cfg = w.cfg
+    spent = 0.0
+    prefixes = np.zeros((1, 0), np.int32)
+    cum = np.zeros(1)
+    for t in range(1, cfg.L + 1):
+        h = workload.hidden(cfg, t, np.full(len(prefixes), r, np.int64), prefixes, threads=1)[1]
+        s0 = time.perf_counter()
+        res = cat.step(t, w.W_f32[t - 1], prefixes, cum, h, cfg.K)
+        spent += time.perf_counter() - s0
+        k = len(res.sel_beam)
+        new = np.empty((k, t), np.int32)
+        new[:, : t - 1] = prefixes[res.sel_beam]
+        new[:, t - 1] = res.sel_token
+        prefixes, cum = new, res.sel_score.copy()
+    return spent
+
+
 def cpu_baseline(w, seconds):
     """The CPU oracle's filter+score+select on a bounded sample of the same
     workload's requests (single thread), scaled to one decode of B requests."""
     import oracle
-    import workload
     cfg = w.cfg
     t0 = time.time()
     cat = oracle.Catalog(w.sids, cfg.V)
@@ -247,18 +267,7 @@ def cpu_baseline(w, seconds):
     spent = 0.0
     done = 0
     for r in range(10 ** 6):
-        prefixes = np.zeros((1, 0), np.int32)
-        cum = np.zeros(1)
-        for t in range(1, cfg.L + 1):
-            h = workload.hidden(cfg, t, np.full(len(prefixes), r, np.int64), prefixes)[1]
-            s0 = time.perf_counter()
-            res = cat.step(t, w.W_f32[t - 1], prefixes, cum, h, cfg.K)
-            spent += time.perf_counter() - s0
-            k = len(res.sel_beam)
-            new = np.empty((k, t), np.int32)
-            new[:, : t - 1] = prefixes[res.sel_beam]
-            new[:, t - 1] = res.sel_token
-            prefixes, cum = new, res.sel_score.copy()
+        spent += _oracle_request(cat, w, r)
         done += 1
         if spent >= seconds:
             break

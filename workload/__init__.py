@@ -165,10 +165,12 @@ def weights(cfg: Config, t: int):
     return bits, f32
 
 
-def hidden(cfg: Config, t: int, req: Sequence[int], prefix: np.ndarray, want_f32: bool = True):
+def hidden(cfg: Config, t: int, req: Sequence[int], prefix: np.ndarray, want_f32: bool = True,
+           threads: Optional[int] = None):
     """Hidden vectors of M beams at step t (1-based).
 
     req: int64 [M] request ids; prefix: int32 [M, >= t-1] prefix tokens.
+    threads: generator threads (default: the host's, at most 16).
     Returns (stored bits [M, d], widened float32 [M, d] or None).
     """
     req = np.ascontiguousarray(np.asarray(req, dtype=np.int64))
@@ -182,7 +184,8 @@ def hidden(cfg: Config, t: int, req: Sequence[int], prefix: np.ndarray, want_f32
     f32 = np.empty((M, cfg.d), dtype=np.float32) if want_f32 else None
     lib().wl_hidden(cfg.seed_h, t, M, req.ctypes.data, prefix.ctypes.data, prefix.shape[1], cfg.d,
                     cfg.h_std, DTYPES[cfg.dtype], bits.ctypes.data,
-                    f32.ctypes.data if f32 is not None else None, _threads())
+                    f32.ctypes.data if f32 is not None else None,
+                    _threads() if threads is None else max(1, int(threads)))
     return bits, f32
 
 
