@@ -235,6 +235,24 @@ def read_traffic(kernel_name, workload):
         return None
 
 
+def host_cpu():
+    """The host's CPU model and the logical CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 0
+    return f"{model}, {n} logical CPUs available"
+
+
 def _oracle_request(cat, w, r):
     """One request decoded by the oracle; returns the seconds spent in its
     steps (hidden-vector generation excluded)."""
@@ -273,6 +291,7 @@ def cpu_baseline(w, seconds):
             break
     per_request_ms = spent / done * 1e3
     return {"value": round(per_request_ms * cfg.B, 3), "unit": "ms", "cores": 1, "kind": "oracle",
+            "host": host_cpu(),
             "sample": f"requests 0..{done - 1} of the {cfg.name} workload decoded by the oracle "
                       f"(double precision, one thread); {spent:.1f}s of step time (filter, score, "
                       f"legal-only log-softmax, select; hidden-vector generation and the "
