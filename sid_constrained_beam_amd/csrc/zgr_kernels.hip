@@ -312,19 +312,35 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
       }
     }
   }
-  __syncthreads();  // beams past the LDS cache are read back from nlegal
-  auto units_at = [&](int b) { return b < kUnitsCache ? ucache[b] : units_of_n(nlegal[b]); };
-  const int per = (M + 1023) / 1024;
-  const int b0 = min(M, (int)threadIdx.x * per), b1 = min(M, b0 + per);
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += units_at(b);
-  int total;
-  int run = block_excl_scan<1024>(mine, sh, &total);
-  for (int b = b0; b < b1; ++b) {
-    unit_start[b] = run;
-    run += units_at(b);
+  // The scan runs over chunks of kUnitsCache beams held in LDS (the first
+  // chunk was filled above; later ones are refilled from nlegal, coalesced):
+  // each thread sums a contiguous piece, the block scans the sums, each thread
+  // turns its piece into prefixes in place, and the chunk is written out
+  // coalesced.  carry is the units of the chunks before.
+  int carry = 0;
+  for (int c0 = 0; c0 < M; c0 += kUnitsCache) {
+    const int n = min(kUnitsCache, M - c0);
+    __syncthreads();  // pass 1 (or the previous chunk's write-out) is done with ucache
+    if (c0 > 0) {
+      for (int i = threadIdx.x; i < n; i += 1024) ucache[i] = units_of_n(nlegal[c0 + i]);
+      __syncthreads();
+    }
+    const int per = (n + 1023) / 1024;
+    const int b0 = min(n, (int)threadIdx.x * per), b1 = min(n, b0 + per);
+    int mine = 0;
+    for (int b = b0; b < b1; ++b) mine += ucache[b];
+    int total;
+    int run = carry + block_excl_scan<1024>(mine, sh, &total);
+    for (int b = b0; b < b1; ++b) {
+      const int u = ucache[b];
+      ucache[b] = run;
+      run += u;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 1024) unit_start[c0 + i] = ucache[i];
+    carry += total;
   }
-  if (threadIdx.x == 0) unit_start[M] = total;
+  if (threadIdx.x == 0) unit_start[M] = carry;
 }
 
 // ---------------------------------------------------------------- k_score_selective
