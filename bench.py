@@ -680,6 +680,42 @@ def time_decode(w, args, stream):
     return times[best], times, best
 
 
+def time_decode_api(w, args, stream):
+    """Seconds per zgr_decode call, end to end: the L steps, the per-step
+    hidden-vector callback (here a replay of the recorded hidden vectors,
+    device to device), the final outputs and the read of the device error
+    flag (a host synchronisation).  The difference to the step-only time is
+    the API's own overhead.  The decode must reproduce the recorded beams."""
+    import torch
+
+    import sid_constrained_beam_amd as zgr
+    cfg = w.cfg
+    hid = [st["hidden"] for st in w.steps]
+
+    def replay(t, B, k_in, pp, ld, hp, sp):
+        h = hid[t - 1]
+        zgr.copy_device(hp, h.data_ptr(), h.numel() * h.element_size(), sp)
+        return 0
+
+    item = torch.empty(cfg.B * cfg.K, dtype=torch.int64, device="cuda")
+    sid = torch.empty(cfg.B * cfg.K * cfg.L, dtype=torch.int32, device="cuda")
+    n = max(10, args.steps // 4)
+    with torch.cuda.stream(stream):
+        zgr.zgr_decode(w.plan, replay, cfg.K, item, sid, None, stream)
+        torch.cuda.synchronize()
+        got = sid.cpu().numpy().reshape(cfg.B, cfg.K, cfg.L)
+        if not np.array_equal(got[w.final_live], w.final_sids[w.final_live]):
+            raise RuntimeError("zgr_decode with replayed hidden vectors left the recorded trajectory")
+        for _ in range(3):
+            zgr.zgr_decode(w.plan, replay, cfg.K, item, None, None, stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            zgr.zgr_decode(w.plan, replay, cfg.K, item, None, None, stream)
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / n
+
+
 def per_kernel_and_line(w, args, stream, sec, times, mode):
     import torch
 
@@ -765,6 +801,9 @@ def per_kernel_and_line(w, args, stream, sec, times, mode):
         "ms_by_launch": {k: round(v * 1e3, 4) for k, v in times.items()},
         "hbm_gbs_algorithmic": round(hbm_bytes / sec / 1e9, 1),
         "roofline": roofline,
+        # zgr_decode end to end (callback replaying device-resident hidden
+        # vectors, final outputs, device-flag read): API overhead included
+        "zgr_decode_ms": round(time_decode_api(w, args, stream) * 1e3, 4),
     }
     if args.calibrate_copy:
         # a plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters

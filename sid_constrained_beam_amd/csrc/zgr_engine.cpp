@@ -62,6 +62,7 @@ struct zgr_plan {
   uint64_t* part_keys = nullptr;
   int32_t* part_cnt = nullptr;
   int32_t* err = nullptr;
+  int32_t* err_host = nullptr;  // pinned copy of the flag, read after one stream sync
   // decode state: double-buffered beams and prefixes, hidden vectors, outputs
   void* hidden = nullptr;
   int32_t *row[2] = {nullptr, nullptr}, *prefix[2] = {nullptr, nullptr};
@@ -333,11 +334,12 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
 }
 
 int32_t read_device_flag(zgr_plan* p, hipStream_t s) {
-  hipError_t e = hipStreamSynchronize(s);
+  // the flag follows the stream's work into pinned memory: one synchronisation
+  hipError_t e = hipMemcpyAsync(p->err_host, p->err, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync error flag");
+  e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-  int32_t flag = 0;
-  e = hipMemcpy(&flag, p->err, sizeof(int32_t), hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpy error flag");
+  const int32_t flag = *(volatile int32_t*)p->err_host;
   if (flag) {
     const int32_t zero = 0;
     e = hipMemcpy(p->err, &zero, sizeof(int32_t), hipMemcpyHostToDevice);
@@ -529,6 +531,11 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   A(&all_rp, 8);
   A(&all_bits, (size_t)words * 4);
   A(&all_rank, (size_t)words * 2);
+  if (rc == ZGR_OK && hipHostMalloc((void**)&p->err_host, sizeof(int32_t), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    p->err_host = nullptr;
+    rc = fail(ZGR_E_NOMEM, "zgr_plan: pinned host flag");
+  }
   if (rc != ZGR_OK) {
     zgr_plan_free(p);
     return rc;
@@ -657,6 +664,7 @@ int32_t zgr_plan_profile_read(zgr_plan* p, int32_t kernel, int32_t t, int64_t* l
 void zgr_plan_free(zgr_plan* p) {
   if (!p) return;
   (void)prof_flush(p);
+  if (p->err_host) (void)hipHostFree(p->err_host);
   for (hipEvent_t e : p->pool) (void)hipEventDestroy(e);
   p->pool.clear();
   for (void* x : {(void*)p->naive_beam, (void*)p->naive_tok, p->naive_tmp})
