@@ -1413,8 +1413,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   __shared__ __attribute__((aligned(16))) char smem[STAGE > CTILE ? STAGE : CTILE];
   char* As = smem;
   char* Bs = smem + BM * kLdsRow;
-  __shared__ uint32_t tbits[BM * TW];
-  __shared__ int trank[BM * TW];
+  __shared__ int2 tword[BM * TW];  // a tile row's bitmap word and its legal rank, together
   int tm, tn;
   GemmOrder(M, N, BM, BN).tile((int)blockIdx.x, tm, tn);
   if (tm < 0) return;  // padding block (before any barrier)
@@ -1605,11 +1604,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   if ((int)threadIdx.x < BM) {
 #pragma unroll
     for (int k = 0; k < TW; ++k) {
-      tbits[threadIdx.x * TW + k] = pdw[k].bits;
-      trank[threadIdx.x * TW + k] = pdw[k].rank;
+      tword[threadIdx.x * TW + k] = make_int2((int)pdw[k].bits, pdw[k].rank);
     }
   }
   __syncthreads();
+  // Each output: one LDS read (word and rank), a bit test, a popcount and a
+  // 32-bit offset from the lane's first row (rows of the tile differ by a
+  // constant times ldc; the compact rows have ldc = V <= 65536, so the
+  // offsets stay below 2^31).
+  const int ldc32 = (int)ldc;
+  const uint32_t below = (1u << l32) - 1u;
+  float* cw = C + (int64_t)(m0 + wm * WM + 4 * half) * ldc;
 #pragma unroll
   for (int i = 0; i < IB; ++i)
 #pragma unroll
@@ -1617,10 +1622,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
       const int kw = (wn * WN + j * 32) >> 5;  // the block's 32 columns are one bitmap word
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int rl = wm * WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        const uint32_t x = tbits[rl * TW + kw];
-        if ((x >> l32) & 1u)
-          C[(int64_t)(m0 + rl) * ldc + trank[rl * TW + kw] + __popc(x & ((1u << l32) - 1u))] = acc[i][j][v];
+        const int ro = i * 32 + 8 * (v >> 2) + (v & 3);  // row within the lane's rows
+        const int2 wr = tword[(wm * WM + 4 * half + ro) * TW + kw];
+        const uint32_t x = (uint32_t)wr.x;
+        if ((x >> l32) & 1u) cw[ro * ldc32 + wr.y + (int)__popc(x & below)] = acc[i][j][v];
       }
     }
 }
