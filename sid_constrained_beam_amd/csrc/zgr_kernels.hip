@@ -484,6 +484,10 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
   const int first_b = by_xcd ? (int)blockIdx.x / 8 : (int)blockIdx.x;
   const int t_step = by_xcd ? 8 : 1;
   const int t_first = by_xcd ? (int)blockIdx.x % 8 : 0;
+  // Wave 0 fetches the next pair's bitmap words while the block scores the
+  // current pair (pf_pb: the pair they belong to, -1 = none).
+  int pf_pb = -1;
+  DWord pf_dw{0u, 0};
   for (int tile = t_first; tile < tiles; tile += t_step) {
     // without the XCD split, pairs run over (tile, beam) in one flat range
     const int nb = by_xcd ? M : M * tiles;
@@ -501,7 +505,20 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       const int nw = min(tt >> 5, tab.words - w0);
       __syncthreads();  // previous pair's readers are done with lst
       if (threadIdx.x < 64) {
-        const DWord dw = (lane < nw) ? dense_word<NX>(tab, r, w0 + lane) : DWord{0u, 0};
+        const DWord dw = (pf_pb == pb) ? pf_dw : (lane < nw) ? dense_word<NX>(tab, r, w0 + lane) : DWord{0u, 0};
+        // the next pair of this block within the tile (its loads overlap the scoring below)
+        pf_pb = -1;
+        const int pn = pb + stride_b;
+        if (pn < nb) {
+          const int bn = by_xcd ? pn : pn / tiles;
+          const int tn = by_xcd ? tile : pn % tiles;
+          const int rn = row_in[bn];
+          const int wn0 = (tn * tt) >> 5;
+          if (rn >= 0 && rn < tab.rows) {
+            pf_pb = pn;
+            pf_dw = (lane < min(tt >> 5, tab.words - wn0)) ? dense_word<NX>(tab, rn, wn0 + lane) : DWord{0u, 0};
+          }
+        }
         const uint32_t word = dw.bits;
         int rk = dw.rank;
         const int pc = __popc(word);
