@@ -1008,10 +1008,13 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       uint32_t x = (dw.bits >> lo) & sub_mask;
       int j = cpre[bl] + dw.rank + __popc(dw.bits & ((1u << lo) - 1u));
       const uint32_t code0 = (uint32_t)(blo + bl) * S + (uint32_t)((w << 5) + lo);
+      // the key's high half (the score) was stored with a zero low half above:
+      // the code goes into the low half alone, with no read of the key
+      uint32_t* key_lo = reinterpret_cast<uint32_t*>(keys);
       while (x) {
         const int k = __ffs(x) - 1;
         x &= x - 1;
-        keys[j++] |= code0 + (uint32_t)k;
+        key_lo[2 * (j++)] = code0 + (uint32_t)k;
       }
     }
     __syncthreads();
