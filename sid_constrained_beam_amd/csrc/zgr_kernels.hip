@@ -1481,22 +1481,36 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
       }
     }
   }
-  // global -> register staging of A and B slices
+  // global -> register staging of A and B slices.  Each load's row pointer
+  // is formed once; rows past M or N read zeros.  A tile wholly inside both
+  // (every tile but the edges) issues its loads without per-load guards.
   uint4 ra[NA], rb[NB];
+  const char* pa[NA];
+  const char* pb[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int c = threadIdx.x + i * kThreads;
+    const int gm = m0 + (c >> 3);
+    pa[i] = gm < M ? Ab + (int64_t)gm * rowbytes + (c & 7) * 16 : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int c = threadIdx.x + i * kThreads;
+    const int gn = n0 + (c >> 3);
+    pb[i] = gn < N ? Bb + (int64_t)gn * rowbytes + (c & 7) * 16 : nullptr;
+  }
+  const bool whole = m0 + BM <= M && n0 + BN <= N;  // uniform over the block
   auto gload = [&](int kbyte) {
+    if (whole) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c >> 3, col = (c & 7) * 16;
-      const int gm = m0 + row;
-      ra[i] = (gm < M) ? *(const uint4*)(Ab + gm * rowbytes + kbyte + col) : make_uint4(0, 0, 0, 0);
-    }
+      for (int i = 0; i < NA; ++i) ra[i] = *(const uint4*)(pa[i] + kbyte);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c >> 3, col = (c & 7) * 16;
-      const int gn = n0 + row;
-      rb[i] = (gn < N) ? *(const uint4*)(Bb + gn * rowbytes + kbyte + col) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < NB; ++i) rb[i] = *(const uint4*)(pb[i] + kbyte);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) ra[i] = pa[i] ? *(const uint4*)(pa[i] + kbyte) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) rb[i] = pb[i] ? *(const uint4*)(pb[i] + kbyte) : make_uint4(0, 0, 0, 0);
     }
   };
   auto sstore = [&]() {
