@@ -716,6 +716,28 @@ def time_decode_api(w, args, stream):
     return (time.perf_counter() - t0) / n
 
 
+def kernel_classes(records, work, n_dec):
+    """Per kernel class: total time (ms) and launches over n_dec profiled
+    decodes, and the algorithmic work those decodes did (work(kernel, step) is
+    one step's bytes or flops, counted once per step per decode however many
+    launches the step took: a request split over blocks launches the parts,
+    then their merge).  records: kernel -> [(step, launches, total_ms)]."""
+    per = {}
+    for kname, steps in records.items():
+        tot_ms, launches, units, bound = 0.0, 0, 0.0, None
+        for st, n, kms in steps:
+            if n == 0:
+                continue
+            b, u = work(kname, st)
+            bound = b
+            tot_ms += kms
+            launches += n
+            units += u * n_dec
+        if launches:
+            per[kname] = dict(ms=tot_ms, launches=launches, units=units, bound=bound)
+    return per
+
+
 def per_kernel_and_line(w, args, stream, sec, times, mode):
     import torch
 
@@ -731,29 +753,20 @@ def per_kernel_and_line(w, args, stream, sec, times, mode):
         for _ in range(n_dec):
             w.run_decode(stream)
         torch.cuda.synchronize()
-    per = {}
-    total_kernel_ms = 0.0
-    for kname in zgr.KERNELS:
-        tot_ms, launches, units, bound = 0.0, 0, 0.0, None
-        for st in w.steps:
-            n, kms = zgr.zgr_plan_profile_read(w.plan, kname, st["t"])
+    records = {kname: [(st, *zgr.zgr_plan_profile_read(w.plan, kname, st["t"])) for st in w.steps]
+               for kname in zgr.KERNELS}
+    per = kernel_classes(records, w.work, n_dec)
+    total_kernel_ms = sum(d["ms"] for d in per.values())
+    for kname, steps in records.items():
+        for st, n, kms in steps:
             if n == 0:
                 continue
-            # u is the step's work; a step may take several launches of one
-            # kernel (a request split over blocks, then its merge)
             b, u = w.work(kname, st)
-            bound = b
-            tot_ms += kms
-            launches += n
-            units += u * n_dec
             step_s = kms / n_dec * 1e-3
             log(f"[bench]   t{st['t']} {kname:15s} {step_s * 1e6:8.2f} us/step ({n // n_dec} launch"
                 f"{'es' if n > n_dec else ''})  {'GB/s' if b == 'hbm' else 'TFLOP/s'} "
                 f"{(u / step_s) / (1e9 if b == 'hbm' else 1e12):9.1f}  "
                 f"cand {int(st['n'].sum())}")
-        if launches:
-            per[kname] = dict(ms=tot_ms, launches=launches, units=units, bound=bound)
-            total_kernel_ms += tot_ms
     zgr.zgr_plan_profile(w.plan, 0)
     dom = max(per, key=lambda k: per[k]["ms"])
     d = per[dom]
