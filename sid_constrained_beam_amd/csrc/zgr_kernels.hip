@@ -1190,21 +1190,19 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         const int i = i0 + threadIdx.x;
         const uint64_t k = i < C ? keys[i] : 0ull;
         const int bn = i < C ? bin_of(k) : kDistBins;
-        if (__ballot(bn <= bstar) == 0) continue;  // wave-uniform: nothing to keep here
-        // one wave scan for both appends: selected keys in the low half,
-        // boundary keys in the high half (at most 64 of each per wave)
-        const int inc = (bn < bstar ? 1 : 0) | (bn == bstar ? (1 << 16) : 0);
-        const int incl = wave_incl_scan(inc);
-        const int tot = __shfl(incl, 63);
+        // the wave's selected and boundary keys as two lane masks: a lane's
+        // append position is the count of its category's lanes below it
+        const uint64_t m1 = __ballot(bn < bstar), m2 = __ballot(bn == bstar);
+        if ((m1 | m2) == 0) continue;  // wave-uniform: nothing to keep here
         int b1 = 0, b2 = 0;
-        if (lane == 63) {
-          if (tot & 0xFFFF) b1 = atomicAdd(&pos, tot & 0xFFFF);
-          if (tot >> 16) b2 = atomicAdd(&pos2, tot >> 16);
+        if (lane == 0) {
+          if (m1) b1 = atomicAdd(&pos, __popcll(m1));
+          if (m2) b2 = atomicAdd(&pos2, __popcll(m2));
         }
-        b1 = __shfl(b1, 63);
-        b2 = __shfl(b2, 63);
-        const int ex = incl - inc;
-        const int a1 = b1 + (ex & 0xFFFF), a2 = b2 + (ex >> 16);
+        b1 = __shfl(b1, 0);
+        b2 = __shfl(b2, 0);
+        const uint64_t lower = (1ull << lane) - 1ull;
+        const int a1 = b1 + __popcll(m1 & lower), a2 = b2 + __popcll(m2 & lower);
         if (bn < bstar && a1 < kMaxK) sel[a1] = k;
         if (bn == bstar && a2 < kBoundary) bnd[a2] = k;
       }
