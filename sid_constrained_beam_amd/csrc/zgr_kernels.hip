@@ -120,14 +120,19 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
   return ((uint64_t)hi << 32) | lo;
 }
-// inclusive prefix sum over the 64 lanes
+// Inclusive prefix sum over the 64 lanes, with DPP moves only (no LDS
+// crossbar permutes): shifts by 1, 2, 4 and 8 within each 16-lane row (a
+// lane without a source adds 0), then lane 15 of rows 0 and 2 is broadcast
+// into rows 1 and 3, and lane 31 (the total of rows 0-1) into rows 2 and 3.
+// DPP controls: row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 =
+// 0x143; row masks 0xa (rows 1, 3) and 0xc (rows 2, 3).
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
   return v;
 }
 
@@ -1898,15 +1903,22 @@ int resident_blocks_per_cu(Kernel kernel, int threads) {
   return n;
 }
 
+// At most this many selective-projection blocks per CU: more resident blocks
+// gather more weight rows at once than an XCD's L2 keeps (1e8-item step 2,
+// d = 1024 f32: 1109 us at 5 blocks per CU, 1181 us at 6).
+constexpr int kSelMaxBlocksPerCu = 5;
+
 template <int DT, int D>
 hipError_t launch_sel_typed(const StepArgs& a, hipStream_t s) {
   const int32_t tt = dense_tile_tokens(D, DT);
   if (a.tab.next) {
-    static const int per_cu = resident_blocks_per_cu(k_score_selective<DT, D, true>, kThreads);
+    static const int per_cu =
+        std::min(kSelMaxBlocksPerCu, resident_blocks_per_cu(k_score_selective<DT, D, true>, kThreads));
     hipLaunchKernelGGL((k_score_selective<DT, D, true>), dim3(a.n_cu * per_cu), dim3(kThreads), 0, s,
                        a.unit_start, a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz, tt);
   } else {
-    static const int per_cu = resident_blocks_per_cu(k_score_selective<DT, D, false>, kThreads);
+    static const int per_cu =
+        std::min(kSelMaxBlocksPerCu, resident_blocks_per_cu(k_score_selective<DT, D, false>, kThreads));
     hipLaunchKernelGGL((k_score_selective<DT, D, false>), dim3(a.n_cu * per_cu), dim3(kThreads), 0, s,
                        a.unit_start, a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz, tt);
   }
