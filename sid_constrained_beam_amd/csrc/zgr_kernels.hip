@@ -687,17 +687,6 @@ __device__ __forceinline__ int dist_bin(uint32_t d) {
   return ((e - 5) << 6) | (int)((d >> (e - 6)) & 63u);
 }
 
-// Each lane asks for cnt slots of a block-shared array: one atomic per wave.
-// Must be reached by all 64 lanes of the wave.
-__device__ __forceinline__ int wave_alloc(int cnt, int* counter) {
-  const int incl = wave_incl_scan(cnt);
-  const int total = __shfl(incl, 63);
-  int base = 0;
-  if ((threadIdx.x & 63) == 63 && total > 0) base = atomicAdd(counter, total);
-  base = __shfl(base, 63);
-  return base + incl - cnt;
-}
-
 // How z reaches the request kernel: token-indexed rows (full projection, or a
 // dense step), slot-indexed rows (selective projection of a sparse step), or
 // computed by the request kernel itself (selective projection of a light
@@ -1204,8 +1193,9 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
           if (m1) b1 = atomicAdd(&pos, __popcll(m1));
           if (m2) b2 = atomicAdd(&pos2, __popcll(m2));
         }
-        b1 = __shfl(b1, 0);
-        b2 = __shfl(b2, 0);
+        // lane 0's results to the whole wave (scalar read, every lane is active)
+        b1 = __builtin_amdgcn_readfirstlane(b1);
+        b2 = __builtin_amdgcn_readfirstlane(b2);
         const uint64_t lower = (1ull << lane) - 1ull;
         const int a1 = b1 + __popcll(m1 & lower), a2 = b2 + __popcll(m2 & lower);
         if (bn < bstar && a1 < kMaxK) sel[a1] = k;
