@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "zgr_internal.h"
 
@@ -106,19 +107,50 @@ __device__ __forceinline__ uint64_t make_key(float cand, uint32_t slotcode) {
 
 // ---------------------------------------------------------------- wave / block helpers
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+// Value of x held by lane (lane ^ O), for a compile-time O in {1, ..., 32}, every
+// lane of the wave active.  Within a 16-lane row the exchange is a DPP move
+// (O = 1, 2: quad permutations 0xB1 and 0x4E; O = 4: row_shl:4 into banks 0
+// and 2, row_shr:4 into banks 1 and 3; O = 8: row_ror:8), so it stays off the
+// LDS crossbar; O = 16 and 32 cross rows and use a permute.
+template <int O>
+__device__ __forceinline__ int xor_lane(int x) {
+  static_assert(O == 1 || O == 2 || O == 4 || O == 8 || O == 16 || O == 32, "lane xor");
+  if constexpr (O == 1) return __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);
+  else if constexpr (O == 2) return __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);
+  else if constexpr (O == 4) {
+    const int t = __builtin_amdgcn_update_dpp(0, x, 0x104, 0xf, 0x5, false);
+    return __builtin_amdgcn_update_dpp(t, x, 0x114, 0xf, 0xa, false);
+  } else if constexpr (O == 8) return __builtin_amdgcn_update_dpp(0, x, 0x128, 0xf, 0xf, false);
+  else return __shfl_xor(x, O);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+template <int O>
+__device__ __forceinline__ float xor_lane(float v) {
+  return __int_as_float(xor_lane<O>(__float_as_int(v)));
 }
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
+template <int O>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  return (uint32_t)xor_lane<O>((int)v);
+}
+template <int O>
+__device__ __forceinline__ uint64_t xor_lane(uint64_t v) {
+  const uint32_t lo = xor_lane<O>((uint32_t)v), hi = xor_lane<O>((uint32_t)(v >> 32));
   return ((uint64_t)hi << 32) | lo;
+}
+// Calls f(integral_constant<O>) for O, O/2, ..., 1: the butterfly stages of a
+// reduction over an aligned group of 2*O lanes.
+template <int O, typename F>
+__device__ __forceinline__ void xor_down(F&& f) {
+  if constexpr (O >= 1) {
+    f(std::integral_constant<int, O>{});
+    xor_down<O / 2>(f);
+  }
+}
+// Sum of v over an aligned group of G lanes (G a power of two, at most 64),
+// every lane of the group active; every lane ends with the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  xor_down<G / 2>([&](auto o) { v += xor_lane<decltype(o)::value>(v); });
+  return v;
 }
 // Inclusive prefix sum over the 64 lanes, with DPP moves only (no LDS
 // crossbar permutes): shifts by 1, 2, 4 and 8 within each 16-lane row (a
@@ -159,11 +191,10 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
 template <int NT>
 __device__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
   constexpr int NW = NT / 64;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t u = shfl_xor_u64(v, o);
+  xor_down<32>([&](auto o) {
+    const uint64_t u = xor_lane<decltype(o)::value>(v);
     v = u > v ? u : v;
-  }
+  });
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -175,11 +206,10 @@ __device__ uint64_t block_max_u64(uint64_t v, uint64_t* sh) {
 template <int NT>
 __device__ uint64_t block_min_u64(uint64_t v, uint64_t* sh) {
   constexpr int NW = NT / 64;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t u = shfl_xor_u64(v, o);
+  xor_down<32>([&](auto o) {
+    const uint64_t u = xor_lane<decltype(o)::value>(v);
     v = u < v ? u : v;
-  }
+  });
   __syncthreads();
   if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
@@ -374,22 +404,23 @@ struct SelShape {
 // power of two, U <= G): U - 1 shuffles halve the vector (each lane keeps
 // the half that its partner does not), then a butterfly over the remaining
 // G / U lanes.  Lane gl ends with the sum of candidate gl / (G / U).
+template <int U, int N, int O>
+__device__ __forceinline__ void group_halve(float (&acc)[U], int gl) {
+  if constexpr (N > 1) {
+    const bool hi = (gl & O) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float send = hi ? acc[i] : acc[i + N / 2];
+      const float keep = hi ? acc[i + N / 2] : acc[i];
+      acc[i] = keep + xor_lane<O>(send);
+    }
+    group_halve<U, N / 2, O / 2>(acc, gl);
+  }
+}
 template <int G, int U>
 __device__ __forceinline__ float group_sum_multi(float (&acc)[U], int gl) {
-#pragma unroll
-  for (int n = U, o = G / 2; n > 1; n >>= 1, o >>= 1) {
-    const bool hi = (gl & o) != 0;
-#pragma unroll
-    for (int i = 0; i < n / 2; ++i) {
-      const float send = hi ? acc[i] : acc[i + n / 2];
-      const float keep = hi ? acc[i + n / 2] : acc[i];
-      acc[i] = keep + __shfl_xor(send, o);
-    }
-  }
-  float v = acc[0];
-#pragma unroll
-  for (int o = G / (2 * U); o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  group_halve<U, U, G / 2>(acc, gl);
+  return group_sum<G / U>(acc[0]);
 }
 
 template <int DT, int D, bool NX>
@@ -659,8 +690,7 @@ __global__ __launch_bounds__(kThreads) void k_naive_dot(const void* __restrict__
 #pragma unroll
       for (int e = 0; e < VEC; ++e) acc = fmaf(w[e], h[e], acc);
     }
-#pragma unroll
-    for (int o = G / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+    acc = group_sum<G>(acc);
     if (gl == 0) z[(int64_t)b * ldz + (c - start[b])] = acc;
   }
 }
@@ -857,8 +887,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       }
 #pragma unroll
       for (int u = 0; u < U2; ++u) {
-#pragma unroll
-        for (int o = G / 2; o >= 1; o >>= 1) acc[u] += __shfl_xor(acc[u], o);
+        acc[u] = group_sum<G>(acc[u]);
         const int f = f0 + u * NGB;
         if (gl == 0 && f < C) {
           z[(int64_t)(b0 + bls[u]) * ldz + js[u]] = acc[u];
@@ -970,8 +999,10 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         if (r3 >= 0) atomicMax(&omax_sh, ord_of(bcum[bl3] + (m - l)));
       }
     } else {
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
+      xor_down<32>([&](auto o) {
+        constexpr int X = decltype(o)::value;
+        lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
+      });
       if (lane == 0) {
         pm[wave] = m;
         ps[wave] = s;
@@ -1056,8 +1087,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         o = max(o, (uint32_t)(kk >> 32));
       }
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) o = max(o, (uint32_t)__shfl_xor((int)o, d));
+    xor_down<32>([&](auto d) { o = max(o, xor_lane<decltype(d)::value>(o)); });
     if (lane == 0) sh[wave] = (int)o;
     __syncthreads();
     omax = 0;
@@ -1861,8 +1891,10 @@ __global__ __launch_bounds__(256) void k_row_lse(const float* __restrict__ z, in
   } else {
     for (int i = lane; i < V; i += 64) acc(zr[i]);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lse_combine(m, sum, __shfl_xor(m, o), __shfl_xor(sum, o));
+  xor_down<32>([&](auto o) {
+    constexpr int X = decltype(o)::value;
+    lse_combine(m, sum, xor_lane<X>(m), xor_lane<X>(sum));
+  });
   if (lane == 0) lse[b] = m + __logf(sum);
 }
 
