@@ -145,6 +145,21 @@ __device__ __forceinline__ void xor_down(F&& f) {
     xor_down<O / 2>(f);
   }
 }
+// The same stages for a group width W known only at run time (a power of two
+// in [1, 64], equal across the wave): the switch falls through from the widest
+// stage the width needs down to offset 1, so each stage is compiled once.
+template <typename F>
+__device__ __forceinline__ void xor_down_width(int W, F&& f) {
+  switch (W) {
+    case 64: f(std::integral_constant<int, 32>{}); [[fallthrough]];
+    case 32: f(std::integral_constant<int, 16>{}); [[fallthrough]];
+    case 16: f(std::integral_constant<int, 8>{}); [[fallthrough]];
+    case 8: f(std::integral_constant<int, 4>{}); [[fallthrough]];
+    case 4: f(std::integral_constant<int, 2>{}); [[fallthrough]];
+    case 2: f(std::integral_constant<int, 1>{}); [[fallthrough]];
+    default: break;
+  }
+}
 // Sum of v over an aligned group of G lanes (G a power of two, at most 64),
 // every lane of the group active; every lane ends with the sum.
 template <int G>
@@ -991,7 +1006,10 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       }
     }
     if (LPB <= 64) {
-      for (int o = LPB >> 1; o >= 1; o >>= 1) lse_combine(m, s, __shfl_xor(m, o), __shfl_xor(s, o));
+      xor_down_width(LPB, [&](auto o) {
+        constexpr int X = decltype(o)::value;
+        lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
+      });
       if (lb == 0 && bl3 < nloc) {
         const float l = lse_ext ? lse_ext[b0 + bl3] : m + __logf(s);
         blse[bl3] = l;
@@ -1179,7 +1197,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
 #pragma unroll
           for (int u = 0; u < 8; ++u) rank += (j0 + u * G < C && kk[u] > mine) ? 1 : 0;
         }
-      for (int o = G >> 1; o >= 1; o >>= 1) rank += __shfl_xor(rank, o);
+      xor_down_width(G, [&](auto o) { rank += xor_lane<decltype(o)::value>(rank); });
       if (i < C && g == 0 && rank < K) sel[rank] = mine;
     }
   } else if (C <= K) {
@@ -1335,7 +1353,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       mine = sel[i];
       for (int j = g; j < nsel; j += G) rank += sel[j] > mine ? 1 : 0;
     }
-    for (int o = G >> 1; o >= 1; o >>= 1) rank += __shfl_xor(rank, o);
+    xor_down_width(G, [&](auto o) { rank += xor_lane<decltype(o)::value>(rank); });
     __syncthreads();
     if (i < nsel && g == 0) keys[rank] = mine;
     __syncthreads();
