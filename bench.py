@@ -8,8 +8,11 @@ per-request select) for a batch of B requests, with every step's inputs
 inputs are those of a real decode of the workload (recorded once, untimed);
 the hidden vectors stand in for the model, whose time the metric excludes.
 
-Default workload: L=3, V=2048, N=1e6 items (Zipf 1.1 per level), d=256,
-beam 64, batch 32, fp32 ("n1e6_v2048").  Prints one JSON line.
+Default workload: the largest codebook of the batch-32 codebook sweep, L=4,
+V=16384, N=1e7 items (Zipf 1.1 per level), d=512, beam 128, batch 32, bf16
+storage with fp32 accumulation ("n1e7_v16384"); the sweep's other codebooks
+(2048, 4096, 8192) and the 1e6-, 5e7- and 1e8-item catalogs are timed after it
+and reported in the same line.  Prints one JSON line.
 """
 import argparse
 import hashlib
@@ -24,6 +27,10 @@ if ROOT not in sys.path:
 
 import numpy as np  # noqa: E402
 
+# the metric's workload: the largest codebook of the batch-32 codebook sweep
+HEADLINE = "n1e7_v16384"
+DEFAULT_SWEEP = ["n1e7_v2048", "n1e7_v4096", "n1e7_v8192", "n1e6_v2048", "n5e7_v1024_dense",
+                 "n1e8_v16384"]
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}
 KERNEL_NAMES = {
@@ -84,6 +91,15 @@ class Workload:
             f"t{t + 1}={'full' if c[0] == 1 else 'selective'} (full {c[1]:.1f}us, sel {c[2]:.1f}us)"
             for t, c in enumerate(self.choices)))
         self._record()
+
+    def free(self):
+        """Release the plan, the index and the device buffers."""
+        import torch
+        torch.cuda.synchronize()
+        self.plan.free()
+        self.index.free()
+        self.W_dev = self.steps = self.out = None
+        torch.cuda.empty_cache()
 
     def _fill_hidden(self, t, B, k_in, prefix_ptr, ld, hidden_ptr, stream_ptr, base):
         import workload
@@ -253,18 +269,17 @@ def host_cpu():
     return f"{model}, {n} logical CPUs available"
 
 
-def _oracle_request(cat, w, r):
+def _oracle_request(cat, cfg, W, r):
     """One request decoded by the oracle; returns the seconds spent in its
     steps (hidden-vector generation excluded)."""
     import workload
-    cfg = w.cfg
     spent = 0.0
     prefixes = np.zeros((1, 0), np.int32)
     cum = np.zeros(1)
     for t in range(1, cfg.L + 1):
         h = workload.hidden(cfg, t, np.full(len(prefixes), r, np.int64), prefixes, threads=1)[1]
         s0 = time.perf_counter()
-        res = cat.step(t, w.W_f32[t - 1], prefixes, cum, h, cfg.K)
+        res = cat.step(t, W[t - 1], prefixes, cum, h, cfg.K)
         spent += time.perf_counter() - s0
         k = len(res.sel_beam)
         new = np.empty((k, t), np.int32)
@@ -274,29 +289,81 @@ def _oracle_request(cat, w, r):
     return spent
 
 
-def cpu_baseline(w, seconds):
-    """The CPU oracle's filter+score+select on a bounded sample of the same
-    workload's requests (single thread), scaled to one decode of B requests."""
-    import oracle
-    cfg = w.cfg
-    t0 = time.time()
-    cat = oracle.Catalog(w.sids, cfg.V)
-    build_s = time.time() - t0
-    spent = 0.0
-    done = 0
-    for r in range(10 ** 6):
-        spent += _oracle_request(cat, w, r)
+# what forked CPU-baseline workers read (set in the parent before the fork)
+_CPU_STATE = {}
+
+
+def _cpu_worker(arg):
+    """One worker process of the all-core baseline: requests first, first +
+    stride, ... until `seconds` of step time; returns (requests, step seconds)."""
+    first, stride, seconds = arg
+    cat, cfg, W = _CPU_STATE["cat"], _CPU_STATE["cfg"], _CPU_STATE["W"]
+    spent, done, r = 0.0, 0, first
+    while spent < seconds:
+        spent += _oracle_request(cat, cfg, W, r)
         done += 1
-        if spent >= seconds:
-            break
-    per_request_ms = spent / done * 1e3
-    return {"value": round(per_request_ms * cfg.B, 3), "unit": "ms", "cores": 1, "kind": "oracle",
+        r += stride
+    return done, spent
+
+
+def cpu_share():
+    """Logical CPUs this process may run on, at most 16 (one GPU's share of
+    the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(cfg, seconds):
+    """The CPU oracle's filter+score+select on bounded samples of the
+    workload's requests, scaled to one decode of B requests: once on one
+    thread, once with requests split over one forked worker process per
+    available core (at most 16).  Runs before the GPU is touched, so the
+    workers are forked from a process without a GPU context; each worker
+    times its own step calls, and the all-core rate is the sum of the
+    workers' rates measured while all of them run."""
+    import multiprocessing as mp
+
+    import oracle
+    import workload
+    t0 = time.time()
+    sids = workload.catalog(cfg)
+    W = [workload.weights(cfg, t)[1] for t in range(1, cfg.L + 1)]
+    gen_s = time.time() - t0
+    t0 = time.time()
+    cat = oracle.Catalog(sids, cfg.V)
+    build_s = time.time() - t0
+    del sids
+    half = seconds / 2.0
+    spent, done = 0.0, 0
+    while spent < half:
+        spent += _oracle_request(cat, cfg, W, done)
+        done += 1
+    single_ms = spent / done * 1e3 * cfg.B
+    log(f"[cpu] {cfg.name}: one thread, {done} requests in {spent:.1f}s of step time "
+        f"-> {single_ms:.1f} ms per decode of {cfg.B}")
+    P = cpu_share()
+    _CPU_STATE.update(cat=cat, cfg=cfg, W=W)
+    with mp.get_context("fork").Pool(P) as pool:
+        res = pool.map(_cpu_worker, [(done + i, P, half) for i in range(P)])
+    _CPU_STATE.clear()
+    rate = sum(n / s for n, s in res)  # requests per second over all workers
+    all_ms = cfg.B / rate * 1e3
+    reqs = sum(n for n, _ in res)
+    log(f"[cpu] {cfg.name}: {P} worker processes, {reqs} requests -> {all_ms:.2f} ms per decode")
+    return {"value": round(all_ms, 3), "unit": "ms", "cores": P, "kind": "oracle",
+            "single_core_ms": round(single_ms, 3), "all_core_ms": round(all_ms, 3),
             "host": host_cpu(),
-            "sample": f"requests 0..{done - 1} of the {cfg.name} workload decoded by the oracle "
-                      f"(double precision, one thread); {spent:.1f}s of step time (filter, score, "
-                      f"legal-only log-softmax, select; hidden-vector generation and the "
-                      f"{build_s:.1f}s trie build excluded), scaled to one decode of "
-                      f"{cfg.B} requests"}
+            "sample": f"{cfg.name} requests decoded by the oracle (double precision): requests "
+                      f"0..{done - 1} on one thread ({spent:.1f}s of step time), then {reqs} "
+                      f"further requests over {P} forked worker processes, one per available "
+                      f"core, ~{half:.0f}s of step time each; step time = filter, score, "
+                      f"legal-only log-softmax, select (hidden-vector generation, the "
+                      f"{gen_s:.1f}s input generation and the {build_s:.1f}s trie build "
+                      f"excluded); value = all-core time per decode of {cfg.B} requests "
+                      f"(B / sum of the workers' request rates)"}
 
 
 def rebuild_bench(name, reps):
@@ -582,7 +649,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="n1e6_v2048")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--sweep", default=None,
+                    help="comma list of further workloads timed for the line's sweep_ms / "
+                         "other_workloads_ms (default: the other codebooks of the 1e7-item sweep, "
+                         "then the 1e6-, 5e7- and 1e8-item catalogs, when the headline workload "
+                         "runs); 'none' for none")
+    ap.add_argument("--sweep-steps", type=int, default=50, help="timed decodes per sweep workload")
     ap.add_argument("--plan-warmup", type=int, default=5, help="warm-up decodes of the planner")
     ap.add_argument("--force", default=None, help="comma list of full/selective per step")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph replay")
@@ -625,20 +698,58 @@ def main():
     if args.projections:
         projections_bench(args)
         return
+    import workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        # before anything touches the GPU: the all-core leg forks worker processes
+        cpu = cpu_baseline(workload.CONFIGS[args.workload], args.cpu_seconds)
     import torch
-
-    import sid_constrained_beam_amd as zgr
     torch.cuda.set_device(0)
     force = args.force.split(",") if args.force else None
     w = Workload(args.workload, args.plan_warmup, force)
-    cfg = w.cfg
 
     # ---- timed region: whole decodes (L steps) over recorded HBM-resident inputs
     stream = torch.cuda.Stream()
     sec, times, mode = time_decode(w, args, stream)
     log("[bench] " + ", ".join(f"{k}: {v * 1e6:.1f} us per decode" for k, v in times.items())
         + f" (value: {mode})")
-    per_kernel_and_line(w, args, stream, sec, times, mode)
+    line = per_kernel_and_line(w, args, stream, sec, times, mode)
+    w.free()
+    del w
+    if args.sweep is None:
+        sweep = DEFAULT_SWEEP if args.workload == HEADLINE and not force else []
+    else:
+        sweep = [] if args.sweep == "none" else args.sweep.split(",")
+    if sweep:
+        sweep_ms, other_ms = sweep_workloads(sweep, args, stream)
+        if args.workload.startswith("n1e7_"):
+            sweep_ms[args.workload] = line["value"]
+        line["sweep_ms"] = dict(sorted(sweep_ms.items(), key=lambda kv: workload.CONFIGS[kv[0]].V))
+        if other_ms:
+            line["other_workloads_ms"] = other_ms
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+def sweep_workloads(names, args, stream):
+    """ms per decode of further workloads (own planner warm-up, own recorded
+    trajectory, same timing as the headline, fewer decodes).  Returns the
+    1e7-item codebook sweep and the other workloads separately."""
+    sweep_ms, other_ms = {}, {}
+    a2 = argparse.Namespace(**vars(args))
+    a2.steps = args.sweep_steps
+    a2.warmup = max(3, min(args.warmup, args.sweep_steps // 4))
+    for name in names:
+        w = Workload(name, args.plan_warmup, None)
+        sec, times, mode = time_decode(w, a2, stream)
+        proj = "".join("f" if c[0] == 1 else "s" for c in w.choices)
+        log(f"[sweep] {name}: {sec * 1e6:.1f} us per decode ({mode}; projections {proj})")
+        rec = round(sec * 1e3, 4)
+        (sweep_ms if name.startswith("n1e7_") else other_ms)[name] = rec
+        w.free()
+        del w
+    return sweep_ms, other_ms
 
 
 def time_decode(w, args, stream):
@@ -827,9 +938,7 @@ def per_kernel_and_line(w, args, stream, sec, times, mode):
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: 5 copies of {args.calibrate_copy} MiB")
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(line), flush=True)
+    return line
 
 
 if __name__ == "__main__":

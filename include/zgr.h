@@ -326,6 +326,31 @@ int32_t zgr_decode(zgr_plan* plan, zgr_hidden_fn hidden_fn, void* user, int32_t 
  * flag: ZGR_OK or ZGR_E_DEVICE; ZGR_E_HIP if the sync fails. */
 int32_t zgr_plan_status(zgr_plan* plan, void* stream);
 
+/* ---- full-projection kernel choice ------------------------------------------------------
+ * Which MFMA kernel the full projection of a step runs ("why fewer scores is
+ * not faster": dense steps compute every score and keep the legal columns).
+ * Host logic only (no HIP call), shared with the launcher, so tests and
+ * reports can list the kernels a workload runs.
+ *   M      beams in the step (B * k_in), V the codebook size
+ *   dtype  ZGR_F32 / ZGR_BF16 / ZGR_F16 (the tile choice does not depend on
+ *          it; it is checked and kept for future per-type rules)
+ *   fmt    the step table's ZGR_FMT_DENSE, ZGR_FMT_SPARSE or ZGR_FMT_DENSE_NEXT
+ *   mode   ZGR_MODE_* of the plan; n_cu the device's compute units
+ * Outputs (any may be NULL): kernel ZGR_GEMM_SMALL (16x16 MFMA over 32x32
+ * tiles, for few beams) or ZGR_GEMM_TILED (32x32 MFMA, tile_m x tile_n block
+ * tiles); epilogue ZGR_EPI_PLAIN (every column, token-indexed rows),
+ * ZGR_EPI_DENSE (legal columns at their legal rank) or ZGR_EPI_SLOT (sparse
+ * rows: legal columns at their slot).
+ * Errors: ZGR_E_ARG (non-positive sizes, unknown dtype, fmt or mode). */
+#define ZGR_GEMM_SMALL 0
+#define ZGR_GEMM_TILED 1
+#define ZGR_EPI_PLAIN 0
+#define ZGR_EPI_DENSE 1
+#define ZGR_EPI_SLOT 2
+int32_t zgr_full_projection_variant(int32_t M, int32_t V, int32_t dtype, int32_t fmt, int32_t mode,
+                                    int32_t n_cu, int32_t* kernel, int32_t* tile_m, int32_t* tile_n,
+                                    int32_t* epilogue);
+
 /* ---- per-kernel timing ------------------------------------------------------------------ */
 
 /* Kernel classes of a step, for zgr_plan_profile_read. */

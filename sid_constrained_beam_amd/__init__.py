@@ -121,6 +121,9 @@ def lib() -> ctypes.CDLL:
             "zgr_plan_profile": (_I32, [_P, _I32]),
             "zgr_plan_profile_read": (_I32, [_P, _I32, _I32, ctypes.POINTER(_I64),
                                              ctypes.POINTER(ctypes.c_double)]),
+            "zgr_full_projection_variant": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32,
+                                                   ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                                   ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -433,6 +436,21 @@ def zgr_decode(plan: Plan, hidden_fn: HiddenCallable, top_k: int, item_out, sid_
     cb = make_hidden_fn(hidden_fn)
     _check(lib().zgr_decode(plan.handle, cb, None, top_k, _dptr(item_out), _dptr(sid_out),
                             _dptr(score_out), _stream_ptr(stream)))
+
+
+GEMM_KERNELS = {0: "small", 1: "tiled"}
+EPILOGUES = {0: "plain", 1: "dense", 2: "slot"}
+
+
+def zgr_full_projection_variant(M: int, V: int, dtype: str, fmt: int, mode, n_cu: int = 256):
+    """The full-projection kernel the library launches for a step shape:
+    (kernel name, tile_m, tile_n, epilogue name).  Host only."""
+    k, tm, tn, ep = _I32(), _I32(), _I32(), _I32()
+    m = MODE_CODES[mode] if isinstance(mode, str) else int(mode)
+    _check(lib().zgr_full_projection_variant(int(M), int(V), DTYPE_CODES[dtype], int(fmt), m, int(n_cu),
+                                             ctypes.byref(k), ctypes.byref(tm), ctypes.byref(tn),
+                                             ctypes.byref(ep)))
+    return GEMM_KERNELS[k.value], tm.value, tn.value, EPILOGUES[ep.value]
 
 
 def zgr_plan_status(plan: Plan, stream=None):

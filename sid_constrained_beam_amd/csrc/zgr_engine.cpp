@@ -713,6 +713,23 @@ int32_t zgr_decode(zgr_plan* p, zgr_hidden_fn hidden_fn, void* user, int32_t top
   return read_device_flag(p, s);
 }
 
+int32_t zgr_full_projection_variant(int32_t M, int32_t V, int32_t dtype, int32_t fmt, int32_t mode,
+                                    int32_t n_cu, int32_t* kernel, int32_t* tile_m, int32_t* tile_n,
+                                    int32_t* epilogue) {
+  if (M < 1 || V < 1 || n_cu < 1) return fail(ZGR_E_ARG, "zgr_full_projection_variant: sizes must be >= 1");
+  if (dtype < ZGR_F32 || dtype > ZGR_F16) return fail(ZGR_E_ARG, "zgr_full_projection_variant: bad dtype");
+  if (fmt != ZGR_FMT_DENSE && fmt != ZGR_FMT_SPARSE && fmt != ZGR_FMT_DENSE_NEXT)
+    return fail(ZGR_E_ARG, "zgr_full_projection_variant: bad fmt");
+  if (mode < ZGR_MODE_FILTER_FIRST || mode > ZGR_MODE_UNCONSTRAINED)
+    return fail(ZGR_E_ARG, "zgr_full_projection_variant: bad mode");
+  const GemmVariant g = gemm_variant(M, V, fmt != ZGR_FMT_SPARSE, mode != ZGR_MODE_FILTER_FIRST, n_cu);
+  if (kernel) *kernel = g.kernel;
+  if (tile_m) *tile_m = g.tile_m;
+  if (tile_n) *tile_n = g.tile_n;
+  if (epilogue) *epilogue = g.epilogue;
+  return ZGR_OK;
+}
+
 int32_t zgr_plan_status(zgr_plan* p, void* stream) {
   if (!p) return fail(ZGR_E_ARG, "zgr_plan_status: null plan");
   return read_device_flag(p, (hipStream_t)stream);

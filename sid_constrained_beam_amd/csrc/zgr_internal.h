@@ -106,6 +106,14 @@ struct StepArgs {
 hipError_t launch_units(const StepArgs& a, hipStream_t s);
 hipError_t launch_selective_score(const StepArgs& a, hipStream_t s);
 hipError_t launch_full_projection(const StepArgs& a, hipStream_t s);
+// Which full-projection kernel, tile and epilogue a step shape gets (host
+// logic only; the launcher and zgr_full_projection_variant share it).
+struct GemmVariant {
+  int32_t kernel;    // ZGR_GEMM_*
+  int32_t tile_m, tile_n;
+  int32_t epilogue;  // ZGR_EPI_*
+};
+GemmVariant gemm_variant(int32_t M, int32_t V, bool dense, bool plain, int32_t n_cu);
 // true when the full projection of this step writes sparse rows by slot
 // (legal columns only, ldz = stride) rather than token-indexed rows (ldz = V)
 bool full_projection_slot_layout(const StepArgs& a);

@@ -1984,26 +1984,25 @@ template <int DT, bool NX>
 hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
   const int V = a.tab.V;
   const bool dense = a.tab.fmt == ZGR_FMT_DENSE || a.tab.fmt == ZGR_FMT_DENSE_NEXT;
-  const int compact = a.plain_z ? 0 : (dense ? 1 : (full_projection_slot_layout(a) ? 2 : 0));
-  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((V + bn - 1) / bn); };
+  const GemmVariant g = gemm_variant(a.M, V, dense, a.plain_z, a.n_cu);
+  const int compact = g.epilogue;  // ZGR_EPI_PLAIN / DENSE / SLOT = 0 / 1 / 2
 #define ZGR_GEMM(BM_, BN_, SP_)                                                                    \
   hipLaunchKernelGGL((k_gemm_nt<DT, BM_, BN_, NX, SP_>), dim3(GemmOrder(a.M, V, BM_, BN_).blocks()), \
                      dim3(kThreads), 0, s,                                                          \
                      a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in)
-  // the largest tile that still gives every compute unit two blocks (or one)
-  if (tiles(128, 128) >= 2 * a.n_cu) {
-    if (compact == 2)
+  if (g.kernel == ZGR_GEMM_TILED && g.tile_m == 128) {
+    if (compact == ZGR_EPI_SLOT)
       ZGR_GEMM(128, 128, true);
     else
       ZGR_GEMM(128, 128, false);
-  } else if (tiles(64, 64) >= a.n_cu) {
-    if (compact == 2)
+  } else if (g.kernel == ZGR_GEMM_TILED) {
+    if (compact == ZGR_EPI_SLOT)
       ZGR_GEMM(64, 64, true);
     else
       ZGR_GEMM(64, 64, false);
   } else {
-    hipLaunchKernelGGL((k_gemm_small<DT, NX>), dim3(tiles(32, 32)), dim3(kSmallThreads), 0, s, a.hidden, a.W, a.z,
-                       a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
+    hipLaunchKernelGGL((k_gemm_small<DT, NX>), dim3(((a.M + 31) / 32) * ((V + 31) / 32)), dim3(kSmallThreads), 0, s,
+                       a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
   }
 #undef ZGR_GEMM
   return hipGetLastError();
@@ -2011,12 +2010,36 @@ hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
 
 }  // namespace
 
+GemmVariant gemm_variant(int32_t M, int32_t V, bool dense, bool plain, int32_t n_cu) {
+  auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((V + bn - 1) / bn); };
+  GemmVariant g{};
+  // the largest tile that still gives every compute unit two blocks (or one);
+  // few beams (the first step) take the 16x16-MFMA kernel
+  if (tiles(128, 128) >= 2 * (int64_t)n_cu) {
+    g.kernel = ZGR_GEMM_TILED;
+    g.tile_m = g.tile_n = 128;
+  } else if (tiles(64, 64) >= n_cu) {
+    g.kernel = ZGR_GEMM_TILED;
+    g.tile_m = g.tile_n = 64;
+  } else {
+    g.kernel = ZGR_GEMM_SMALL;
+    g.tile_m = g.tile_n = 32;
+  }
+  // filter-first: dense rows keep their legal columns by legal rank; sparse
+  // rows by slot when the tiled kernels run (the few-beam kernel writes
+  // token-indexed rows there); the comparison modes keep every column
+  if (plain)
+    g.epilogue = ZGR_EPI_PLAIN;
+  else if (dense)
+    g.epilogue = ZGR_EPI_DENSE;
+  else
+    g.epilogue = g.kernel == ZGR_GEMM_TILED ? ZGR_EPI_SLOT : ZGR_EPI_PLAIN;
+  return g;
+}
+
 bool full_projection_slot_layout(const StepArgs& a) {
-  // sparse step, filter-first, and enough beams for the tiled kernels (the
-  // few-beam kernel writes token-indexed rows)
-  const bool sparse = a.tab.fmt == ZGR_FMT_SPARSE;
-  const int64_t t64 = (int64_t)((a.M + 63) / 64) * ((a.tab.V + 63) / 64);
-  return sparse && !a.plain_z && t64 >= a.n_cu;
+  const bool dense = a.tab.fmt == ZGR_FMT_DENSE || a.tab.fmt == ZGR_FMT_DENSE_NEXT;
+  return gemm_variant(a.M, a.tab.V, dense, a.plain_z, a.n_cu).epilogue == ZGR_EPI_SLOT;
 }
 
 bool supported_hidden_size(int d) {

@@ -154,10 +154,19 @@ def run_gpu_step(setup, plan, t, prefixes, cum, B, K, requests, with_dbg=True, m
 
 
 def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests=None,
-               mode="filter_first"):
+               mode="filter_first", diag=None):
     """Step check against the oracle (in the same mode) on identical inputs
     (all requests, or the listed ones).  Returns the number of requests whose
-    K-th score boundary was ambiguous."""
+    K-th score boundary was ambiguous.
+
+    diag (a dict, optional) collects diagnostics beside the protocol, without
+    loosening it: the largest |logp_gpu - logp_oracle| over the checked legal
+    slots and |cum_out - oracle score| over the picks ("max_dlogp",
+    "max_dscore"), and a second, tight selection check: with the band set to
+    ten times the error this request-step actually shows (at least 8 ulps of
+    the K-th score), a request whose K-th boundary is unambiguous at that band
+    must pick exactly the oracle's candidates ("tight_exact" counts them,
+    "tight_ambiguous" the others)."""
     cfg = setup.cfg
     M = len(cum)
     k_in = M // B
@@ -170,6 +179,7 @@ def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests
         pq = prefixes[sl, : t - 1] if t > 1 else np.zeros((k_in, 0), np.int32)
         cq = np.asarray(cum[sl], np.float64)
         res = setup.cat.step(t, setup.W_f32[t - 1], pq, cq, out["h32"][sl], K, mode)
+        err_q = 0.0  # largest log-prob / score error seen in this request-step
         # (i) legal slots and their log-probs
         if check_dbg and out["dbg"] is not None:
             dbg = out["dbg"][q] if isinstance(out["dbg"], dict) else out["dbg"][sl]
@@ -183,6 +193,7 @@ def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests
                 assert np.array_equal(got_legal, np.sort(legal_slots)), (q, k, got_legal[:10], legal_slots[:10])
                 err = np.abs(row[legal_slots] - lp)
                 assert err.max(initial=0) <= tol, (q, k, err.max())
+                err_q = max(err_q, float(err.max(initial=0)))
         # (ii) selection by the band protocol
         scores = {(int(b), int(v)): s for b, v, s in zip(res.cand_beam, res.cand_token, res.cand_score)}
         allv = np.sort(np.fromiter(scores.values(), np.float64))[::-1]
@@ -202,6 +213,7 @@ def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests
             assert key in scores, ("illegal pick", q, key)
             s = scores[key]
             assert abs(cumo[i] - s) <= tol, (q, i, cumo[i], s)
+            err_q = max(err_q, abs(float(cumo[i]) - s))
             if unc:
                 assert rowo[i] == 0, (q, i)
             else:
@@ -215,12 +227,23 @@ def check_step(setup, t, prefixes, cum, out, B, K, tol, check_dbg=True, requests
         assert np.all(picks >= tau - tol)
         assert np.all(np.diff(picks) <= 2 * tol)
         band = sum(1 for s in scores.values() if abs(s - tau) <= tol)
+        want = list(zip(res.sel_beam.tolist(), res.sel_token.tolist()))
+        got = [(int(par[i]) - q * k_in, int(tok[i])) for i in range(kk)]
         if band == 1:
-            want = list(zip(res.sel_beam.tolist(), res.sel_token.tolist()))
-            got = [(int(par[i]) - q * k_in, int(tok[i])) for i in range(kk)]
             assert set(got) == set(want), (q, "selection differs without ambiguity")
         else:
             ambiguous += 1
+        if diag is not None:
+            diag["max_dlogp"] = max(diag.get("max_dlogp", 0.0), err_q if check_dbg else 0.0)
+            diag["max_dscore"] = max(diag.get("max_dscore", 0.0),
+                                     max(abs(float(cumo[i]) - scores[g]) for i, g in enumerate(got)))
+            tight = max(10.0 * err_q, 8.0 * float(np.spacing(np.float32(abs(tau)))))
+            diag["tight_band_max"] = max(diag.get("tight_band_max", 0.0), tight)
+            if len(allv) > kk and allv[kk - 1] - allv[kk] <= tight:
+                diag["tight_ambiguous"] = diag.get("tight_ambiguous", 0) + 1
+            else:
+                assert set(got) == set(want), (q, "selection differs at ten times the observed error")
+                diag["tight_exact"] = diag.get("tight_exact", 0) + 1
     return ambiguous
 
 

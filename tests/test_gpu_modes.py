@@ -8,19 +8,11 @@ import pytest
 
 import gpu_util as gu
 import sid_constrained_beam_amd as zgr
-from workload import CONFIGS
+from cases import MODE_CASES
 
 pytestmark = pytest.mark.gpu
 
-CASES = {
-    "n1e4_v256": CONFIGS["n1e4_v256"],
-    "n1e6_v2048_small": CONFIGS["n1e6_v2048"].scaled(N=100_000, B=4, K=32),
-    "n1e7_v2048_small": CONFIGS["n1e7_v2048"].scaled(N=300_000, B=3, K=24),
-    "n5e7_v1024_dense_small": CONFIGS["n5e7_v1024_dense"].scaled(N=500_000, B=2, K=40),
-    # 16 beams x 16384 tokens per request: a part holds one beam, more
-    # candidates than its key array, so keys are recomputed from the scores
-    "n1e8_v16384_small": CONFIGS["n1e8_v16384"].scaled(N=200_000, B=2, K=16),
-}
+CASES = MODE_CASES
 MODES = ["score_first", "unconstrained"]
 
 _setups = {}

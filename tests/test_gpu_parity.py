@@ -13,22 +13,15 @@ import pytest
 import gpu_util as gu
 import sid_constrained_beam_amd as zgr
 import workload
+from cases import NEXT_CASES, PARITY_CASES
 from workload import CONFIGS
 
 pytestmark = pytest.mark.gpu
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
-# Reduced versions of every precision / table-format mix (same L, V, d, dtype
-# and catalog law as the named workload, fewer items, requests and beams).
-CASES = {
-    "n1e4_v256": CONFIGS["n1e4_v256"],
-    "n1e6_v2048": CONFIGS["n1e6_v2048"],
-    "n1e7_v2048_small": CONFIGS["n1e7_v2048"].scaled(N=300_000, B=4, K=32),
-    "n1e7_v16384_small": CONFIGS["n1e7_v16384"].scaled(N=300_000, B=3, K=24),
-    "n5e7_v1024_dense_small": CONFIGS["n5e7_v1024_dense"].scaled(N=2_000_000, B=3, K=40),
-    "n1e8_v16384_small": CONFIGS["n1e8_v16384"].scaled(N=1_000_000, B=2, K=48),
-}
+# Reduced versions of every precision / table-format mix (tests/cases.py).
+CASES = PARITY_CASES
 
 _setups = {}
 
@@ -291,13 +284,6 @@ def test_naive_baseline_matches_padded_slots():
     assert same > 0.99, same
     ok = np.isfinite(outs["selective"][1])
     assert np.allclose(outs["selective"][1][ok], outs["naive"][1][ok], atol=1e-4, rtol=0)
-
-
-NEXT_CASES = {
-    "n1e6_v2048": ["N", "N", "S"],
-    "n1e7_v2048_small": ["N", "N", "S", "S"],
-    "n5e7_v1024_dense_small": ["N", "N", "S", "S"],
-}
 
 
 @pytest.mark.parametrize("proj", ["selective", "full"])
