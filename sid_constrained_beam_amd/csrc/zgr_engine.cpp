@@ -61,6 +61,7 @@ struct zgr_plan {
   float* lse = nullptr;
   uint64_t* part_keys = nullptr;
   int32_t* part_cnt = nullptr;
+  float2* part_ms = nullptr;
   int32_t* err = nullptr;
   int32_t* err_host = nullptr;  // pinned copy of the flag, read after one stream sync
   // decode state: double-buffered beams and prefixes, hidden vectors, outputs
@@ -159,6 +160,7 @@ StepArgs make_args(zgr_plan* p, int32_t t, const void* hidden, const int32_t* ro
   a.parts = 1;
   a.part_keys = p->part_keys;
   a.part_cnt = p->part_cnt;
+  a.part_ms = p->part_ms;
   a.err = p->err;
   a.n_cu = p->n_cu;
   return a;
@@ -217,22 +219,28 @@ bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
   return bytes <= (double)(1 << 20);
 }
 
-// Blocks per request for the request kernel.  A request whose candidates are
-// many (a dense or full-projection step, or a heavy sparse one) is split over
-// several blocks so that more compute units stream its scores, then merged;
-// light requests stay whole (one launch).
-int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool heavy_step) {
-  if (a.k_in < 2) return 1;
+// Blocks per request for the request kernel.  A request with many candidates
+// is split over several blocks, each taking an equal share of its flat
+// candidate list (a beam may span blocks), then merged; a request of at most
+// kSmallRequest candidates (estimated from the table's mean row) stays whole,
+// since below that a split does not pay for the merge launch.  Enough parts
+// that a part's keys fit the LDS key array with room for requests above the
+// mean; beyond that, as many as one round of blocks at two per compute unit
+// takes, but parts of at least kPartMinCandidates; the parts' best K keys must
+// fit the merge's LDS.
+constexpr double kPartMinCandidates = 2048.0;
+constexpr double kSmallRequest = 6144.0;
+int32_t request_parts(const zgr_plan* p, const StepArgs& a) {
   const HostTable& h = p->idx->host[a.t - 1];
   double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
   if (a.tab.fmt == kFmtAll) mean_n = p->V;
   const double est_c = a.k_in * std::min<double>(mean_n, a.tab.stride);
-  if (!heavy_step && est_c <= 2048.0) return 1;
-  // enough parts to cover the compute units, and enough that a part's
-  // candidates (estimated) fit the LDS key array
-  int P = std::max(1, p->n_cu / std::max(1, a.B));
-  P = std::max(P, (int)std::ceil(est_c / (0.75 * kSelCapHost)));
-  P = std::min({P, a.k_in, kMaxParts, kSelCapHost / std::max(1, a.K)});
+  if (est_c <= kSmallRequest) return 1;
+  const int p_fit = (int)std::ceil(est_c / (0.6 * kKeyCapHost));
+  const int p_occ = std::max(1, 2 * p->n_cu / std::max(1, a.B));
+  const int p_size = std::max(1, (int)std::ceil(est_c / kPartMinCandidates));
+  int P = std::max(p_fit, std::min(p_occ, p_size));
+  P = std::min({P, kMaxParts, kMergeCapHost / std::max(1, a.K)});
   return std::max(1, P);
 }
 
@@ -259,7 +267,8 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
       if (e != hipSuccess) return hip_fail(e, "codebook log-sum-exp launch");
     }
     zmode = unc ? 1 : 0;
-    a.parts = request_parts(p, a, true);
+    a.z_token = zmode == 0;
+    a.parts = request_parts(p, a);
     e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
     if (e != hipSuccess) return hip_fail(e, "request step launch");
     if (a.parts > 1) {
@@ -323,7 +332,8 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     if (e != hipSuccess) return hip_fail(e, "selective score launch");
     zmode = 1;
   }
-  a.parts = request_parts(p, a, proj == ZGR_PROJ_FULL || dense);
+  a.z_token = zmode == 0;
+  a.parts = request_parts(p, a);
   e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
   if (e != hipSuccess) return hip_fail(e, "request step launch");
   if (a.parts > 1) {
@@ -516,6 +526,7 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   A((void**)&p->lse, (size_t)MK * 4);
   A((void**)&p->part_keys, (size_t)B * kMaxParts * K * 8);
   A((void**)&p->part_cnt, (size_t)B * kMaxParts * 4);
+  A((void**)&p->part_ms, (size_t)B * kMaxParts * 8);
   A((void**)&p->err, 4);
   A(&p->hidden, (size_t)MK * d * elem_size(dtype));
   for (int i = 0; i < 2; ++i) {

@@ -96,9 +96,11 @@ struct StepArgs {
   float* lse;           // [M] per-beam log-sum-exp over legal tokens
   float* lse_ext;       // [M] or null: normaliser given to the request kernel (score-first)
   bool plain_z;         // full projection writes token-indexed rows even on dense steps
+  bool z_token;         // the request kernel reads token-indexed score rows (zmode 0)
   int32_t parts;        // blocks per request in the request kernel (1 = no merge)
   uint64_t* part_keys;  // [B * parts][K] best keys of each part
   int32_t* part_cnt;    // [B * parts]
+  float2* part_ms;      // [B * parts] single-beam parts: (max, sum of exp) of their range
   int32_t* err;         // device error flag
   int32_t n_cu;
 };
@@ -118,9 +120,10 @@ GemmVariant gemm_variant(int32_t M, int32_t V, bool dense, bool plain, int32_t n
 // (legal columns only, ldz = stride) rather than token-indexed rows (ldz = V)
 bool full_projection_slot_layout(const StepArgs& a);
 // zmode: 0 = z token-indexed, 1 = z slot-indexed, 2 = score inside the request kernel.
-// With a.parts > 1 each request is split over a.parts blocks, then merged.
-constexpr int kMaxParts = 32;
-constexpr int kSelCapHost = 14336;  // candidates whose keys fit the request kernel's LDS
+// With a.parts > 1 each request's candidates are split over a.parts blocks, then merged.
+constexpr int kMaxParts = 64;
+constexpr int kKeyCapHost = 5120;     // candidates of a request part whose keys fit the request kernel's LDS
+constexpr int kMergeCapHost = 14336;  // part keys (parts x K) the merge holds in LDS
 hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s);
 // after launch_request_step with a.parts > 1: the per-request merge of the parts
 hipError_t launch_request_merge(const StepArgs& a, hipStream_t s);

@@ -714,7 +714,12 @@ __global__ __launch_bounds__(kThreads) void k_naive_dot(const void* __restrict__
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelCap = kSelCapHost;  // candidates of a request whose keys fit in LDS (112 KiB)
+constexpr int kKeyCap = kKeyCapHost;      // candidates of a part whose keys fit in LDS (40 KiB: two
+                                          // blocks per compute unit)
+constexpr int kMergeCap = kMergeCapHost;  // the parts' best keys a merge holds in LDS (112 KiB)
+// unit partials of the log-sum-exp pass that fit beside the unit prefix in the
+// selection's LDS (before the selection needs it)
+constexpr int kUnitCap = 1400;
 constexpr int kMaxK = 1024;
 
 // Distance histogram: 64 exact bins for distances below 64 ulps, then 64
@@ -749,61 +754,80 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
   m = mn;
 }
 
-// One block per request (or per part of a request), the step after scoring:
-//   1. each beam's row of table t, legal count and row base; prefixes over the
-//      block's beams of candidates (candidate f = beam, legal rank) and of
-//      work items (sparse: candidates; dense: bitmap words);
-//   2. (kZScore) z = W_t[token] . h_beam for every legal candidate, the weight
-//      row read in place by a lane group;
-//   3. legal-only log-sum-exp of every beam (online max / sum of exp, fixed
-//      order; several waves per beam when the block has few beams); when the
-//      block's candidates fit in LDS the same pass leaves each one's
-//      (z, beam*S + slot) in keys[] at its flat index;
+// One block per part of a request, the step after scoring.  A request's
+// candidates are numbered flat: beams in rank order, each beam's candidates in
+// slot order (sparse: legal rank; dense: token order, z stored by legal rank).
+// Part p of P takes the flat range [Cq p / P, Cq (p + 1) / P) of the request's
+// Cq candidates, so parts carry equal work however unevenly the legal tokens
+// fall on the beams, and one beam may span several parts:
+//   1. every beam of the request: row of table t, legal count, row base,
+//      cumulative score; the candidate prefix over the beams;
+//   2. (kZScore) z = W_t[token] . h_beam for the candidates of the beams this
+//      part touches, the weight row read in place by a lane group;
+//   3. legal-only log-sum-exp of those beams over all their candidates (also
+//      the ones in neighbouring parts): every beam is cut into units of SEG
+//      candidates counted from its first candidate (SEG depends only on the
+//      request), a 16-lane group reduces a unit with contiguous loads to an
+//      online (max, sum of exp), and one wave joins a beam's units in a fixed
+//      butterfly, so every part that touches a beam computes the same value;
+//      the same pass leaves the part's (z, beam*S + slot) in keys[] when they
+//      fit in LDS;
 //   4. cand = cum + (z - lse) as a 64-bit key (ord(cand), ~(beam*S + slot));
 //      the K largest through a distance histogram (in LDS, or by passes over
 //      z when they do not fit);
-//   5. a part hands its best K to the merge; otherwise sort by rank counting,
-//      decode and advance: next row = row_ptr[r] + slot (sparse: the position
-//      is the next row) or row_ptr[r] + legal rank (dense); prefix gather.
+//   5. with P > 1 a part hands its best K to the merge (MODE kZParts, one
+//      block per request); otherwise sort by rank counting, decode and
+//      advance: next row = row_ptr[r] + slot (sparse: the position is the
+//      next row) or row_ptr[r] + legal rank (dense); prefix gather.
 // Scores z[b][j] are stored by legal rank j on sparse selective steps and on
-// every dense step; after a full projection of a sparse step they are
-// token-indexed (kZToken).  On dense rows the token of rank j is the row's
-// j-th set bit; the rank directory gives each word's first rank.
+// every dense step; after a full projection of a sparse step, and in the
+// score-first comparison, they are token-indexed (kZToken).  On dense rows
+// the token of rank j is the row's j-th set bit; the rank directory gives each
+// word's first rank.
+// The part kernels of heavy steps (scores already in z) are compiled for 8
+// waves per SIMD, i.e. two 1024-thread blocks per compute unit (their LDS
+// allows two); left to itself the compiler takes about 106 scalar registers,
+// which leaves room for 7 waves and so one block.
+constexpr int request_waves_per_eu(int mode) { return (mode == kZToken || mode == kZSlot) ? 8 : 1; }
+
 template <int MODE, int DT, int D, bool NX>
-__global__ __launch_bounds__(kSelThreads) void k_request_step(
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(request_waves_per_eu(MODE))))
+void k_request_step(
     DevTable tab, int32_t t, int32_t L, int32_t k_in, int32_t K, const int32_t* __restrict__ row_in,
     const float* __restrict__ cum_in, const void* __restrict__ hidden, const void* __restrict__ W,
     float* __restrict__ z, int64_t ldz, int32_t P, uint64_t* __restrict__ part_keys,
-    int32_t* __restrict__ part_cnt, int32_t* __restrict__ parent_out,
+    int32_t* __restrict__ part_cnt, float2* __restrict__ part_ms, int32_t* __restrict__ parent_out,
     int32_t* __restrict__ token_out, int32_t* __restrict__ row_out, float* __restrict__ cum_out,
     const int32_t* __restrict__ prefix_in, int32_t* __restrict__ prefix_out,
-    float* __restrict__ slot_dbg, const float* __restrict__ lse_ext, int32_t* __restrict__ err) {
+    float* __restrict__ slot_dbg, const float* __restrict__ lse_ext, int32_t ztok,
+    int32_t* __restrict__ err) {
   constexpr int NT = kSelThreads;
   constexpr bool TOKEN_IDX = (MODE == kZToken);
   constexpr bool MERGE = (MODE == kZParts);
-  __shared__ uint64_t keys[kSelCap];
-  __shared__ uint64_t sel[kMaxK];
-  __shared__ int pre[kMaxK + 1];   // work-item prefix over the block's beams
-  __shared__ int cpre[kMaxK + 1];  // candidate prefix over the block's beams
+  __shared__ uint64_t keys[MERGE ? kMergeCap : kKeyCap];
+  // sel (the selection) and dhist (the distance histogram, then the boundary
+  // keys) from phase 4 on; before that the log-sum-exp pass keeps its unit
+  // partials and the unit prefix over the beams here
+  __shared__ __attribute__((aligned(16))) uint64_t selhist[kMaxK + kDistBins / 2];
+  uint64_t* sel = selhist;
+  int* dhist = reinterpret_cast<int*>(selhist + kMaxK);
+  float2* upart = reinterpret_cast<float2*>(selhist);             // [kUnitCap]
+  int* upre = reinterpret_cast<int*>(selhist + kUnitCap);          // [kMaxK + 1]
+  __shared__ int cpre[kMaxK + 1];  // candidate prefix over the request's beams
   __shared__ int brow[kMaxK];
   __shared__ int bbase[kMaxK];
   __shared__ float bcum[kMaxK];
   __shared__ float blse[kMaxK];
-  __shared__ float pm[kSelWaves], ps[kSelWaves];
-  __shared__ __attribute__((aligned(16))) int dhist[kDistBins];
+  __shared__ int mpre[kMaxParts + 1], mcn[kMaxParts];  // merge: the parts' key counts and prefix
   __shared__ int hist[256];
   __shared__ int sh[kSelWaves];
-  __shared__ int pos, pos2, pick_bin, pick_above;
+  __shared__ int pos, pos2, pick_bin, pick_above, bl_lo_sh, bl_hi_sh, multi_sh;
+  __shared__ float pm[kSelWaves], ps[kSelWaves];
+  __shared__ float2 zms_sh;  // single-beam part: (max, sum of exp) of its own range
   __shared__ unsigned int omax_sh;
-  // P > 1: block (q, p) takes beams [blo, blo + nloc) of request q and
-  // leaves its best K keys in part_keys; the merge (MODE kZParts) picks the
-  // request's best K among the parts' keys.
   const int q = MERGE ? blockIdx.x : blockIdx.x / P;
   const int part = MERGE ? 0 : blockIdx.x - q * P;
-  const int kp = (k_in + P - 1) / P;
-  const int blo = MERGE ? 0 : min(k_in, part * kp);
-  const int nloc = MERGE ? k_in : min(k_in, blo + kp) - blo;
-  const int b0 = q * k_in + blo;
+  const int b0 = q * k_in;  // the request's first beam
   const bool dense = tab.fmt != ZGR_FMT_SPARSE;
   const bool all_legal = tab.fmt == kFmtAll;
   const uint32_t S = (uint32_t)tab.stride;
@@ -812,25 +836,29 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   // 0. the merge's part counts and first keys: their addresses are known
   //    before the beams' rows, so they overlap the row lookups below
   constexpr int U = 8;  // phase-3 loads issued together per thread
-  int LPB = 1;          // phase-3 threads per beam
-  while (LPB < NT && LPB * 2 * max(nloc, 1) <= NT) LPB *= 2;
+  // a single-beam request split over parts selects by the score alone (cand
+  // is monotone in z within a beam): each part reduces only its own range to
+  // a (max, sum of exp) partial, and the merge joins the partials into the
+  // normaliser (fixed order) and forms the cumulative scores
+  const bool zkey = k_in == 1 && P > 1;
   int mcnt = 0;
   uint64_t mkey0 = 0;
+  float2 mms = make_float2(-INFINITY, 0.f);
   if constexpr (MERGE) {
     if ((int)threadIdx.x < P) mcnt = part_cnt[q * P + threadIdx.x];
+    if (zkey && (int)threadIdx.x < P) mms = part_ms[q * P + threadIdx.x];
     if ((int)threadIdx.x < P * K) mkey0 = part_keys[(int64_t)q * P * K + threadIdx.x];
   }
 
-  // 1. the block's beams
-  int cnt = 0, items = 0;
-  if ((int)threadIdx.x < nloc) {
+  // 1. the request's beams
+  int cnt = 0;
+  if ((int)threadIdx.x < k_in) {
     int r = row_in[b0 + threadIdx.x];
     if (all_legal && r > 0) r = 0;  // every live beam has the one all-legal row
     int base = 0;
     if (r >= 0 && r < tab.rows) {
       base = tab.row_ptr[r];
-      cnt = MERGE ? 0 : tab.row_ptr[r + 1] - base;
-      items = dense ? (cnt > 0 ? tab.words : 0) : cnt;
+      cnt = tab.row_ptr[r + 1] - base;
     } else {
       if (r >= tab.rows && !MERGE) atomicOr(err, 1);
       r = -1;
@@ -839,48 +867,76 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     bbase[threadIdx.x] = base;
     bcum[threadIdx.x] = cum_in[b0 + threadIdx.x];
   }
-  int T, C;
-  const int ex = block_excl_scan<NT>(items, sh, &T);
-  if ((int)threadIdx.x < nloc) pre[threadIdx.x] = ex;
-  const int exc = block_excl_scan<NT>(cnt, sh, &C);
-  if ((int)threadIdx.x < nloc) cpre[threadIdx.x] = exc;
+  int Cq;
+  const int exc = block_excl_scan<NT>(cnt, sh, &Cq);
+  if ((int)threadIdx.x < k_in) cpre[threadIdx.x] = exc;
+  // 2. this part's candidates [f0, f1) and the beams they fall on
+  //    [bl_lo, bl_hi]: the beams holding f0 and f1 - 1 say so themselves
+  const int f0 = MERGE ? 0 : (int)((int64_t)Cq * part / P);
+  const int f1 = MERGE ? 0 : (int)((int64_t)Cq * (part + 1) / P);
+  if (cnt > 0 && exc <= f0 && f0 < exc + cnt) bl_lo_sh = threadIdx.x;
+  if (cnt > 0 && exc <= f1 - 1 && f1 - 1 < exc + cnt) bl_hi_sh = threadIdx.x;
+  // units of the log-sum-exp pass: SEG candidates from each beam's first,
+  // reduced by GL lanes with UL loads each per pass; GL follows the
+  // request's mean legal count (1 lane for the one or two legal tokens of a
+  // late step, 16 for rows of hundreds) and SEG = GL * UL * 2^s is the
+  // smallest that keeps any part's units within kUnitCap.  Both depend only
+  // on the request, so every part reduces a beam the same way.
+  constexpr int UL = 8;
+  const int mean_n = Cq / max(1, k_in);
+  const int GL = mean_n >= 64 ? 16 : (mean_n >= 8 ? 4 : 1);
+  int SEG = GL * UL;
+  while ((Cq + SEG - 1) / SEG + k_in > kUnitCap) SEG *= 2;
+  if constexpr (!MERGE) {
+    int Uq;
+    const int uex = block_excl_scan<NT>((cnt + SEG - 1) / SEG, sh, &Uq);
+    if ((int)threadIdx.x < k_in) upre[threadIdx.x] = uex;
+    if (threadIdx.x == 0) upre[k_in] = Uq;
+  }
   if (threadIdx.x == 0) {
-    pre[nloc] = T;
-    cpre[nloc] = C;
+    cpre[k_in] = Cq;
     pos = 0;
+    multi_sh = 0;
     omax_sh = 0u;
+    zms_sh = make_float2(-INFINITY, 0.f);
   }
   __syncthreads();
-  auto beam_of = [&](const int* pf, int f) {  // last beam with pf[b] <= f
-    int lo = 0, hi = nloc;
+  auto beam_of = [&](int f) {  // the beam of flat candidate f < Cq: last b with cpre[b] <= f
+    int lo = 0, hi = k_in;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (pf[mid] <= f)
+      if (cpre[mid] <= f)
         lo = mid;
       else
         hi = mid;
     }
     return lo;
   };
-  bool store = C <= kSelCap;
+  //    (and all those beams' candidates [e0, e1))
+  int C = f1 - f0;
+  const int bl_lo = C > 0 ? bl_lo_sh : 0;
+  const int bl_hi = C > 0 ? bl_hi_sh : -1;
+  const int e0 = C > 0 ? cpre[bl_lo] : 0, e1 = C > 0 ? cpre[bl_hi + 1] : 0;
+  bool store = C <= kKeyCap;
+  auto code_of = [&](int b, int slot) { return (uint32_t)b * S + (uint32_t)slot; };
 
-  // 2. selective projection inside the block: U2 candidates per lane group
-  //    with their token and row loads issued together; z goes to its slot and,
-  //    when the block's candidates fit in LDS, to keys[] as (z, beam*S + slot)
+  //    (kZScore) selective projection inside the block: U2 candidates per
+  //    lane group with their token and row loads issued together; z goes to
+  //    its slot and, for this part's candidates, to keys[]
   if constexpr (MODE == kZScore) {
     using Sh = SelShape<DT, D>;
     constexpr int G = Sh::G, NV = Sh::NV, VEC = Sh::VEC, ES = Sh::ES;
     constexpr int NGB = NT / G;
-    constexpr int U2 = 2;
+    constexpr int U2 = NV <= 8 ? 2 : 1;  // two candidates' rows in flight unless that spills
     const int gl = threadIdx.x % G, grp = threadIdx.x / G;
-    for (int f0 = grp; f0 < C; f0 += NGB * U2) {
+    for (int f00 = e0 + grp; f00 < e1; f00 += NGB * U2) {
       int bls[U2], js[U2], toks[U2];
 #pragma unroll
       for (int u = 0; u < U2; ++u) {
-        const int f = f0 + u * NGB;
-        bls[u] = f < C ? beam_of(cpre, f) : 0;
-        js[u] = f < C ? f - cpre[bls[u]] : 0;
-        toks[u] = f < C ? (int)tab.tok[bbase[bls[u]] + js[u]] : 0;
+        const int f = f00 + u * NGB;
+        bls[u] = f < e1 ? beam_of(f) : bl_lo;
+        js[u] = f < e1 ? f - cpre[bls[u]] : 0;
+        toks[u] = f < e1 ? (int)tab.tok[bbase[bls[u]] + js[u]] : 0;
       }
       float acc[U2];
 #pragma unroll
@@ -903,12 +959,11 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
 #pragma unroll
       for (int u = 0; u < U2; ++u) {
         acc[u] = group_sum<G>(acc[u]);
-        const int f = f0 + u * NGB;
-        if (gl == 0 && f < C) {
+        const int f = f00 + u * NGB;
+        if (gl == 0 && f < e1) {
           z[(int64_t)(b0 + bls[u]) * ldz + js[u]] = acc[u];
-          if (store)
-            keys[f] = ((uint64_t)__float_as_uint(acc[u]) << 32) |
-                      ((uint32_t)(blo + bls[u]) * S + (uint32_t)js[u]);
+          if (store && f >= f0 && f < f1)
+            keys[f - f0] = ((uint64_t)__float_as_uint(acc[u]) << 32) | code_of(bls[u], js[u]);
         }
       }
     }
@@ -920,103 +975,65 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   // LPW grows while the pairs leave threads idle, so a full row at the first
   // step needs no long serial walks.  The first round's bitmap words are
   // loaded now so that phase 3 hides their latency.
+  const int nbl = bl_hi - bl_lo + 1;  // beams this part touches (0 when C = 0)
   const bool code_pass = !MERGE && dense && store && !TOKEN_IDX;
-  const int pairs = nloc * tab.words;
+  const int pairs = nbl * tab.words;
   int LPW = 1;
   while (LPW < 32 && pairs * LPW * 2 <= NT) LPW *= 2;
   DWord dwpf{0u, 0};
   if (code_pass && (int)threadIdx.x < pairs * LPW) {
-    const int pr = threadIdx.x / LPW, bl = pr / tab.words, w = pr - bl * tab.words;
+    const int pr = threadIdx.x / LPW, bl = bl_lo + pr / tab.words, w = pr % tab.words;
     if (brow[bl] >= 0) dwpf = dense_word<NX>(tab, brow[bl], w);
   }
 
-  // 3. legal-only log-sum-exp of every beam, LPB threads per beam
+  // 3. legal-only log-sum-exp of the beams bl_lo..bl_hi over [e0, e1)
+  auto final_lse = [&](int b, float m, float s) {
+    const float l = lse_ext ? lse_ext[b0 + b] : m + __logf(s);
+    blse[b] = l;
+    // best candidate of the beam (cand is monotone in z within a beam)
+    atomicMax(&omax_sh, ord_of(bcum[b] + (m - l)));
+  };
   if constexpr (!MERGE) {
-    const int bl3 = threadIdx.x / LPB, lb = threadIdx.x - bl3 * LPB;
-    const int r3 = (bl3 < nloc) ? brow[bl3] : -1;
-    const float* z3 = z + (int64_t)(b0 + (bl3 < nloc ? bl3 : 0)) * ldz;
-    const int at = (bl3 < nloc) ? cpre[bl3] : 0;
-    const int n3 = (r3 >= 0) ? cpre[bl3 + 1] - at : 0;
-    const uint32_t code0 = (uint32_t)(blo + bl3) * S;
-    float m = -INFINITY, s = 0.f;
-    auto acc_lse = [&](float zv) {
-      if (zv > m) {
-        s = s * __expf(m - zv) + 1.f;
-        m = zv;
-      } else {
-        s += __expf(zv - m);
-      }
-    };
-    if (r3 >= 0) {
-      if (MODE == kZScore && store) {
-        // the projection left the scores in keys[]
-        for (int j = lb; j < n3; j += LPB) acc_lse(__uint_as_float((uint32_t)(keys[at + j] >> 32)));
-      } else if (!dense) {
-        for (int j0 = lb; j0 < n3; j0 += LPB * U) {
-          float zv[U];
+    if (zkey && !(TOKEN_IDX && dense)) {
+      // this part's own range only, coalesced, with its keys' scores
+      float m = -INFINITY, s = 0.f;
+      const float* zb = z + (int64_t)b0 * ldz;
+      for (int i0 = threadIdx.x; i0 < C; i0 += NT * U) {
+        float zv[U];
+        int tk[U];
+        if constexpr (TOKEN_IDX) {
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            const int j = j0 + u * LPB;
-            if (j < n3)
-              zv[u] = TOKEN_IDX ? z3[tab.tok[bbase[bl3] + j]] : z3[j];
+            const int i = i0 + u * NT;
+            tk[u] = i < C ? (int)tab.tok[bbase[0] + f0 + i] : 0;
           }
+        }
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int j = j0 + u * LPB;
-            if (j < n3) {
-              acc_lse(zv[u]);
-              if (store) keys[at + j] = ((uint64_t)__float_as_uint(zv[u]) << 32) | (code0 + (uint32_t)j);
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * NT;
+          if (i < C) {
+            if (MODE == kZScore && store)
+              zv[u] = __uint_as_float((uint32_t)(keys[i] >> 32));
+            else
+              zv[u] = zb[TOKEN_IDX ? tk[u] : f0 + i];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * NT;
+          if (i < C) {
+            const float x = zv[u];
+            if (x > m) {
+              s = s * __expf(m - x) + 1.f;
+              m = x;
+            } else {
+              s += __expf(x - m);
             }
-          }
-        }
-      } else if (TOKEN_IDX) {
-        // dense, token-indexed scores: walk the row's bitmap words; a set
-        // bit's legal rank is the word's directory entry plus the bits below
-        for (int w = lb; w < tab.words; w += LPB) {
-          const DWord dw = dense_word<NX>(tab, r3, w);
-          uint32_t x = dw.bits;
-          int j = at + dw.rank;
-          while (x) {
-            const int v = (w << 5) + __ffs(x) - 1;
-            x &= x - 1;
-            const float zv = z3[v];
-            acc_lse(zv);
-            if (store) keys[j] = ((uint64_t)__float_as_uint(zv) << 32) | (code0 + (uint32_t)v);
-            ++j;
-          }
-        }
-      } else {
-        // dense: scores by legal rank; the token of rank j is the j-th set bit
-        for (int j0 = lb; j0 < n3; j0 += LPB * U) {
-          float zv[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int j = j0 + u * LPB;
-            if (j < n3) zv[u] = z3[j];
-          }
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int j = j0 + u * LPB;
-            if (j < n3) {
-              acc_lse(zv[u]);
-              if (store) keys[at + j] = (uint64_t)__float_as_uint(zv[u]) << 32;  // code after the barrier
-            }
+            if (MODE != kZScore && store)
+              keys[i] = ((uint64_t)__float_as_uint(x) << 32) | (dense ? 0u : code_of(0, f0 + i));
           }
         }
       }
-    }
-    if (LPB <= 64) {
-      xor_down_width(LPB, [&](auto o) {
-        constexpr int X = decltype(o)::value;
-        lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
-      });
-      if (lb == 0 && bl3 < nloc) {
-        const float l = lse_ext ? lse_ext[b0 + bl3] : m + __logf(s);
-        blse[bl3] = l;
-        // best candidate of the beam (cand is monotone in z within a beam)
-        if (r3 >= 0) atomicMax(&omax_sh, ord_of(bcum[bl3] + (m - l)));
-      }
-    } else {
       xor_down<32>([&](auto o) {
         constexpr int X = decltype(o)::value;
         lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
@@ -1026,60 +1043,211 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
         ps[wave] = s;
       }
       __syncthreads();
-      const int wpb = LPB >> 6;
-      if ((int)threadIdx.x < nloc) {
-        float mm = pm[threadIdx.x * wpb], ss = ps[threadIdx.x * wpb];
-        for (int i = 1; i < wpb; ++i) lse_combine(mm, ss, pm[threadIdx.x * wpb + i], ps[threadIdx.x * wpb + i]);
-        const float l = lse_ext ? lse_ext[b0 + threadIdx.x] : mm + __logf(ss);
-        blse[threadIdx.x] = l;
-        if (brow[threadIdx.x] >= 0) atomicMax(&omax_sh, ord_of(bcum[threadIdx.x] + (mm - l)));
+      if (threadIdx.x == 0) {
+        float mm = pm[0], ss = ps[0];
+        for (int w = 1; w < kSelWaves; ++w) lse_combine(mm, ss, pm[w], ps[w]);
+        zms_sh = make_float2(mm, ss);
+        omax_sh = ord_of(mm);
+      }
+    } else if (TOKEN_IDX && dense) {
+      // token-indexed rows of a dense table (the score-first comparison; its
+      // normaliser over the whole codebook is given): keys from a walk of the
+      // beams' bitmap words, the beams' best score by an exact atomic max
+      uint32_t* bmo = reinterpret_cast<uint32_t*>(sel);  // sel is free until phase 4
+      for (int i = threadIdx.x; i < nbl; i += NT) bmo[i] = 0u;
+      __syncthreads();
+      for (int u = threadIdx.x; u < pairs; u += NT) {
+        const int bl = bl_lo + u / tab.words, w = u % tab.words;
+        const int r = brow[bl];
+        if (r < 0) continue;
+        const DWord dw = dense_word<NX>(tab, r, w);
+        const float* zb = z + (int64_t)(b0 + bl) * ldz;
+        uint32_t x = dw.bits;
+        int f = cpre[bl] + dw.rank;
+        uint32_t mo = 0u;
+        while (x) {
+          const int v = (w << 5) + __ffs(x) - 1;
+          x &= x - 1;
+          const float zv = zb[v];
+          mo = max(mo, ord_of(zv));
+          if (store && f >= f0 && f < f1) keys[f - f0] = ((uint64_t)__float_as_uint(zv) << 32) | code_of(bl, v);
+          ++f;
+        }
+        if (mo) atomicMax(&bmo[bl - bl_lo], mo);
+      }
+      __syncthreads();
+      for (int bl = bl_lo + threadIdx.x; bl <= bl_hi; bl += NT)
+        if (brow[bl] >= 0 && cpre[bl + 1] > cpre[bl]) {
+          if (zkey)
+            omax_sh = bmo[0];  // single beam, score-first: keys by the score alone
+          else
+            final_lse(bl, float_of_ord(bmo[bl - bl_lo]), 1.f);
+        }
+    } else {
+      // unit u of the part (u_lo + u is the request's unit) to a 16-lane
+      // group; the group's lanes read the unit's scores at a stride of 16
+      // (contiguous per load), each keeping an online (max, sum of exp)
+      const int NGR = NT / GL;
+      const int u_lo = C > 0 ? upre[bl_lo] : 0, u_hi = C > 0 ? upre[bl_hi + 1] : 0;
+      const int gl = threadIdx.x % GL, grp = threadIdx.x / GL;
+      auto unit_beam = [&](int u) {  // last b with upre[b] <= u
+        int lo = bl_lo, hi = bl_hi + 1;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (upre[mid] <= u)
+            lo = mid;
+          else
+            hi = mid;
+        }
+        return lo;
+      };
+      for (int u = u_lo + grp; u < u_hi; u += NGR) {  // uniform over the group
+        const int b = unit_beam(u);
+        const int ua = u - upre[b];
+        const int n_b = cpre[b + 1] - cpre[b];
+        const int j0 = ua * SEG, j1 = min(n_b, j0 + SEG);
+        const float* zb = z + (int64_t)(b0 + b) * ldz;
+        float m = -INFINITY, s = 0.f;
+        for (int jb = j0; jb < j1; jb += GL * UL) {
+          float zv[UL];
+          int tk[UL];
+          if constexpr (TOKEN_IDX) {
+#pragma unroll
+            for (int i = 0; i < UL; ++i) {
+              const int j = jb + i * GL + gl;
+              tk[i] = j < j1 ? (int)tab.tok[bbase[b] + j] : 0;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < UL; ++i) {
+            const int j = jb + i * GL + gl;
+            const int f = cpre[b] + j;
+            if (j < j1) {
+              if (MODE == kZScore && store && f >= f0 && f < f1)
+                zv[i] = __uint_as_float((uint32_t)(keys[f - f0] >> 32));
+              else
+                zv[i] = zb[TOKEN_IDX ? tk[i] : j];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < UL; ++i) {
+            const int j = jb + i * GL + gl;
+            if (j < j1) {
+              const float x = zv[i];
+              if (x > m) {
+                s = s * __expf(m - x) + 1.f;
+                m = x;
+              } else {
+                s += __expf(x - m);
+              }
+              const int f = cpre[b] + j;
+              if (MODE != kZScore && store && f >= f0 && f < f1) {
+                // sparse rows: slot = legal rank; dense rows (rank-indexed
+                // scores): the code goes in after this pass
+                const uint32_t code = dense ? 0u : code_of(b, j);
+                keys[f - f0] = ((uint64_t)__float_as_uint(x) << 32) | code;
+              }
+            }
+          }
+        }
+        xor_down_width(GL, [&](auto o) {
+          constexpr int X = decltype(o)::value;
+          lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
+        });
+        if (gl == 0) {
+          if (upre[b + 1] - upre[b] == 1) {
+            final_lse(b, m, s);
+          } else {
+            upart[u - u_lo] = make_float2(m, s);
+            multi_sh = 1;
+          }
+        }
+      }
+      __syncthreads();
+      // beams of several units: one wave joins the unit partials in order
+      for (int b = bl_lo + wave; multi_sh && b <= bl_hi; b += kSelWaves) {
+        const int nu = upre[b + 1] - upre[b];
+        if (nu < 2) continue;  // uniform over the wave
+        float m = -INFINITY, s = 0.f;
+        for (int i = lane; i < nu; i += 64) {
+          const float2 pq = upart[upre[b] - u_lo + i];
+          lse_combine(m, s, pq.x, pq.y);
+        }
+        xor_down<32>([&](auto o) {
+          constexpr int X = decltype(o)::value;
+          lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
+        });
+        if (lane == 0) final_lse(b, m, s);
       }
     }
   }
   __syncthreads();
   if (code_pass) {
-    // a bit's legal rank is the word's count before it plus the set bits below it
+    // a bit's legal rank is the word's count before it plus the set bits below
+    // it; only this part's flat range [f0, f1) is coded
     const int nb = 32 / LPW;
     const uint32_t sub_mask = (nb == 32) ? 0xFFFFFFFFu : ((1u << nb) - 1u);
+    uint32_t* key_lo = reinterpret_cast<uint32_t*>(keys);
     for (int u = threadIdx.x; u < pairs * LPW; u += NT) {
       const int pr = u / LPW, sub = u - pr * LPW;
-      const int bl = pr / tab.words, w = pr - bl * tab.words;
+      const int bl = bl_lo + pr / tab.words, w = pr % tab.words;
       const int r = brow[bl];
       if (r < 0) continue;
       const DWord dw = (u == (int)threadIdx.x) ? dwpf : dense_word<NX>(tab, r, w);
       const int lo = sub * nb;  // <= 31
       uint32_t x = (dw.bits >> lo) & sub_mask;
-      int j = cpre[bl] + dw.rank + __popc(dw.bits & ((1u << lo) - 1u));
-      const uint32_t code0 = (uint32_t)(blo + bl) * S + (uint32_t)((w << 5) + lo);
+      int f = cpre[bl] + dw.rank + __popc(dw.bits & ((1u << lo) - 1u));
+      if (f >= f1 || f + __popc(x) <= f0) continue;
+      const uint32_t code0 = code_of(bl, (w << 5) + lo);
       // the key's high half (the score) was stored with a zero low half above:
       // the code goes into the low half alone, with no read of the key
-      uint32_t* key_lo = reinterpret_cast<uint32_t*>(keys);
       while (x) {
         const int k = __ffs(x) - 1;
         x &= x - 1;
-        key_lo[2 * (j++)] = code0 + (uint32_t)k;
+        if (f >= f0 && f < f1) key_lo[2 * (f - f0)] = code0 + (uint32_t)k;
+        ++f;
       }
     }
     __syncthreads();
   }
-  if (slot_dbg && !MERGE) {
-    for (int bl = wave; bl < nloc; bl += kSelWaves) {
-      const int b = b0 + bl;
-      const int r = brow[bl];
-      float* dbg = slot_dbg + (int64_t)b * S;
-      const float* zb = z + (int64_t)b * ldz;
-      const int n = r >= 0 ? cpre[bl + 1] - cpre[bl] : 0;
-      const float l = blse[bl];
+  if constexpr (MERGE) {
+    if (zkey) {
+      // the single beam's normaliser: the parts' partials joined in a fixed
+      // butterfly over wave 0 (lane i holds part i), or the given one
+      if (wave == 0) {
+        float m = (lane < P) ? mms.x : -INFINITY, s = (lane < P) ? mms.y : 0.f;
+        xor_down<32>([&](auto o) {
+          constexpr int X = decltype(o)::value;
+          lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
+        });
+        if (lane == 0) blse[0] = lse_ext ? lse_ext[b0] : m + __logf(s);
+      }
+      __syncthreads();
+    }
+  }
+  if (slot_dbg && (MERGE ? zkey : !zkey)) {
+    // each beam's row is written by one part: the one holding its first
+    // candidate (beams without candidates: part b mod P); a single beam
+    // split over parts by the merge
+    for (int b = wave; b < k_in; b += kSelWaves) {
+      const int r = brow[b];
+      const int n = cpre[b + 1] - cpre[b];
+      const bool mine = MERGE || ((n > 0) ? (cpre[b] >= f0 && cpre[b] < f1) : (b % P == part));
+      if (!mine) continue;
+      float* dbg = slot_dbg + (int64_t)(b0 + b) * S;
+      const float* zb = z + (int64_t)(b0 + b) * ldz;
+      const bool tix = MERGE ? ztok != 0 : TOKEN_IDX;  // the merge is told the score layout
+      const float l = n > 0 ? blse[b] : 0.f;
       for (int j = lane; j < (int)S; j += 64) {
         float v = -INFINITY;
-        if (r >= 0) {
+        if (r >= 0 && n > 0) {
           if (!dense) {
-            if (j < n) v = (TOKEN_IDX ? zb[tab.tok[bbase[bl] + j]] : zb[j]) - l;
+            if (j < n) v = (tix ? zb[tab.tok[bbase[b] + j]] : zb[j]) - l;
           } else {
             const DWord dw = dense_word<NX>(tab, r, j >> 5);
             const uint32_t x = dw.bits;
             if ((x >> (j & 31)) & 1u)
-              v = (TOKEN_IDX ? zb[j] : zb[dw.rank + __popc(x & ((1u << (j & 31)) - 1u))]) - l;
+              v = (tix ? zb[j] : zb[dw.rank + __popc(x & ((1u << (j & 31)) - 1u))]) - l;
           }
         }
         dbg[j] = v;
@@ -1092,16 +1260,16 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     // the parts' keys (already final) into LDS, in part order
     const int exp_ = block_excl_scan<NT>(mcnt, sh, &C);
     if ((int)threadIdx.x < P) {
-      pre[threadIdx.x] = exp_;
-      cpre[threadIdx.x] = mcnt;  // part counts (the merge has no per-beam candidates)
+      mpre[threadIdx.x] = exp_;
+      mcn[threadIdx.x] = mcnt;
     }
     __syncthreads();
     uint32_t o = 0;
     for (int f = threadIdx.x; f < P * K; f += NT) {
       const int pi = f / K, i = f - pi * K;
-      if (i < cpre[pi]) {
+      if (i < mcn[pi]) {
         const uint64_t kk = (f == (int)threadIdx.x) ? mkey0 : part_keys[(int64_t)(q * P + pi) * K + i];
-        keys[pre[pi] + i] = kk;
+        keys[mpre[pi] + i] = kk;
         o = max(o, (uint32_t)(kk >> 32));
       }
     }
@@ -1135,43 +1303,50 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
     for (int i = threadIdx.x; i < C; i += NT) {
       const uint64_t e = keys[i];
       const uint32_t code = (uint32_t)e;
-      const int bl = (int)(code / S) - blo;
-      const uint64_t k = make_key(bcum[bl] + (__uint_as_float((uint32_t)(e >> 32)) - blse[bl]), code);
+      const int bl = (int)(code / S);
+      const float zv = __uint_as_float((uint32_t)(e >> 32));
+      const uint64_t k = zkey ? make_key(zv, code) : make_key(bcum[bl] + (zv - blse[bl]), code);
       keys[i] = k;
       if (histo) atomicAdd(&dhist[bin_of(k)], 1);
     }
     __syncthreads();
   }
-  // without room in LDS, keys are recomputed from z in every pass; on dense
-  // rows LPE threads share a bitmap word (each walks 32 / LPE of its bits)
-  // while that leaves no thread idle
+  // without room in LDS, keys are recomputed from z in every pass, over this
+  // part's flat range; on dense rows LPE threads share a bitmap word (each
+  // walks 32 / LPE of its bits) while that leaves no thread idle
   int LPE = 1;
   if (dense)
-    while (LPE < 32 && T * LPE * 2 <= NT) LPE *= 2;
+    while (LPE < 32 && pairs * LPE * 2 <= NT) LPE *= 2;
   auto enumerate = [&](auto&& fn) {
-    for (int f2 = threadIdx.x; f2 < T * LPE; f2 += NT) {
-      const int f = f2 / LPE, sub = f2 - f * LPE;
-      const int bl = beam_of(pre, f), i = f - pre[bl];
-      const int b = b0 + bl;
-      const int r = brow[bl];
-      const float c = bcum[bl], l = blse[bl];
-      const float* zb = z + (int64_t)b * ldz;
-      const uint32_t code0 = (uint32_t)(blo + bl) * S;
-      if (!dense) {
+    if (!dense) {
+      for (int f = f0 + threadIdx.x; f < f1; f += NT) {
+        const int bl = beam_of(f), i = f - cpre[bl];
+        const float* zb = z + (int64_t)(b0 + bl) * ldz;
         const float zv = TOKEN_IDX ? zb[tab.tok[bbase[bl] + i]] : zb[i];
-        fn(make_key(c + (zv - l), code0 + (uint32_t)i));
-      } else {
-        const DWord dw = dense_word<NX>(tab, r, i);
-        const int nb = 32 / LPE, lo = sub * nb;  // this thread's bits [lo, lo + nb)
-        uint32_t y = (dw.bits >> lo) & (nb == 32 ? 0xFFFFFFFFu : ((1u << nb) - 1u));
-        int j = dw.rank + __popc(dw.bits & ((1u << lo) - 1u));
-        while (y) {
-          const int v = (i << 5) + lo + __ffs(y) - 1;
-          y &= y - 1;
+        fn(zkey ? make_key(zv, code_of(bl, i)) : make_key(bcum[bl] + (zv - blse[bl]), code_of(bl, i)));
+      }
+      return;
+    }
+    for (int f2 = threadIdx.x; f2 < pairs * LPE; f2 += NT) {
+      const int pr = f2 / LPE, sub = f2 - pr * LPE;
+      const int bl = bl_lo + pr / tab.words, i = pr % tab.words;
+      const int r = brow[bl];
+      if (r < 0) continue;
+      const float c = bcum[bl], l = blse[bl];
+      const float* zb = z + (int64_t)(b0 + bl) * ldz;
+      const DWord dw = dense_word<NX>(tab, r, i);
+      const int nb = 32 / LPE, lo = sub * nb;  // this thread's bits [lo, lo + nb)
+      uint32_t y = (dw.bits >> lo) & (nb == 32 ? 0xFFFFFFFFu : ((1u << nb) - 1u));
+      int j = dw.rank + __popc(dw.bits & ((1u << lo) - 1u));
+      while (y) {
+        const int v = (i << 5) + lo + __ffs(y) - 1;
+        y &= y - 1;
+        const int f = cpre[bl] + j;
+        if (f >= f0 && f < f1) {
           const float zv = TOKEN_IDX ? zb[v] : zb[j];
-          ++j;
-          fn(make_key(c + (zv - l), code0 + (uint32_t)v));
+          fn(zkey ? make_key(zv, code_of(bl, v)) : make_key(c + (zv - l), code_of(bl, v)));
         }
+        ++j;
       }
     }
   };
@@ -1201,7 +1376,7 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       if (i < C && g == 0 && rank < K) sel[rank] = mine;
     }
   } else if (C <= K) {
-    for (int i = threadIdx.x; i < C; i += NT) sel[i] = keys[i];  // C <= K <= kSelCap: stored
+    for (int i = threadIdx.x; i < C; i += NT) sel[i] = keys[i];  // C <= K <= kKeyCap: stored
   } else {
     if (!store) {
       enumerate([&](uint64_t k) { atomicAdd(&dhist[bin_of(k)], 1); });
@@ -1310,7 +1485,10 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
   if (!MERGE && P > 1) {
     // a part: its best keys go to the merge (in any order)
     for (int i = threadIdx.x; i < nsel; i += NT) part_keys[(int64_t)blockIdx.x * K + i] = sel[i];
-    if (threadIdx.x == 0) part_cnt[blockIdx.x] = nsel;
+    if (threadIdx.x == 0) {
+      part_cnt[blockIdx.x] = nsel;
+      if (zkey) part_ms[blockIdx.x] = zms_sh;
+    }
     return;
   }
 
@@ -1381,7 +1559,9 @@ __global__ __launch_bounds__(kSelThreads) void k_request_step(
       parent_out[oi] = b;
       token_out[oi] = token;
       row_out[oi] = next;
-      cum_out[oi] = float_of_ord((uint32_t)(key >> 32));
+      // split single-beam requests ranked by the score: cum = cum_in + (z - lse)
+      cum_out[oi] = zkey ? bcum[bl] + (float_of_ord((uint32_t)(key >> 32)) - blse[bl])
+                         : float_of_ord((uint32_t)(key >> 32));
       if (prefix_out) {
         for (int l = 0; l < t - 1; ++l) prefix_out[oi * L + l] = prefix_in[(int64_t)b * L + l];
         prefix_out[oi * L + t - 1] = token;
@@ -2074,8 +2254,8 @@ hipError_t launch_full_projection(const StepArgs& a, hipStream_t s) {
 
 #define ZGR_STEP_ARGS                                                                            \
   a.tab, a.t, a.L, a.k_in, a.K, a.row_in, a.cum_in, a.hidden, a.W, a.z, a.ldz, a.parts,            \
-      a.part_keys, a.part_cnt, a.parent_out, a.token_out, a.row_out, a.cum_out, a.prefix_in,       \
-      a.prefix_out, a.slot_dbg, a.lse_ext, a.err
+      a.part_keys, a.part_cnt, a.part_ms, a.parent_out, a.token_out, a.row_out, a.cum_out, a.prefix_in,       \
+      a.prefix_out, a.slot_dbg, a.lse_ext, (int32_t)a.z_token, a.err
 
 template <int DT, int D>
 hipError_t launch_scored_step(const StepArgs& a, hipStream_t s) {

@@ -270,6 +270,25 @@ def gpu_trajectory(s, plan, requests, mode="filter_first"):
     return out["row_out"].reshape(B, K), prefixes.reshape(B, K, L), cum.reshape(B, K), amb
 
 
+def assert_same_ranking(got, want, want_score, tol, what=""):
+    """End-to-end comparison of a returned list with the oracle's (keys are
+    item ids, or SIDs where off-catalog codes share the id -1).  The lists
+    hold the same entries, and position i holds an entry whose oracle score
+    is within tol of the oracle's i-th score: entries whose oracle scores
+    differ by less than the tolerance may come in either order (a float32
+    path cannot order scores closer than its own rounding; the step check
+    allows the same band), every other pair keeps the oracle's order."""
+    got = [tuple(np.atleast_1d(x).tolist()) for x in got]
+    want = [tuple(np.atleast_1d(x).tolist()) for x in want]
+    assert sorted(got) == sorted(want), (what, "different entries")
+    score = {}
+    for w, s in zip(want, want_score):
+        score.setdefault(w, s)
+    for i, g in enumerate(got):
+        a, b = score[g], want_score[i]
+        assert (a == b) or abs(a - b) <= tol, (what, i, g, a, b)
+
+
 def oracle_unambiguous(dec, K, tol):
     for st in dec.steps:
         sc = np.sort(st["res"].cand_score)[::-1]

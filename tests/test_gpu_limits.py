@@ -76,7 +76,7 @@ def test_limit_decode(name, proj):
             assert np.array_equal(s.sids[s.cat.input_row(int(it))], sid)
         dec = s.oracle_decode(q)
         if gu.oracle_unambiguous(dec, K, gu.TOL[cfg.dtype]):
-            assert np.array_equal(rows[q], dec.item), q
+            gu.assert_same_ranking(rows[q], dec.item, dec.score, gu.TOL[cfg.dtype], q)
     print(f"{name} {proj}: {amb} ambiguous request-steps")
 
 

@@ -100,7 +100,7 @@ def test_decode_parity(name, proj):
         dec = s.oracle_decode(q)
         if oracle_unambiguous(dec, K, tol):
             exact += 1
-            assert np.array_equal(d_items[q], dec.item), q
+            gu.assert_same_ranking(d_items[q], dec.item, dec.score, tol, q)
             assert np.allclose(sc_t.cpu().numpy().reshape(B, K)[q][live], dec.score[live], atol=tol * L, rtol=0)
     print(f"{name} {proj}: {exact}/{B} requests compared item-for-item, {amb} ambiguous request-steps")
 
