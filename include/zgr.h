@@ -322,6 +322,35 @@ int32_t zgr_step(zgr_plan* plan, int32_t t, const void* hidden_dev, const int32_
 int32_t zgr_decode(zgr_plan* plan, zgr_hidden_fn hidden_fn, void* user, int32_t top_k,
                    int64_t* item_out, int32_t* sid_out, float* score_out, void* stream);
 
+/*
+ * zgr_step without allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It runs the kernels of zgr_step for one step t of a
+ * batch of B requests (beam width K, hidden size d, weights W_t of dtype) with
+ * the given projection (ZGR_PROJ_FULL or ZGR_PROJ_SELECTIVE; there is no plan,
+ * so no warm-up choice), filter-first, and keeps the step's scratch (score
+ * buffer, unit scan, request parts' keys and partials, device flag) in one
+ * file-scope device array of at most 64 MiB that each GPU holds for the life
+ * of the process; it calls no allocator.
+ *   idx        an index on the current device; W_t device [V][d] of dtype
+ *   hidden_dev, row_in, cum_in, k_in, parent_out .. cum_out, slot_dbg: as in
+ *              zgr_step (device buffers, caller-owned)
+ *   err_out    device int32 or NULL: receives 1 when a beam row was outside
+ *              the step's table (such beams count as dead), else 0
+ * Every call on a GPU shares that GPU's scratch array, which keeps the last
+ * call's contents: calls that overlap on one GPU (two streams, two host
+ * threads) race and must be serialised by the caller.
+ * Errors (before any work is enqueued): ZGR_E_ARG, ZGR_E_STATE (index not on
+ * this device), ZGR_E_SHAPE (unsupported size, or a step whose scratch
+ * exceeds the array: about B*k_in*max(S_t, V)*4 bytes for the scores plus
+ * B*64*K*8 for the part keys), ZGR_E_HIP.
+ */
+int32_t zgr_step_noalloc(const zgr_index* idx, const void* W_t, int32_t dtype, int32_t d, int32_t B,
+                         int32_t K, int32_t t, int32_t proj, const void* hidden_dev,
+                         const int32_t* row_in, const float* cum_in, int32_t k_in,
+                         int32_t* parent_out, int32_t* token_out, int32_t* row_out, float* cum_out,
+                         float* slot_dbg, int32_t* err_out, void* stream);
+
 /* Synchronise stream and report (then clear) the plan's device-side error
  * flag: ZGR_OK or ZGR_E_DEVICE; ZGR_E_HIP if the sync fails. */
 int32_t zgr_plan_status(zgr_plan* plan, void* stream);

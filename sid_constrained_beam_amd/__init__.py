@@ -121,6 +121,8 @@ def lib() -> ctypes.CDLL:
             "zgr_plan_profile": (_I32, [_P, _I32]),
             "zgr_plan_profile_read": (_I32, [_P, _I32, _I32, ctypes.POINTER(_I64),
                                              ctypes.POINTER(ctypes.c_double)]),
+            "zgr_step_noalloc": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P, _P,
+                                        _I32, _P, _P, _P, _P, _P, _P, _P]),
             "zgr_full_projection_variant": (_I32, [_I32, _I32, _I32, _I32, _I32, _I32,
                                                    ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                                    ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
@@ -429,6 +431,17 @@ def zgr_step(plan: Plan, t: int, hidden, row_in, cum_in, k_in: int, parent_out, 
     _check(lib().zgr_step(plan.handle, t, _dptr(hidden), _dptr(row_in), _dptr(cum_in), k_in,
                           _dptr(parent_out), _dptr(token_out), _dptr(row_out), _dptr(cum_out),
                           _dptr(slot_dbg), _stream_ptr(stream)))
+
+
+def zgr_step_noalloc(index: Index, W_t, dtype: str, d: int, B: int, K: int, t: int, proj, hidden,
+                     row_in, cum_in, k_in: int, parent_out, token_out, row_out, cum_out,
+                     slot_dbg=None, err_out=None, stream=None):
+    """One step without a plan: scratch from the library's static device array."""
+    _check(lib().zgr_step_noalloc(index.handle, _dptr(W_t), DTYPE_CODES[dtype], int(d), int(B), int(K),
+                                  int(t), PROJ_CODES[proj] if isinstance(proj, str) else int(proj),
+                                  _dptr(hidden), _dptr(row_in), _dptr(cum_in),
+                                  int(k_in), _dptr(parent_out), _dptr(token_out), _dptr(row_out),
+                                  _dptr(cum_out), _dptr(slot_dbg), _dptr(err_out), _stream_ptr(stream)))
 
 
 def zgr_decode(plan: Plan, hidden_fn: HiddenCallable, top_k: int, item_out, sid_out=None,

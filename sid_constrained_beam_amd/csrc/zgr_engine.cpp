@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -747,3 +748,169 @@ int32_t zgr_plan_status(zgr_plan* p, void* stream) {
 }
 
 }  // extern "C"
+
+// ---- step without allocation --------------------------------------------------------------
+//
+// zgr_step_noalloc runs the kernels of zgr_step with the step's scratch (the
+// score buffer, the unit scan, the request parts' keys and partials, the
+// device flag) in one file-scope device array instead of a plan's HBM.  Each
+// device holds its own copy of the array for the life of the process; host
+// code reaches a device's copy only through the address hipGetSymbolAddress
+// gives for it, taken once per device with that device current.
+
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;  // 64 MiB per device
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kNoAllocMaxDevices = 64;
+struct NoAllocDevice {
+  unsigned char* ptr = nullptr;  // the device's copy of scratch
+  int n_cu = 0;
+  bool ready = false;
+};
+std::mutex g_noalloc_mu;
+NoAllocDevice g_noalloc[kNoAllocMaxDevices];
+
+// The flag is cleared by a kernel, not a memset, so a captured graph replays it.
+__global__ void k_noalloc_flag_clear(int32_t* flag) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *flag = 0;
+}
+__global__ void k_noalloc_flag_copy(const int32_t* flag, int32_t* out) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *out = *flag;
+}
+
+int32_t noalloc_device(NoAllocDevice** out, int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(ZGR_E_STATE, "zgr_step_noalloc: device id beyond the supported range");
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoAllocDevice& d = g_noalloc[dev];
+  if (!d.ready) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    }
+    int n_cu = 0;
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    d.ptr = (unsigned char*)ptr;
+    d.n_cu = n_cu > 0 ? n_cu : 256;
+    d.ready = true;
+  }
+  *out = &d;
+  *dev_out = dev;
+  return ZGR_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" int32_t zgr_step_noalloc(const zgr_index* idx, const void* W_t, int32_t dtype, int32_t d,
+                                    int32_t B, int32_t K, int32_t t, int32_t proj,
+                                    const void* hidden_dev, const int32_t* row_in, const float* cum_in,
+                                    int32_t k_in, int32_t* parent_out, int32_t* token_out,
+                                    int32_t* row_out, float* cum_out, float* slot_dbg,
+                                    int32_t* err_out, void* stream) {
+  using namespace zgr;
+  if (!idx || !W_t || !hidden_dev || !row_in || !cum_in || !parent_out || !token_out || !row_out ||
+      !cum_out)
+    return fail(ZGR_E_ARG, "zgr_step_noalloc: null argument");
+  if (dtype < ZGR_F32 || dtype > ZGR_F16) return fail(ZGR_E_ARG, "zgr_step_noalloc: bad dtype");
+  if (B < 1 || K < 1) return fail(ZGR_E_ARG, "zgr_step_noalloc: B and K must be >= 1");
+  if (K > 1024) return fail(ZGR_E_SHAPE, "zgr_step_noalloc: K must be <= 1024");
+  if (d < 64 || d % 64 != 0 || !supported_hidden_size(d))
+    return fail(ZGR_E_SHAPE, "zgr_step_noalloc: d must be one of 64,128,256,512,768,1024,2048,4096");
+  if (t < 1 || t > idx->L) return fail(ZGR_E_ARG, "zgr_step_noalloc: t out of range");
+  if (k_in < 1 || k_in > K) return fail(ZGR_E_ARG, "zgr_step_noalloc: k_in must be in [1, K]");
+  if (proj != ZGR_PROJ_FULL && proj != ZGR_PROJ_SELECTIVE)
+    return fail(ZGR_E_ARG, "zgr_step_noalloc: proj must be ZGR_PROJ_FULL or ZGR_PROJ_SELECTIVE");
+  if (!idx->on_device) return fail(ZGR_E_STATE, "zgr_step_noalloc: index is not on the device");
+  const HostTable& h = idx->host[t - 1];
+  if ((int64_t)K * std::max<int32_t>(1, h.stride) >= (int64_t)UINT32_MAX)
+    return fail(ZGR_E_SHAPE, "zgr_step_noalloc: K * slot stride too large");
+  const int64_t M = (int64_t)B * k_in;
+  if ((int64_t)B * K >= INT32_MAX) return fail(ZGR_E_SHAPE, "zgr_step_noalloc: B*K must be < 2^31");
+  // the step's scratch, carved from the array at 256-byte boundaries
+  const int64_t ldz_max = std::max<int64_t>(h.stride, idx->V);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align256(off + std::max<size_t>(bytes, 4));
+    return at;
+  };
+  const size_t o_err = take(4);
+  const size_t o_pcnt = take((size_t)B * kMaxParts * 4);
+  const size_t o_pms = take((size_t)B * kMaxParts * 8);
+  const size_t o_pkeys = take((size_t)B * kMaxParts * K * 8);
+  const size_t o_nlegal = take((size_t)M * 4);
+  const size_t o_units = take((size_t)(M + 1) * 4);
+  const size_t o_lse = take((size_t)M * 4);
+  const size_t o_z = take((size_t)M * ldz_max * 4);
+  if (off > kNoAllocScratchBytes)
+    return fail(ZGR_E_SHAPE, "zgr_step_noalloc: the step needs " + std::to_string(off) +
+                                 " bytes of scratch; the static maximum is " +
+                                 std::to_string(kNoAllocScratchBytes) + " bytes (use zgr_step with a plan)");
+  NoAllocDevice* dv = nullptr;
+  int dev = -1;
+  int32_t rc = noalloc_device(&dv, &dev);
+  if (rc != ZGR_OK) return rc;
+  if (dev != idx->device) return fail(ZGR_E_STATE, "zgr_step_noalloc: index lives on another device");
+  unsigned char* base = dv->ptr;
+  // the fields of a plan that a step reads (no device memory of its own)
+  zgr_plan p;
+  p.idx = idx;
+  p.L = idx->L;
+  p.V = idx->V;
+  p.d = d;
+  p.B = B;
+  p.K = K;
+  p.dtype = dtype;
+  p.n_cu = dv->n_cu;
+  StepArgs a{};
+  a.tab = idx->dev[t - 1];
+  a.t = t;
+  a.L = idx->L;
+  a.B = B;
+  a.K = K;
+  a.k_in = k_in;
+  a.M = (int32_t)M;
+  a.d = d;
+  a.dtype = dtype;
+  a.hidden = hidden_dev;
+  a.W = W_t;
+  a.row_in = row_in;
+  a.cum_in = cum_in;
+  a.parent_out = parent_out;
+  a.token_out = token_out;
+  a.row_out = row_out;
+  a.cum_out = cum_out;
+  a.slot_dbg = slot_dbg;
+  a.z = (float*)(base + o_z);
+  a.nlegal = (int32_t*)(base + o_nlegal);
+  a.unit_start = (int32_t*)(base + o_units);
+  a.lse = (float*)(base + o_lse);
+  a.parts = 1;
+  a.part_keys = (uint64_t*)(base + o_pkeys);
+  a.part_cnt = (int32_t*)(base + o_pcnt);
+  a.part_ms = (float2*)(base + o_pms);
+  a.err = (int32_t*)(base + o_err);
+  a.n_cu = dv->n_cu;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(k_noalloc_flag_clear, dim3(1), dim3(64), 0, s, a.err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "flag clear launch");
+  rc = run_step(&p, a, proj, s);
+  if (rc != ZGR_OK) return rc;
+  if (err_out) {
+    hipLaunchKernelGGL(k_noalloc_flag_copy, dim3(1), dim3(64), 0, s, a.err, err_out);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "flag copy launch");
+  }
+  return ZGR_OK;
+}

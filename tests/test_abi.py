@@ -129,3 +129,28 @@ def test_last_error_is_thread_local():
     th.join()
     assert "share one SID" in seen["other"]
     assert "V must be" in zgr.last_error()
+
+
+def test_step_noalloc_argument_errors():
+    """zgr_step_noalloc checks its arguments before any HIP call."""
+    L = zgr.lib()
+    sids = np.array([[0, 1], [1, 0], [1, 1]], np.int32)
+    idx, _ = zgr.zgr_index_build_host(sids, 4)   # host only: not on a device
+    p = ctypes.c_void_p(8)  # never dereferenced: every call below fails its checks first
+    args = lambda **kw: dict(dict(idx=idx.handle, W=p, dtype=zgr.ZGR_F32, d=64, B=2, K=4, t=1,
+                                  proj=zgr.ZGR_PROJ_SELECTIVE, k_in=1), **kw)
+
+    def call(a):
+        return L.zgr_step_noalloc(a["idx"], a["W"], a["dtype"], a["d"], a["B"], a["K"], a["t"],
+                                  a["proj"], p, p, p, a["k_in"], p, p, p, p, None, None, None)
+    assert call(args(idx=None)) == zgr.ZGR_E_ARG
+    assert call(args(W=None)) == zgr.ZGR_E_ARG
+    assert call(args(dtype=5)) == zgr.ZGR_E_ARG
+    assert call(args(K=2000)) == zgr.ZGR_E_SHAPE
+    assert call(args(d=100)) == zgr.ZGR_E_SHAPE
+    assert call(args(t=3)) == zgr.ZGR_E_ARG
+    assert call(args(k_in=5)) == zgr.ZGR_E_ARG
+    assert call(args(proj=zgr.ZGR_PROJ_AUTO)) == zgr.ZGR_E_ARG
+    assert call(args(proj=zgr.ZGR_PROJ_NAIVE)) == zgr.ZGR_E_ARG
+    assert call(args()) == zgr.ZGR_E_STATE  # the index is not on a device
+    idx.free()
