@@ -224,23 +224,25 @@ bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
 // is split over several blocks, each taking an equal share of its flat
 // candidate list (a beam may span blocks), then merged; a request of at most
 // kSmallRequest candidates (estimated from the table's mean row) stays whole,
-// since below that a split does not pay for the merge launch.  Enough parts
-// that a part's keys fit the LDS key array with room for requests above the
-// mean; beyond that, as many as one round of blocks at two per compute unit
-// takes, but parts of at least kPartMinCandidates; the parts' best K keys must
-// fit the merge's LDS.
-constexpr double kPartMinCandidates = 2048.0;
+// since below that a split does not pay for the merge launch.  A part aims at
+// kPartCandidates candidates, with no more parts than one round of blocks at
+// two per compute unit takes, but always enough parts that a part's keys fit
+// the LDS key array (a part whose keys do not fit recomputes them from the
+// scores in each pass, which costs more than more parts: measured on the
+// dense-early catalog's second step); the parts' best K keys must fit the
+// merge's LDS.
 constexpr double kSmallRequest = 6144.0;
+constexpr double kPartCandidates = 2048.0;
+constexpr double kPartMaxCandidates = 0.9 * kKeyCapHost;
 int32_t request_parts(const zgr_plan* p, const StepArgs& a) {
   const HostTable& h = p->idx->host[a.t - 1];
   double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
   if (a.tab.fmt == kFmtAll) mean_n = p->V;
   const double est_c = a.k_in * std::min<double>(mean_n, a.tab.stride);
   if (est_c <= kSmallRequest) return 1;
-  const int p_fit = (int)std::ceil(est_c / (0.6 * kKeyCapHost));
   const int p_occ = std::max(1, 2 * p->n_cu / std::max(1, a.B));
-  const int p_size = std::max(1, (int)std::ceil(est_c / kPartMinCandidates));
-  int P = std::max(p_fit, std::min(p_occ, p_size));
+  int P = std::min((int)std::ceil(est_c / kPartCandidates), p_occ);
+  P = std::max(P, (int)std::ceil(est_c / kPartMaxCandidates));
   P = std::min({P, kMaxParts, kMergeCapHost / std::max(1, a.K)});
   return std::max(1, P);
 }

@@ -887,7 +887,7 @@ void k_request_step(
   const int GL = mean_n >= 64 ? 16 : (mean_n >= 8 ? 4 : 1);
   int SEG = GL * UL;
   while ((Cq + SEG - 1) / SEG + k_in > kUnitCap) SEG *= 2;
-  if constexpr (!MERGE) {
+  if (!MERGE && !zkey) {  // uniform; split single-beam parts reduce only their own range
     int Uq;
     const int uex = block_excl_scan<NT>((cnt + SEG - 1) / SEG, sh, &Uq);
     if ((int)threadIdx.x < k_in) upre[threadIdx.x] = uex;
