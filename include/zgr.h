@@ -93,7 +93,7 @@ typedef struct {
   int32_t stride;  /* S_t: slots per beam (max legal count of a row; V when dense) */
   int64_t bytes;   /* device bytes of this table */
   int32_t max_legal;  /* largest legal count of any row */
-  int32_t reserved;
+  int32_t slice_dir;  /* 1 if the (sparse) table holds a slice directory, else 0 */
 } zgr_step_stats;
 
 /* Text of a status code (static storage). */
@@ -143,10 +143,24 @@ int32_t zgr_index_upload(const int32_t* sids, int64_t N, int32_t L, int32_t V, c
 #define ZGR_UPLOAD_STAGED 0 /* double-buffered pinned staging (default) */
 #define ZGR_UPLOAD_DIRECT 1 /* one hipMemcpyAsync per array from the pageable host tables */
 
+/* Slice directory of a sparse table: per row, uint16 [8], entry x < 7 the
+ * number of the row's legal tokens below (x + 1) * ceil(V / 8) (entry 7 is
+ * 0).  With it, the selective projection lets the compute units of one XCD
+ * (one L2 cache) score only the candidates whose tokens fall in one eighth
+ * of the codebook, so each L2 holds one eighth of the weight rows.  Our
+ * addition to the per-step layout; AUTO builds it for sparse tables with
+ * V >= 1024 whose rows hold 32 or more legal tokens on average (16 bytes per
+ * row, at most a quarter of the table's token bytes). */
+#define ZGR_SLICES_AUTO 0
+#define ZGR_SLICES_ALWAYS 1 /* every sparse table */
+#define ZGR_SLICES_NEVER 2
+
 typedef struct {
   int32_t host_threads;  /* 0 = hardware threads (at most 16) for large catalogs; else 1..64 */
   int32_t upload;        /* ZGR_UPLOAD_STAGED or ZGR_UPLOAD_DIRECT */
   int64_t staging_bytes; /* bytes per staging buffer; 0 = 64 MiB (clamped to [4 KiB, upload size]) */
+  int32_t slices;        /* ZGR_SLICES_* (build only) */
+  int32_t reserved;      /* 0 */
 } zgr_build_opts;
 
 /* Wall-clock milliseconds of each phase of the last build / upload. */
@@ -165,7 +179,7 @@ typedef struct {
 
 /* zgr_index_build_host with options (NULL = defaults); times (nullable)
  * receives the build phases.  Errors: as zgr_index_build_host, and ZGR_E_ARG
- * for a negative host_threads. */
+ * for a negative host_threads or an unknown slices value. */
 int32_t zgr_index_build_host_ex(const int32_t* sids, int64_t N, int32_t L, int32_t V,
                                 const int32_t* fmt, int64_t* rank_of_input,
                                 const zgr_build_opts* opts, zgr_build_times* times,
@@ -205,6 +219,11 @@ int32_t zgr_index_stats(const zgr_index* idx, int32_t t, zgr_step_stats* out);
  * pointer may be NULL.  Errors: ZGR_E_ARG. */
 int32_t zgr_index_host_table(const zgr_index* idx, int32_t t, const int32_t** row_ptr,
                              const uint16_t** tok, const uint32_t** bits);
+
+/* Host copy of table t's slice directory (uint16 [rows][8], see
+ * ZGR_SLICES_AUTO), or NULL in *sdir when the table has none.
+ * Errors: ZGR_E_ARG. */
+int32_t zgr_index_host_slices(const zgr_index* idx, int32_t t, const uint16_t** sdir);
 
 /* Index shape: L, V, N (any output may be NULL). */
 int32_t zgr_index_shape(const zgr_index* idx, int32_t* L, int32_t* V, int64_t* N);

@@ -26,6 +26,8 @@ ZGR_FMT_AUTO, ZGR_FMT_DENSE, ZGR_FMT_SPARSE, ZGR_FMT_DENSE_NEXT = 0, 1, 2, 3
 ZGR_PROJ_AUTO, ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE = 0, 1, 2
 ZGR_UPLOAD_STAGED, ZGR_UPLOAD_DIRECT = 0, 1
 UPLOAD_CODES = {"staged": ZGR_UPLOAD_STAGED, "direct": ZGR_UPLOAD_DIRECT}
+ZGR_SLICES_AUTO, ZGR_SLICES_ALWAYS, ZGR_SLICES_NEVER = 0, 1, 2
+SLICE_CODES = {"auto": ZGR_SLICES_AUTO, "always": ZGR_SLICES_ALWAYS, "never": ZGR_SLICES_NEVER}
 KERNELS = ["units", "selective", "gemm", "request", "norm"]
 ZGR_MODE_FILTER_FIRST, ZGR_MODE_SCORE_FIRST, ZGR_MODE_UNCONSTRAINED = 0, 1, 2
 MODE_CODES = {"filter_first": ZGR_MODE_FILTER_FIRST, "score_first": ZGR_MODE_SCORE_FIRST,
@@ -46,11 +48,12 @@ HIDDEN_FN = ctypes.CFUNCTYPE(ctypes.c_int32, _P, _I32, _I32, _I32, _P, _I32, _P,
 
 class StepStats(ctypes.Structure):
     _fields_ = [("rows", _I64), ("nnz", _I64), ("fmt", _I32), ("stride", _I32), ("bytes", _I64),
-                ("max_legal", _I32), ("reserved", _I32)]
+                ("max_legal", _I32), ("slice_dir", _I32)]
 
 
 class BuildOpts(ctypes.Structure):
-    _fields_ = [("host_threads", _I32), ("upload", _I32), ("staging_bytes", _I64)]
+    _fields_ = [("host_threads", _I32), ("upload", _I32), ("staging_bytes", _I64),
+                ("slices", _I32), ("reserved", _I32)]
 
 
 class BuildTimes(ctypes.Structure):
@@ -104,6 +107,7 @@ def lib() -> ctypes.CDLL:
             "zgr_index_stats": (_I32, [_P, _I32, ctypes.POINTER(StepStats)]),
             "zgr_index_host_table": (_I32, [_P, _I32, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                             ctypes.POINTER(_P)]),
+            "zgr_index_host_slices": (_I32, [_P, _I32, ctypes.POINTER(_P)]),
             "zgr_index_shape": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                        ctypes.POINTER(_I64)]),
             "zgr_index_free": (None, [_P]),
@@ -213,12 +217,13 @@ def _fmt_array(fmt, L):
     return a
 
 
-def _opts(threads: int, upload, staging_bytes: int):
-    if threads == 0 and upload in (None, "staged") and staging_bytes == 0:
+def _opts(threads: int, upload, staging_bytes: int, slices="auto"):
+    sl = SLICE_CODES[slices] if isinstance(slices, str) else int(slices)
+    if threads == 0 and upload in (None, "staged") and staging_bytes == 0 and sl == ZGR_SLICES_AUTO:
         return None
     code = UPLOAD_CODES[upload] if isinstance(upload, str) else (
         ZGR_UPLOAD_STAGED if upload is None else int(upload))
-    return BuildOpts(int(threads), code, int(staging_bytes))
+    return BuildOpts(int(threads), code, int(staging_bytes), sl, 0)
 
 
 def _ref(x):
@@ -226,16 +231,17 @@ def _ref(x):
 
 
 def zgr_index_build_host(sids: np.ndarray, V: int, fmt=None, want_rank: bool = True,
-                         threads: int = 0, times: bool = False):
-    """Host-only build on `threads` threads (0 = automatic).  Returns
-    (Index, rank_of_input int64 [N] or None), plus the phase times as a dict
-    when `times`."""
+                         threads: int = 0, times: bool = False, slices="auto"):
+    """Host-only build on `threads` threads (0 = automatic); `slices` is
+    "auto", "always" or "never" (the sparse tables' slice directory).
+    Returns (Index, rank_of_input int64 [N] or None), plus the phase times as
+    a dict when `times`."""
     sids = np.ascontiguousarray(sids, dtype=np.int32)
     N, L = sids.shape
     f = _fmt_array(fmt, L)
     rank = np.empty(N, dtype=np.int64) if want_rank else None
     h = ctypes.c_void_p()
-    o = _opts(threads, None, 0)
+    o = _opts(threads, None, 0, slices)
     tm = BuildTimes() if times else None
     fp = None if f is None else f.ctypes.data
     rp = None if rank is None else rank.ctypes.data
@@ -262,14 +268,14 @@ def zgr_index_to_device(index: Index, stream=None, threads: int = 0, upload=None
 
 
 def zgr_index_upload(sids: np.ndarray, V: int, fmt=None, stream=None, want_rank: bool = True,
-                     threads: int = 0, upload=None, staging_bytes: int = 0):
+                     threads: int = 0, upload=None, staging_bytes: int = 0, slices="auto"):
     """Build on the host and copy to HBM.  Returns (Index, rank_of_input)."""
     sids = np.ascontiguousarray(sids, dtype=np.int32)
     N, L = sids.shape
     f = _fmt_array(fmt, L)
     rank = np.empty(N, dtype=np.int64) if want_rank else None
     h = ctypes.c_void_p()
-    o = _opts(threads, upload, staging_bytes)
+    o = _opts(threads, upload, staging_bytes, slices)
     fp = None if f is None else f.ctypes.data
     rp = None if rank is None else rank.ctypes.data
     if o is None:
@@ -297,7 +303,7 @@ def zgr_index_device_table(index: Index, t: int):
 def zgr_index_stats(index: Index, t: int) -> dict:
     st = StepStats()
     _check(lib().zgr_index_stats(index.handle, t, ctypes.byref(st)))
-    return {k: getattr(st, k) for k, _ in StepStats._fields_ if k != "reserved"}
+    return {k: getattr(st, k) for k, _ in StepStats._fields_}
 
 
 def zgr_index_shape(index: Index):
@@ -323,6 +329,16 @@ def zgr_index_host_table(index: Index, t: int):
         bits = np.ctypeslib.as_array(ctypes.cast(bt, ctypes.POINTER(ctypes.c_uint32)),
                                      (rows, words)).copy()
     return row_ptr, tok, bits
+
+
+def zgr_index_host_slices(index: Index, t: int):
+    """Copy of table t's slice directory (uint16 [rows, 8]), or None when the table has none."""
+    sp = _P()
+    _check(lib().zgr_index_host_slices(index.handle, t, ctypes.byref(sp)))
+    if not sp.value:
+        return None
+    rows = zgr_index_stats(index, t)["rows"]
+    return np.ctypeslib.as_array(ctypes.cast(sp, ctypes.POINTER(ctypes.c_uint16)), (rows, 8)).copy()
 
 
 def zgr_index_free(index: Index):

@@ -31,7 +31,7 @@ namespace {
 // bitmap and its rank directory (dense), or the next-row matrix.
 int64_t table_device_bytes(const zgr::HostTable& h, int32_t words) {
   const int64_t rp = (h.rows + 1) * 4;
-  if (h.fmt == ZGR_FMT_SPARSE) return rp + h.nnz * 2;
+  if (h.fmt == ZGR_FMT_SPARSE) return rp + h.nnz * 2 + (int64_t)h.sdir.size() * 2;
   if (h.fmt == ZGR_FMT_DENSE_NEXT) return rp + h.rows * (int64_t)h.stride * 4;
   return rp + h.rows * (int64_t)words * 6;
 }
@@ -176,6 +176,9 @@ int32_t build_host(const int32_t* sids, int64_t N, int32_t L, int32_t V, const i
   if (V < 2 || V > 65536) return fail(ZGR_E_ARG, "zgr_index_build_host: V must be in [2, 65536]");
   if (opts && opts->host_threads < 0)
     return fail(ZGR_E_ARG, "zgr_index_build_host: host_threads must be >= 0");
+  const int32_t slices = opts ? opts->slices : ZGR_SLICES_AUTO;
+  if (slices < ZGR_SLICES_AUTO || slices > ZGR_SLICES_NEVER)
+    return fail(ZGR_E_ARG, "zgr_index_build_host: slices must be ZGR_SLICES_AUTO, _ALWAYS or _NEVER");
   int bits = 0;
   while ((1 << bits) < V) ++bits;
   if (bits * L > 64) return fail(ZGR_E_SHAPE, "zgr_index_build_host: ceil(log2 V) * L > 64");
@@ -366,6 +369,31 @@ int32_t build_host(const int32_t* sids, int64_t N, int32_t L, int32_t V, const i
                                    : want;
     const bool next_matrix = h.fmt == ZGR_FMT_DENSE_NEXT;
     h.stride = (h.fmt != ZGR_FMT_SPARSE) ? V : h.max_legal;
+    const bool want_sdir = h.fmt == ZGR_FMT_SPARSE &&
+                           (slices == ZGR_SLICES_ALWAYS ||
+                            (slices == ZGR_SLICES_AUTO && V >= 1024 && h.nnz >= 32 * h.rows));
+    if (want_sdir) {
+      // Slice directory: a row's legal tokens below the end of each codebook
+      // eighth (tokens are sorted, so one walk per row).  Counts below 7/8 of
+      // V stay under 2^16 for any V <= 65536.
+      try {
+        h.sdir.assign((size_t)h.rows * kSlices, 0);
+      } catch (...) {
+        delete idx;
+        return fail(ZGR_E_NOMEM, "zgr_index_build_host: host allocation");
+      }
+      const int32_t span = (V + kSlices - 1) / kSlices;
+      par_chunks(Tr, h.rows, [&](int64_t lo, int64_t hi, int) {
+        for (int64_t q = lo; q < hi; ++q) {
+          const int32_t b0 = h.row_ptr[q], b1 = h.row_ptr[q + 1];
+          int32_t j = b0;
+          for (int x = 0; x + 1 < kSlices; ++x) {
+            while (j < b1 && (int32_t)h.tok[j] < (x + 1) * span) ++j;
+            h.sdir[q * kSlices + x] = (uint16_t)(j - b0);
+          }
+        }
+      });
+    }
     if (h.fmt != ZGR_FMT_SPARSE) {
       try {
         h.bits.assign((size_t)h.rows * words, 0u);
@@ -456,13 +484,14 @@ int32_t upload_index(zgr_index* idx, void* stream, const zgr_build_opts* opts, z
     void** dst;
   };
   std::vector<Piece> pieces;
-  void* ptrs[kMaxL][5] = {};
+  void* ptrs[kMaxL][6] = {};
   size_t total = 0;
   for (int l = 0; l < idx->L; ++l) {
     const HostTable& h = idx->host[l];
     pieces.push_back({h.row_ptr.data(), h.row_ptr.size() * 4, &ptrs[l][0]});
     if (h.fmt == ZGR_FMT_SPARSE) {
       pieces.push_back({h.tok.data(), h.tok.size() * 2, &ptrs[l][1]});
+      if (!h.sdir.empty()) pieces.push_back({h.sdir.data(), h.sdir.size() * 2, &ptrs[l][5]});
     } else if (h.fmt == ZGR_FMT_DENSE_NEXT) {
       pieces.push_back({h.next.data(), h.next.size() * 4, &ptrs[l][4]});
     } else {
@@ -562,6 +591,7 @@ int32_t upload_index(zgr_index* idx, void* stream, const zgr_build_opts* opts, z
     d.bits = (const uint32_t*)ptrs[l][2];
     d.rank = (const uint16_t*)ptrs[l][3];
     d.next = (const int32_t*)ptrs[l][4];
+    d.sdir = (const uint16_t*)ptrs[l][5];
   }
   idx->on_device = true;
   if (times) *times = tm;
@@ -655,7 +685,7 @@ extern "C" int32_t zgr_index_stats(const zgr_index* idx, int32_t t, zgr_step_sta
   out->fmt = h.fmt;
   out->stride = h.stride;
   out->max_legal = h.max_legal;
-  out->reserved = 0;
+  out->slice_dir = h.sdir.empty() ? 0 : 1;
   out->bytes = table_device_bytes(h, (int32_t)words);
   return ZGR_OK;
 }
@@ -669,6 +699,15 @@ extern "C" int32_t zgr_index_host_table(const zgr_index* idx, int32_t t, const i
   if (row_ptr) *row_ptr = h.row_ptr.data();
   if (tok) *tok = h.tok.data();
   if (bits) *bits = h.fmt != ZGR_FMT_SPARSE ? h.bits.data() : nullptr;
+  return ZGR_OK;
+}
+
+extern "C" int32_t zgr_index_host_slices(const zgr_index* idx, int32_t t, const uint16_t** sdir) {
+  using namespace zgr;
+  if (!idx || !sdir) return fail(ZGR_E_ARG, "zgr_index_host_slices: null argument");
+  if (t < 1 || t > idx->L) return fail(ZGR_E_ARG, "zgr_index_host_slices: t out of range");
+  const HostTable& h = idx->host[t - 1];
+  *sdir = h.sdir.empty() ? nullptr : h.sdir.data();
   return ZGR_OK;
 }
 

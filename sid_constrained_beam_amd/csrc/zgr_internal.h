@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -16,6 +17,8 @@ constexpr int kMaxL = 8;
 // Internal table format: one row in which every codebook token is legal (the
 // unconstrained mode); laid out like a dense row.
 constexpr int32_t kFmtAll = 4;
+// Codebook slices of the slice directory: one per XCD of the MI355X.
+constexpr int kSlices = 8;
 
 // One step's table on the host.
 struct HostTable {
@@ -29,6 +32,7 @@ struct HostTable {
   std::vector<uint32_t> bits;    // dense: [rows][words]
   std::vector<uint16_t> rank;    // dense: [rows][words] set bits of the row before each word
   std::vector<int32_t> next;     // next-row matrix encoding: [rows][V], -1 = not legal
+  std::vector<uint16_t> sdir;    // sparse, optional: [rows][kSlices] slice directory
 };
 
 // One step's table in HBM (plain pointers, passed to kernels by value).
@@ -43,6 +47,7 @@ struct DevTable {
   const uint32_t* bits;  // dense only
   const uint16_t* rank;  // dense only: [rows][words] set bits of the row before each word
   const int32_t* next;   // next-row matrix encoding only: [rows][V], -1 = not legal
+  const uint16_t* sdir;  // sparse, optional: [rows][kSlices] legal tokens below each slice's end
 };
 
 }  // namespace zgr
@@ -91,8 +96,12 @@ struct StepArgs {
   // scratch
   float* z;             // score buffer
   int64_t ldz;          // its row stride
-  int32_t* nlegal;      // [M]
-  int32_t* unit_start;  // [M + 1]
+  int32_t* nlegal;      // [M] ([kSlices][M] for a sliced sparse table)
+  int32_t* unit_start;  // [M + 1] ([kSlices][M + 1] for a sliced sparse table)
+  int32_t* seg_base;    // sliced sparse table: [kSlices][M] first entry of each beam's run
+  uint32_t* seg_lon;    // sliced sparse table: [kSlices][M] first slot | length << 16
+  int4* umeta;          // sliced sparse table: [kSlices][ucap] (beam, first entry, first slot, size)
+  int64_t ucap;         // units per slice that umeta holds
   float* lse;           // [M] per-beam log-sum-exp over legal tokens
   float* lse_ext;       // [M] or null: normaliser given to the request kernel (score-first)
   bool plain_z;         // full projection writes token-indexed rows even on dense steps
@@ -146,5 +155,11 @@ hipError_t launch_decode_final(const int32_t* row, const float* cum, const int32
 // Tile of tokens handled by one work unit on dense steps, and of candidates on sparse steps.
 constexpr int kDenseTile = 1024;
 constexpr int kSparseTile = 64;
+// Units a beam can have in one codebook slice of a sliced sparse table: its
+// run there holds at most min(S_t, ceil(V / kSlices)) tokens.
+inline int64_t slice_units_per_beam(int32_t stride, int32_t V) {
+  const int64_t run = std::min<int64_t>(stride, (V + kSlices - 1) / kSlices);
+  return std::max<int64_t>(1, (run + kSparseTile - 1) / kSparseTile);
+}
 
 }  // namespace zgr

@@ -326,13 +326,26 @@ constexpr int kUnitsCache = 16384;
 // Per beam: legal count n_b and its work units (sparse: ceil(n_b / 64)
 // candidates; dense: ceil(V / 1024) token tiles), then the exclusive scan of
 // units over the M beams into unit_start[0..M] (unit_start[M] = total).
+// A sparse table with a slice directory runs kSlices blocks: block x takes
+// every beam's run of legal tokens in codebook slice x (its first entry in
+// seg_base, its first slot and length packed in seg_lon), scans those runs'
+// units into its own unit_start, nlegal, seg_base and seg_lon rows, and
+// writes each unit's (beam, first entry, first slot, size) to umeta[x][u],
+// so the selective projection reads a unit's place with one load.
 // The counts are read coalesced with kUnitsInFlight beams' row lookups in
 // flight per thread; the scan then runs over contiguous chunks per thread.
 constexpr int kUnitsInFlight = 8;
+template <bool SLICED>
 __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_in, int32_t M,
                                                 DevTable tab, int32_t* __restrict__ nlegal,
                                                 int32_t* __restrict__ unit_start,
+                                                int32_t* __restrict__ seg_base,
+                                                uint32_t* __restrict__ seg_lon,
+                                                int4* __restrict__ umeta, int64_t ucap,
                                                 int32_t* __restrict__ err) {
+  const int x = SLICED ? (int)blockIdx.x : 0;
+  nlegal += (int64_t)x * M;
+  unit_start += (int64_t)x * (M + 1);
   __shared__ int ucache[kUnitsCache];
   __shared__ int sh[16];
   constexpr int R = kUnitsInFlight;
@@ -341,8 +354,18 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
     if (n == 0) return 0;
     return is_dense(tab.fmt) ? dense_units : (n + kSparseTile - 1) / kSparseTile;
   };
+  // entry i of a row's slice directory (eight uint16 in one 16-byte word)
+  auto dir_entry = [](const uint4& d, int i) {
+    const uint32_t w = i < 2 ? d.x : (i < 4 ? d.y : (i < 6 ? d.z : d.w));
+    return (int)((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+  };
+  // sliced: this thread's beams' runs (kept for the unit places when every
+  // beam fits one pass, M <= 1024 R)
+  int keep_sb[R];
+  uint32_t keep_lon[R];
   for (int c = threadIdx.x; c < M; c += 1024 * R) {
     int r[R], lo[R], hi[R];
+    uint4 dir[R];
 #pragma unroll
     for (int u = 0; u < R; ++u) r[u] = row_in[min(c + u * 1024, M - 1)];
 #pragma unroll
@@ -350,13 +373,25 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
       const int rr = (r[u] >= 0 && r[u] < tab.rows) ? r[u] : 0;
       lo[u] = tab.row_ptr[rr];
       hi[u] = tab.row_ptr[rr + 1];
+      if constexpr (SLICED) dir[u] = *reinterpret_cast<const uint4*>(tab.sdir + (int64_t)rr * kSlices);
     }
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int b = c + u * 1024;
       if (b < M) {
-        if (r[u] >= tab.rows) atomicOr(err, 1);
-        const int n = (r[u] >= 0 && r[u] < tab.rows) ? hi[u] - lo[u] : 0;
+        if (r[u] >= tab.rows && x == 0) atomicOr(err, 1);
+        const bool live = r[u] >= 0 && r[u] < tab.rows;
+        int n = live ? hi[u] - lo[u] : 0;
+        if constexpr (SLICED) {
+          // the row's run of slice x: entries [first, end) of the row
+          const int first = (live && x > 0) ? dir_entry(dir[u], x - 1) : 0;
+          const int end = (x + 1 < kSlices) ? dir_entry(dir[u], x) : n;
+          n = live ? end - first : 0;
+          keep_sb[u] = lo[u] + first;
+          keep_lon[u] = (uint32_t)first | ((uint32_t)n << 16);
+          seg_base[(int64_t)x * M + b] = keep_sb[u];
+          seg_lon[(int64_t)x * M + b] = keep_lon[u];
+        }
         nlegal[b] = n;
         if (b < kUnitsCache) ucache[b] = units_of_n(n);
       }
@@ -391,6 +426,31 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
     carry += total;
   }
   if (threadIdx.x == 0) unit_start[M] = carry;
+  if constexpr (SLICED) {
+    // each unit's place: (beam, first entry, first slot, size)
+    umeta += (int64_t)x * ucap;
+    auto put = [&](int b, int s0, int s1, int sb, uint32_t lon) {
+      const int first = (int)(lon & 0xFFFFu), n = (int)(lon >> 16);
+      for (int k = 0; k < s1 - s0; ++k)
+        umeta[s0 + k] = make_int4(b, sb + k * kSparseTile, first + k * kSparseTile,
+                                  min(kSparseTile, n - k * kSparseTile));
+    };
+    if (M <= 1024 * R && M <= kUnitsCache) {
+      // one pass and one chunk: the prefixes are still in LDS and this
+      // thread's runs in registers
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int b = threadIdx.x + u * 1024;
+        if (b < M) put(b, ucache[b], b + 1 < M ? ucache[b + 1] : carry, keep_sb[u], keep_lon[u]);
+      }
+    } else {
+      // this block's own stores are read back (block scope)
+      __threadfence_block();
+      __syncthreads();
+      for (int b = threadIdx.x; b < M; b += 1024)
+        put(b, unit_start[b], unit_start[b + 1], seg_base[(int64_t)x * M + b], seg_lon[(int64_t)x * M + b]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- k_score_selective
@@ -438,6 +498,178 @@ __device__ __forceinline__ float group_sum_multi(float (&acc)[U], int gl) {
   return group_sum<G / U>(acc[0]);
 }
 
+typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2_t;
+
+// A lane group's gather-dot: the group's share of one beam's hidden vector
+// in registers (load_h), then U candidates at once (score): tok(u) gives
+// candidate u's token (callers clamp it to a real candidate, so every load is
+// in bounds) and slot(u) its z index; only the first nvalid are stored.  The
+// hidden share and the weight loads stay packed as loaded (16-bit types: two
+// values per register) and are widened element by element in the FMA chain,
+// which halves their registers; the FMA order is the element order.
+template <int DT, int D>
+struct GatherDot {
+  using S = SelShape<DT, D>;
+  static constexpr int G = S::G, NV = S::NV, ES = S::ES, U = S::U;
+  const char* Wb;
+  const char* hidden;
+  int gl;  // lane within the candidate group
+  uint4 h[NV];
+  __device__ __forceinline__ void load_h(int b) {
+    const char* hb = hidden + (int64_t)b * D * ES;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) h[c] = *(const uint4*)(hb + (int64_t)(c * G + gl) * 16);
+  }
+  // acc += the dot product of two packed 16-byte chunks, in element order
+  static __device__ __forceinline__ float dot16(const uint4& w, const uint4& x, float acc) {
+    const uint32_t a[4] = {w.x, w.y, w.z, w.w}, b[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == ZGR_F32) {
+        acc = fmaf(__uint_as_float(a[i]), __uint_as_float(b[i]), acc);
+      } else if constexpr (DT == ZGR_BF16) {
+        // two bf16 products (exact in f32) and the sum in one instruction
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a[i]),
+                                              __builtin_bit_cast(bf16x2_t, b[i]), acc, false);
+      } else {
+        acc = fmaf(f16_to_f32(a[i] & 0xFFFFu), f16_to_f32(b[i] & 0xFFFFu), acc);
+        acc = fmaf(f16_to_f32(a[i] >> 16), f16_to_f32(b[i] >> 16), acc);
+      }
+    }
+    return acc;
+  }
+  template <typename Tok, typename Slot>
+  __device__ __forceinline__ void score(float* zb, Tok&& tok, Slot&& slot, int nvalid) {
+    const char* wr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) wr[u] = Wb + (int64_t)tok(u) * D * ES;
+    uint4 w[U][NV];
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[u][c] = *(const uint4*)(wr[u] + (int64_t)(c * G + gl) * 16);
+    // the packed hidden share is opaque to the compiler here, so it widens it
+    // at each use instead of hoisting a widened copy (twice the registers)
+    if constexpr (DT != ZGR_F32) {
+#pragma unroll
+      for (int c = 0; c < NV; ++c) asm volatile("" : "+v"(h[c].x), "+v"(h[c].y), "+v"(h[c].z), "+v"(h[c].w));
+    }
+    float acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) acc[u] = dot16(w[u][c], h[c], acc[u]);
+    }
+    const float v = group_sum_multi<G, U>(acc, gl);
+    const int mine = gl / (G / U);
+    if (gl % (G / U) == 0 && mine < nvalid) zb[slot(mine)] = v;
+  }
+};
+
+// Selective projection of a sparse step: units (a beam's run of up to
+// kSparseTile candidates) in one contiguous range per block, each wave taking
+// every NW-th unit of the range on its own (no block barrier).  With a slice
+// directory the blocks are dealt to the XCDs in turn (block i runs on XCD
+// i mod 8), so block i takes slice i mod kSlices: the units of the beams'
+// runs of legal tokens in that eighth of the codebook, whose weight rows then
+// stay in the XCD's own L2 (the grid is a multiple of kSlices); a unit's
+// place comes from umeta in one load.  Without one, one search finds the
+// range's first beam and the beams advance with the unit index.  A kernel of
+// its own, so its register count (and so its occupancy) is not the dense
+// path's.
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void k_score_sparse(
+    const int32_t* __restrict__ unit_start, const int4* __restrict__ umeta, int64_t ucap,
+    int32_t M, DevTable tab, const int32_t* __restrict__ row_in, const void* __restrict__ hidden,
+    const void* __restrict__ W, float* __restrict__ z, int64_t ldz) {
+  using GD = GatherDot<DT, D>;
+  constexpr int G = GD::G, U = GD::U;
+  constexpr int NW = kThreads / 64, GW = 64 / G;  // waves per block, lane groups per wave
+  GD gd;
+  gd.Wb = (const char*)W;
+  gd.hidden = (const char*)hidden;
+  gd.gl = threadIdx.x % G;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x / 64, wg = (threadIdx.x % 64) / G;
+  if (tab.sdir != nullptr) {
+    const int x = (int)blockIdx.x % kSlices;
+    const int lb = (int)blockIdx.x / kSlices, nb = (int)gridDim.x / kSlices;
+    const int total = unit_start[(int64_t)x * (M + 1) + M];
+    const int chunk = (total + nb - 1) / nb;
+    const int u0 = lb * chunk, u1 = min(total, u0 + chunk);
+    const int4* um = umeta + (int64_t)x * ucap;
+    // each wave takes every NW-th unit of the block's range on its own (no
+    // block barrier); lane i holds the place of the wave's i-th unit of a
+    // round, and the next unit's tokens load while a unit is scored, so a
+    // unit waits only on its weight rows
+    for (int ub = u0 + wv; ub < u1; ub += NW * 64) {
+      const int ui = ub + lane * NW;
+      const int4 m = ui < u1 ? um[ui] : make_int4(0, 0, 0, 0);
+      const int nr = min(64, (u1 - ub + NW - 1) / NW);
+      int tk;
+      {
+        const int e0 = __builtin_amdgcn_readlane(m.y, 0), cnt = __builtin_amdgcn_readlane(m.w, 0);
+        tk = lane < cnt ? (int)tab.tok[e0 + lane] : 0;
+      }
+      for (int i = 0; i < nr; ++i) {
+        const int b = __builtin_amdgcn_readlane(m.x, i);
+        const int j0 = __builtin_amdgcn_readlane(m.z, i), cnt = __builtin_amdgcn_readlane(m.w, i);
+        int tk_next = 0;
+        if (i + 1 < nr) {
+          const int e0n = __builtin_amdgcn_readlane(m.y, i + 1);
+          const int cntn = __builtin_amdgcn_readlane(m.w, i + 1);
+          tk_next = lane < cntn ? (int)tab.tok[e0n + lane] : 0;
+        }
+        gd.load_h(b);
+        float* zb = z + (int64_t)b * ldz;
+        // the trip count is uniform over the wave (the token shuffle needs
+        // every lane); a group past the unit's end stores nothing
+        for (int jb = 0; jb < cnt; jb += GW * U) {
+          const int j = jb + wg;
+          const int nv = min(U, (cnt - j + GW - 1) / GW);
+          gd.score(
+              zb, [&](int u) { return __shfl(tk, min(j + u * GW, cnt - 1)); },
+              [&](int u) { return j0 + j + u * GW; }, nv);
+        }
+        tk = tk_next;
+      }
+    }
+    return;
+  }
+  const int total = unit_start[M];
+  const int chunk = (total + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int u0 = (int)blockIdx.x * chunk, u1 = min(total, u0 + chunk);
+  if (u0 >= u1) return;
+  int lo = 0, hi = M;  // the last b with unit_start[b] <= u0
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (unit_start[mid] <= u0)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  // each wave takes every NW-th unit of the range, walking the beams
+  int b = lo, next = unit_start[b + 1];
+  for (int u = u0 + wv; u < u1; u += NW) {
+    while (next <= u) next = unit_start[++b + 1];
+    const int tile = u - unit_start[b];
+    const int r = row_in[b];
+    const int base = tab.row_ptr[r];
+    const int j0 = tile * kSparseTile;
+    const int e0 = base + j0;
+    const int cnt = min(kSparseTile, tab.row_ptr[r + 1] - base - j0);
+    gd.load_h(b);
+    float* zb = z + (int64_t)b * ldz;
+    for (int j = wg; j < cnt; j += GW * U) {
+      const int nv = min(U, (cnt - j + GW - 1) / GW);
+      gd.score(
+          zb, [&](int u) { return (int)tab.tok[e0 + min(j + u * GW, cnt - 1)]; },
+          [&](int u) { return j0 + j + u * GW; }, nv);
+    }
+  }
+}
+
 template <int DT, int D, bool NX>
 __global__ __launch_bounds__(kThreads) void k_score_selective(
     const int32_t* __restrict__ unit_start, int32_t M, DevTable tab,
@@ -483,42 +715,6 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
     const int mine = gl / (G / U);
     if (gl % (G / U) == 0 && mine < nvalid) zb[slot(mine)] = v;
   };
-
-  if (tab.fmt == ZGR_FMT_SPARSE) {
-    // units (a beam's run of up to kSparseTile candidates) in one contiguous
-    // range per block: one search for the first unit's beam, then the beam
-    // advances with the unit index
-    const int total = unit_start[M];
-    const int chunk = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int u0 = (int)blockIdx.x * chunk, u1 = min(total, u0 + chunk);
-    if (u0 >= u1) return;
-    int lo = 0, hi = M;  // the last b with unit_start[b] <= u0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (unit_start[mid] <= u0)
-        lo = mid;
-      else
-        hi = mid;
-    }
-    int b = lo, next = unit_start[b + 1];
-    for (int u = u0; u < u1; ++u) {
-      while (next <= u) next = unit_start[++b + 1];
-      const int tile = u - unit_start[b];
-      const int r = row_in[b];
-      load_h(b);
-      float* zb = z + (int64_t)b * ldz;
-      const int base = tab.row_ptr[r];
-      const int n = tab.row_ptr[r + 1] - base;
-      const int j0 = tile * kSparseTile, j1 = min(n, j0 + kSparseTile);
-      for (int j = j0 + grp; j < j1; j += NG * U) {
-        const int nv = min(U, (j1 - j + NG - 1) / NG);
-        score_u(
-            zb, [&](int u) { return (int)tab.tok[base + min(j + u * NG, j1 - 1)]; },
-            [&](int u) { return j + u * NG; }, nv);
-      }
-    }
-    return;
-  }
 
   // Dense rows: every live beam has the same tiles of tt tokens (a multiple
   // of 32, at most kDenseTile; the host sizes a tile's weight rows to a
@@ -2128,10 +2324,22 @@ int resident_blocks_per_cu(Kernel kernel, int threads) {
 // d = 1024 f32: 1109 us at 5 blocks per CU, 1181 us at 6).
 constexpr int kSelMaxBlocksPerCu = 5;
 
+// At most this many sparse-projection blocks per CU (the occupancy query
+// decides below that).
+constexpr int kSparseMaxBlocksPerCu = 8;
+
 template <int DT, int D>
 hipError_t launch_sel_typed(const StepArgs& a, hipStream_t s) {
   const int32_t tt = dense_tile_tokens(D, DT);
-  if (a.tab.next) {
+  if (a.tab.fmt == ZGR_FMT_SPARSE) {
+    static const int per_cu =
+        std::min(kSparseMaxBlocksPerCu, resident_blocks_per_cu(k_score_sparse<DT, D>, kThreads));
+    // a sliced table needs a grid that is a multiple of kSlices
+    int grid = a.n_cu * per_cu;
+    if (a.tab.sdir) grid = std::max(kSlices, grid - grid % kSlices);
+    hipLaunchKernelGGL((k_score_sparse<DT, D>), dim3(grid), dim3(kThreads), 0, s, a.unit_start,
+                       a.umeta, a.ucap, a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
+  } else if (a.tab.next) {
     static const int per_cu =
         std::min(kSelMaxBlocksPerCu, resident_blocks_per_cu(k_score_selective<DT, D, true>, kThreads));
     hipLaunchKernelGGL((k_score_selective<DT, D, true>), dim3(a.n_cu * per_cu), dim3(kThreads), 0, s,
@@ -2228,8 +2436,12 @@ bool supported_hidden_size(int d) {
 }
 
 hipError_t launch_units(const StepArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_units, dim3(1), dim3(1024), 0, s, a.row_in, a.M, a.tab, a.nlegal,
-                     a.unit_start, a.err);
+  if (a.tab.sdir && a.tab.fmt == ZGR_FMT_SPARSE)
+    hipLaunchKernelGGL(k_units<true>, dim3(kSlices), dim3(1024), 0, s, a.row_in, a.M, a.tab,
+                       a.nlegal, a.unit_start, a.seg_base, a.seg_lon, a.umeta, a.ucap, a.err);
+  else
+    hipLaunchKernelGGL(k_units<false>, dim3(1), dim3(1024), 0, s, a.row_in, a.M, a.tab, a.nlegal,
+                       a.unit_start, a.seg_base, a.seg_lon, a.umeta, a.ucap, a.err);
   return hipGetLastError();
 }
 

@@ -50,12 +50,12 @@ def to_device_bits(bits, dtype):
 class Setup:
     """One workload on the GPU and in the oracle."""
 
-    def __init__(self, cfg, with_oracle=True, sids=None):
+    def __init__(self, cfg, with_oracle=True, sids=None, slices="auto"):
         import torch
         self.cfg = cfg
         self.sids = workload.catalog(cfg) if sids is None else np.ascontiguousarray(sids, np.int32)
         fmt = cfg.fmt
-        self.index, self.rank = zgr.zgr_index_upload(self.sids, cfg.V, fmt)
+        self.index, self.rank = zgr.zgr_index_upload(self.sids, cfg.V, fmt, slices=slices)
         self.W_bits, self.W_f32 = [], []
         for t in range(1, cfg.L + 1):
             b, f = workload.weights(cfg, t)

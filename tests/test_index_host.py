@@ -214,3 +214,59 @@ def test_encoding_bytes():
                     "N": rp + st["rows"] * cfg.V * 4}[f]
             assert st["bytes"] == want
             assert st["stride"] == (st["max_legal"] if f == "S" else cfg.V)
+
+
+def _long_row_sids(V, n1, per_row, seed):
+    """Two-level catalog: n1 first tokens, each with per_row distinct second tokens."""
+    rng = np.random.default_rng(seed)
+    first = rng.choice(V, n1, replace=False)
+    rows = [np.stack([np.full(per_row, f), rng.choice(V, per_row, replace=False)], 1) for f in first]
+    return np.concatenate(rows).astype(np.int32)
+
+
+@pytest.mark.parametrize("V,n1,per_row", [(4, 3, 3), (300, 20, 40), (1024, 16, 100), (5000, 8, 700),
+                                          (65536, 2, 9000)])
+def test_slice_directory(V, n1, per_row):
+    """Slice directory of sparse rows: entry x < 7 counts the row's legal
+    tokens (the oracle's trie children) below (x + 1) * ceil(V / 8); entry 7 is
+    0; the tables themselves do not depend on it."""
+    sids = _long_row_sids(V, n1, per_row, seed=V)
+    cat = oracle.Catalog(sids, V)
+    span = -(-V // 8)
+    never, _ = zgr.zgr_index_build_host(sids, V, ["S", "S"], slices="never")
+    idx, _ = zgr.zgr_index_build_host(sids, V, ["S", "S"], slices="always")
+    pre = row_prefixes(idx, 2)
+    for t in (1, 2):
+        assert zgr.zgr_index_host_slices(never, t) is None and never.stats(t)["slice_dir"] == 0
+        st = idx.stats(t)
+        assert st["slice_dir"] == 1
+        assert st["bytes"] == never.stats(t)["bytes"] + st["rows"] * 16
+        a, b = idx.host_table(t), never.host_table(t)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        sd = zgr.zgr_index_host_slices(idx, t)
+        assert sd.shape == (st["rows"], 8) and sd.dtype == np.uint16
+        for r in range(st["rows"]):
+            legal = np.asarray(cat.legal(pre[t - 1][r]), np.int64)
+            want = [int((legal < (x + 1) * span).sum()) for x in range(7)] + [0]
+            assert sd[r].tolist() == want
+
+
+def test_slice_directory_auto_rule_and_errors():
+    """AUTO: sparse tables with V >= 1024 and at least 32 legal tokens per row
+    on average; dense tables never; an unknown value is an argument error."""
+    seen = set()
+    for V, n1, per_row in [(2048, 40, 40), (2048, 40, 20), (512, 10, 60), (4096, 64, 200)]:
+        sids = _long_row_sids(V, n1, per_row, seed=n1 + per_row)
+        idx, _ = zgr.zgr_index_build_host(sids, V)
+        for t in (1, 2):
+            st = idx.stats(t)
+            want = st["fmt"] == zgr.ZGR_FMT_SPARSE and V >= 1024 and st["nnz"] >= 32 * st["rows"]
+            assert st["slice_dir"] == int(want), (V, n1, per_row, t, st)
+            assert (zgr.zgr_index_host_slices(idx, t) is not None) == want
+            seen.add(want)
+    assert seen == {True, False}
+    sids = _long_row_sids(2048, 40, 40, seed=1)
+    assert zgr.zgr_index_build_host(sids, 2048, ["D", "D"], slices="always")[0].stats(2)["slice_dir"] == 0
+    with pytest.raises(zgr.ZgrError) as e:
+        zgr.zgr_index_build_host(sids, 2048, slices=7)
+    assert e.value.status == zgr.ZGR_E_ARG
