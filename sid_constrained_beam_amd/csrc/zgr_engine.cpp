@@ -60,7 +60,7 @@ struct zgr_plan {
   int32_t* nlegal = nullptr;
   int32_t* unit_start = nullptr;
   int32_t* seg_base = nullptr;
-  uint32_t* seg_lon = nullptr;
+  int32_t* seg_first = nullptr;
   int4* umeta = nullptr;
   int64_t ucap = 0;
   float* lse = nullptr;
@@ -162,7 +162,7 @@ StepArgs make_args(zgr_plan* p, int32_t t, const void* hidden, const int32_t* ro
   a.nlegal = p->nlegal;
   a.unit_start = p->unit_start;
   a.seg_base = p->seg_base;
-  a.seg_lon = p->seg_lon;
+  a.seg_first = p->seg_first;
   a.umeta = p->umeta;
   a.ucap = p->ucap;
   a.lse = p->lse;
@@ -536,11 +536,12 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   A((void**)&p->nlegal, (size_t)kSlices * MK * 4);
   A((void**)&p->unit_start, (size_t)kSlices * (MK + 1) * 4);
   A((void**)&p->seg_base, (size_t)kSlices * MK * 4);
-  A((void**)&p->seg_lon, (size_t)kSlices * MK * 4);
-  // units of one slice: a beam's run there holds at most min(S_t, ceil(V / 8)) tokens
+  A((void**)&p->seg_first, (size_t)kSlices * MK * 4);
+  // unit places of one slice of a sparse step
   for (int l = 0; l < idx->L; ++l)
-    if (idx->dev[l].sdir)
-      p->ucap = std::max<int64_t>(p->ucap, MK * slice_units_per_beam(idx->host[l].stride, idx->V));
+    if (idx->host[l].fmt == ZGR_FMT_SPARSE)
+      p->ucap = std::max<int64_t>(
+          p->ucap, MK * slice_units_per_beam(idx->host[l].stride, idx->V, idx->dev[l].sdir != nullptr));
   if (p->ucap > 0) A((void**)&p->umeta, (size_t)kSlices * p->ucap * 16);
   A((void**)&p->lse, (size_t)MK * 4);
   A((void**)&p->part_keys, (size_t)B * kMaxParts * K * 8);
@@ -871,7 +872,8 @@ extern "C" int32_t zgr_step_noalloc(const zgr_index* idx, const void* W_t, int32
   const size_t o_units = take((size_t)(nsl * (M + 1)) * 4);
   const size_t o_segb = take((size_t)(nsl * M) * 4);
   const size_t o_segl = take((size_t)(nsl * M) * 4);
-  const int64_t ucap = nsl > 1 ? M * slice_units_per_beam(h.stride, idx->V) : 0;
+  const int64_t ucap =
+      h.fmt == ZGR_FMT_SPARSE ? M * slice_units_per_beam(h.stride, idx->V, !h.sdir.empty()) : 0;
   const size_t o_umeta = take((size_t)(nsl * ucap) * 16);
   const size_t o_lse = take((size_t)M * 4);
   const size_t o_z = take((size_t)M * ldz_max * 4);
@@ -918,7 +920,7 @@ extern "C" int32_t zgr_step_noalloc(const zgr_index* idx, const void* W_t, int32
   a.nlegal = (int32_t*)(base + o_nlegal);
   a.unit_start = (int32_t*)(base + o_units);
   a.seg_base = (int32_t*)(base + o_segb);
-  a.seg_lon = (uint32_t*)(base + o_segl);
+  a.seg_first = (int32_t*)(base + o_segl);
   a.umeta = (int4*)(base + o_umeta);
   a.ucap = ucap;
   a.lse = (float*)(base + o_lse);

@@ -96,11 +96,11 @@ struct StepArgs {
   // scratch
   float* z;             // score buffer
   int64_t ldz;          // its row stride
-  int32_t* nlegal;      // [M] ([kSlices][M] for a sliced sparse table)
-  int32_t* unit_start;  // [M + 1] ([kSlices][M + 1] for a sliced sparse table)
-  int32_t* seg_base;    // sliced sparse table: [kSlices][M] first entry of each beam's run
-  uint32_t* seg_lon;    // sliced sparse table: [kSlices][M] first slot | length << 16
-  int4* umeta;          // sliced sparse table: [kSlices][ucap] (beam, first entry, first slot, size)
+  int32_t* nlegal;      // [slices][M] legal count of each beam's run (sparse steps)
+  int32_t* unit_start;  // [slices][M + 1] unit prefix over the beams (sparse steps)
+  int32_t* seg_base;    // sparse: [slices][M] first entry of each beam's run
+  int32_t* seg_first;   // sparse: [slices][M] first slot of each beam's run
+  int4* umeta;          // sparse: [slices][ucap] (beam, first entry, first slot, size) per unit
   int64_t ucap;         // units per slice that umeta holds
   float* lse;           // [M] per-beam log-sum-exp over legal tokens
   float* lse_ext;       // [M] or null: normaliser given to the request kernel (score-first)
@@ -155,10 +155,10 @@ hipError_t launch_decode_final(const int32_t* row, const float* cum, const int32
 // Tile of tokens handled by one work unit on dense steps, and of candidates on sparse steps.
 constexpr int kDenseTile = 1024;
 constexpr int kSparseTile = 64;
-// Units a beam can have in one codebook slice of a sliced sparse table: its
-// run there holds at most min(S_t, ceil(V / kSlices)) tokens.
-inline int64_t slice_units_per_beam(int32_t stride, int32_t V) {
-  const int64_t run = std::min<int64_t>(stride, (V + kSlices - 1) / kSlices);
+// Units a beam can have in one slice of a sparse table: its run there holds
+// at most S_t tokens, and with a slice directory at most ceil(V / kSlices).
+inline int64_t slice_units_per_beam(int32_t stride, int32_t V, bool sliced) {
+  const int64_t run = sliced ? std::min<int64_t>(stride, (V + kSlices - 1) / kSlices) : stride;
   return std::max<int64_t>(1, (run + kSparseTile - 1) / kSparseTile);
 }
 

@@ -323,46 +323,44 @@ __device__ __forceinline__ DWord dense_word(const DevTable& tab, int64_t r, int 
 
 constexpr int kUnitsCache = 16384;
 
-// Per beam: legal count n_b and its work units (sparse: ceil(n_b / 64)
-// candidates; dense: ceil(V / 1024) token tiles), then the exclusive scan of
-// units over the M beams into unit_start[0..M] (unit_start[M] = total).
-// A sparse table with a slice directory runs kSlices blocks: block x takes
-// every beam's run of legal tokens in codebook slice x (its first entry in
-// seg_base, its first slot and length packed in seg_lon), scans those runs'
-// units into its own unit_start, nlegal, seg_base and seg_lon rows, and
-// writes each unit's (beam, first entry, first slot, size) to umeta[x][u],
-// so the selective projection reads a unit's place with one load.
-// The counts are read coalesced with kUnitsInFlight beams' row lookups in
-// flight per thread; the scan then runs over contiguous chunks per thread.
+// Before the selective projection of a sparse step: every beam's run of
+// legal tokens (the whole row, or with a slice directory its tokens in one
+// eighth of the codebook), the run's units of up to kSparseTile candidates,
+// the exclusive scan of the units over the M beams into unit_start[0..M]
+// (unit_start[M] = total), and each unit's place (beam, first entry of the
+// token list, first slot, size) in umeta, so the projection reads a unit's
+// place with one load.  A sliced table runs kSlices blocks, block x taking
+// slice x into its own rows of nlegal, unit_start, seg_base, seg_first and
+// umeta; otherwise one block.  The counts are read coalesced with
+// kUnitsInFlight beams' row lookups in flight per thread; the scan runs over
+// contiguous chunks per thread.
 constexpr int kUnitsInFlight = 8;
 template <bool SLICED>
 __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_in, int32_t M,
                                                 DevTable tab, int32_t* __restrict__ nlegal,
                                                 int32_t* __restrict__ unit_start,
                                                 int32_t* __restrict__ seg_base,
-                                                uint32_t* __restrict__ seg_lon,
+                                                int32_t* __restrict__ seg_first,
                                                 int4* __restrict__ umeta, int64_t ucap,
                                                 int32_t* __restrict__ err) {
   const int x = SLICED ? (int)blockIdx.x : 0;
   nlegal += (int64_t)x * M;
   unit_start += (int64_t)x * (M + 1);
+  seg_base += (int64_t)x * M;
+  seg_first += (int64_t)x * M;
+  umeta += (int64_t)x * ucap;
   __shared__ int ucache[kUnitsCache];
   __shared__ int sh[16];
   constexpr int R = kUnitsInFlight;
-  const int dense_units = (tab.V + kDenseTile - 1) / kDenseTile;
-  auto units_of_n = [&](int n) {
-    if (n == 0) return 0;
-    return is_dense(tab.fmt) ? dense_units : (n + kSparseTile - 1) / kSparseTile;
-  };
+  auto units_of_n = [](int n) { return (n + kSparseTile - 1) / kSparseTile; };
   // entry i of a row's slice directory (eight uint16 in one 16-byte word)
   auto dir_entry = [](const uint4& d, int i) {
     const uint32_t w = i < 2 ? d.x : (i < 4 ? d.y : (i < 6 ? d.z : d.w));
     return (int)((i & 1) ? (w >> 16) : (w & 0xFFFFu));
   };
-  // sliced: this thread's beams' runs (kept for the unit places when every
-  // beam fits one pass, M <= 1024 R)
-  int keep_sb[R];
-  uint32_t keep_lon[R];
+  // this thread's beams' runs, kept for the unit places when every beam fits
+  // one pass (M <= 1024 R)
+  int keep_sb[R], keep_first[R], keep_n[R];
   for (int c = threadIdx.x; c < M; c += 1024 * R) {
     int r[R], lo[R], hi[R];
     uint4 dir[R];
@@ -382,16 +380,18 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
         if (r[u] >= tab.rows && x == 0) atomicOr(err, 1);
         const bool live = r[u] >= 0 && r[u] < tab.rows;
         int n = live ? hi[u] - lo[u] : 0;
+        int first = 0;
         if constexpr (SLICED) {
           // the row's run of slice x: entries [first, end) of the row
-          const int first = (live && x > 0) ? dir_entry(dir[u], x - 1) : 0;
+          first = (live && x > 0) ? dir_entry(dir[u], x - 1) : 0;
           const int end = (x + 1 < kSlices) ? dir_entry(dir[u], x) : n;
           n = live ? end - first : 0;
-          keep_sb[u] = lo[u] + first;
-          keep_lon[u] = (uint32_t)first | ((uint32_t)n << 16);
-          seg_base[(int64_t)x * M + b] = keep_sb[u];
-          seg_lon[(int64_t)x * M + b] = keep_lon[u];
         }
+        keep_sb[u] = lo[u] + first;
+        keep_first[u] = first;
+        keep_n[u] = n;
+        seg_base[b] = keep_sb[u];
+        seg_first[b] = first;
         nlegal[b] = n;
         if (b < kUnitsCache) ucache[b] = units_of_n(n);
       }
@@ -426,30 +426,27 @@ __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_
     carry += total;
   }
   if (threadIdx.x == 0) unit_start[M] = carry;
-  if constexpr (SLICED) {
-    // each unit's place: (beam, first entry, first slot, size)
-    umeta += (int64_t)x * ucap;
-    auto put = [&](int b, int s0, int s1, int sb, uint32_t lon) {
-      const int first = (int)(lon & 0xFFFFu), n = (int)(lon >> 16);
-      for (int k = 0; k < s1 - s0; ++k)
-        umeta[s0 + k] = make_int4(b, sb + k * kSparseTile, first + k * kSparseTile,
-                                  min(kSparseTile, n - k * kSparseTile));
-    };
-    if (M <= 1024 * R && M <= kUnitsCache) {
-      // one pass and one chunk: the prefixes are still in LDS and this
-      // thread's runs in registers
+  // each unit's place: (beam, first entry, first slot, size)
+  auto put = [&](int b, int s0, int s1, int sb, int first, int n) {
+    for (int k = 0; k < s1 - s0; ++k)
+      umeta[s0 + k] = make_int4(b, sb + k * kSparseTile, first + k * kSparseTile,
+                                min(kSparseTile, n - k * kSparseTile));
+  };
+  if (M <= 1024 * R && M <= kUnitsCache) {
+    // one pass and one chunk: the prefixes are still in LDS and this
+    // thread's runs in registers
 #pragma unroll
-      for (int u = 0; u < R; ++u) {
-        const int b = threadIdx.x + u * 1024;
-        if (b < M) put(b, ucache[b], b + 1 < M ? ucache[b + 1] : carry, keep_sb[u], keep_lon[u]);
-      }
-    } else {
-      // this block's own stores are read back (block scope)
-      __threadfence_block();
-      __syncthreads();
-      for (int b = threadIdx.x; b < M; b += 1024)
-        put(b, unit_start[b], unit_start[b + 1], seg_base[(int64_t)x * M + b], seg_lon[(int64_t)x * M + b]);
+    for (int u = 0; u < R; ++u) {
+      const int b = threadIdx.x + u * 1024;
+      if (b < M)
+        put(b, ucache[b], b + 1 < M ? ucache[b + 1] : carry, keep_sb[u], keep_first[u], keep_n[u]);
     }
+  } else {
+    // this block's own stores are read back (block scope)
+    __threadfence_block();
+    __syncthreads();
+    for (int b = threadIdx.x; b < M; b += 1024)
+      put(b, unit_start[b], unit_start[b + 1], seg_base[b], seg_first[b], nlegal[b]);
   }
 }
 
@@ -568,16 +565,14 @@ struct GatherDot {
 };
 
 // Selective projection of a sparse step: units (a beam's run of up to
-// kSparseTile candidates) in one contiguous range per block, each wave taking
-// every NW-th unit of the range on its own (no block barrier).  With a slice
-// directory the blocks are dealt to the XCDs in turn (block i runs on XCD
-// i mod 8), so block i takes slice i mod kSlices: the units of the beams'
-// runs of legal tokens in that eighth of the codebook, whose weight rows then
-// stay in the XCD's own L2 (the grid is a multiple of kSlices); a unit's
-// place comes from umeta in one load.  Without one, one search finds the
-// range's first beam and the beams advance with the unit index.  A kernel of
-// its own, so its register count (and so its occupancy) is not the dense
-// path's.
+// kSparseTile candidates, placed by k_units) in one contiguous range per
+// block, each wave taking every NW-th unit of the range on its own (no block
+// barrier).  With a slice directory the blocks are dealt to the XCDs in turn
+// (block i runs on XCD i mod 8), so block i takes slice i mod kSlices: the
+// units of the beams' runs of legal tokens in that eighth of the codebook,
+// whose weight rows then stay in the XCD's own L2 (the grid is a multiple of
+// kSlices).  A kernel of its own, so its register count (and so its
+// occupancy) is not the dense path's.
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_score_sparse(
     const int32_t* __restrict__ unit_start, const int4* __restrict__ umeta, int64_t ucap,
@@ -592,80 +587,49 @@ __global__ __launch_bounds__(kThreads) void k_score_sparse(
   gd.gl = threadIdx.x % G;
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x / 64, wg = (threadIdx.x % 64) / G;
-  if (tab.sdir != nullptr) {
-    const int x = (int)blockIdx.x % kSlices;
-    const int lb = (int)blockIdx.x / kSlices, nb = (int)gridDim.x / kSlices;
-    const int total = unit_start[(int64_t)x * (M + 1) + M];
-    const int chunk = (total + nb - 1) / nb;
-    const int u0 = lb * chunk, u1 = min(total, u0 + chunk);
-    const int4* um = umeta + (int64_t)x * ucap;
-    // each wave takes every NW-th unit of the block's range on its own (no
-    // block barrier); lane i holds the place of the wave's i-th unit of a
-    // round, and the next unit's tokens load while a unit is scored, so a
-    // unit waits only on its weight rows
-    for (int ub = u0 + wv; ub < u1; ub += NW * 64) {
-      const int ui = ub + lane * NW;
-      const int4 m = ui < u1 ? um[ui] : make_int4(0, 0, 0, 0);
-      const int nr = min(64, (u1 - ub + NW - 1) / NW);
-      int tk;
-      {
-        const int e0 = __builtin_amdgcn_readlane(m.y, 0), cnt = __builtin_amdgcn_readlane(m.w, 0);
-        tk = lane < cnt ? (int)tab.tok[e0 + lane] : 0;
-      }
-      for (int i = 0; i < nr; ++i) {
-        const int b = __builtin_amdgcn_readlane(m.x, i);
-        const int j0 = __builtin_amdgcn_readlane(m.z, i), cnt = __builtin_amdgcn_readlane(m.w, i);
-        int tk_next = 0;
-        if (i + 1 < nr) {
-          const int e0n = __builtin_amdgcn_readlane(m.y, i + 1);
-          const int cntn = __builtin_amdgcn_readlane(m.w, i + 1);
-          tk_next = lane < cntn ? (int)tab.tok[e0n + lane] : 0;
-        }
-        gd.load_h(b);
-        float* zb = z + (int64_t)b * ldz;
-        // the trip count is uniform over the wave (the token shuffle needs
-        // every lane); a group past the unit's end stores nothing
-        for (int jb = 0; jb < cnt; jb += GW * U) {
-          const int j = jb + wg;
-          const int nv = min(U, (cnt - j + GW - 1) / GW);
-          gd.score(
-              zb, [&](int u) { return __shfl(tk, min(j + u * GW, cnt - 1)); },
-              [&](int u) { return j0 + j + u * GW; }, nv);
-        }
-        tk = tk_next;
-      }
+  // slice x of the blocks' residues mod nsl (one slice, whole rows, without
+  // a directory)
+  const int nsl = tab.sdir != nullptr ? kSlices : 1;
+  const int x = (int)blockIdx.x % nsl;
+  const int lb = (int)blockIdx.x / nsl, nb = (int)gridDim.x / nsl;
+  const int total = unit_start[(int64_t)x * (M + 1) + M];
+  const int chunk = (total + nb - 1) / nb;
+  const int u0 = lb * chunk, u1 = min(total, u0 + chunk);
+  const int4* um = umeta + (int64_t)x * ucap;
+  // each wave takes every NW-th unit of the block's range on its own (no
+  // block barrier); lane i holds the place of the wave's i-th unit of a
+  // round, and the next unit's tokens load while a unit is scored, so a
+  // unit waits only on its weight rows
+  for (int ub = u0 + wv; ub < u1; ub += NW * 64) {
+    const int ui = ub + lane * NW;
+    const int4 m = ui < u1 ? um[ui] : make_int4(0, 0, 0, 0);
+    const int nr = min(64, (u1 - ub + NW - 1) / NW);
+    int tk;
+    {
+      const int e0 = __builtin_amdgcn_readlane(m.y, 0), cnt = __builtin_amdgcn_readlane(m.w, 0);
+      tk = lane < cnt ? (int)tab.tok[e0 + lane] : 0;
     }
-    return;
-  }
-  const int total = unit_start[M];
-  const int chunk = (total + (int)gridDim.x - 1) / (int)gridDim.x;
-  const int u0 = (int)blockIdx.x * chunk, u1 = min(total, u0 + chunk);
-  if (u0 >= u1) return;
-  int lo = 0, hi = M;  // the last b with unit_start[b] <= u0
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (unit_start[mid] <= u0)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  // each wave takes every NW-th unit of the range, walking the beams
-  int b = lo, next = unit_start[b + 1];
-  for (int u = u0 + wv; u < u1; u += NW) {
-    while (next <= u) next = unit_start[++b + 1];
-    const int tile = u - unit_start[b];
-    const int r = row_in[b];
-    const int base = tab.row_ptr[r];
-    const int j0 = tile * kSparseTile;
-    const int e0 = base + j0;
-    const int cnt = min(kSparseTile, tab.row_ptr[r + 1] - base - j0);
-    gd.load_h(b);
-    float* zb = z + (int64_t)b * ldz;
-    for (int j = wg; j < cnt; j += GW * U) {
-      const int nv = min(U, (cnt - j + GW - 1) / GW);
-      gd.score(
-          zb, [&](int u) { return (int)tab.tok[e0 + min(j + u * GW, cnt - 1)]; },
-          [&](int u) { return j0 + j + u * GW; }, nv);
+    for (int i = 0; i < nr; ++i) {
+      const int b = __builtin_amdgcn_readlane(m.x, i);
+      const int j0 = __builtin_amdgcn_readlane(m.z, i), cnt = __builtin_amdgcn_readlane(m.w, i);
+      int tk_next = 0;
+      if (i + 1 < nr) {
+        const int e0n = __builtin_amdgcn_readlane(m.y, i + 1);
+        const int cntn = __builtin_amdgcn_readlane(m.w, i + 1);
+        tk_next = lane < cntn ? (int)tab.tok[e0n + lane] : 0;
+      }
+      gd.load_h(b);
+      float* zb = z + (int64_t)b * ldz;
+      // the trip count is uniform over the wave (the token shuffle needs
+      // every lane); a group past the unit's end stores nothing
+      for (int jb = 0; jb < cnt; jb += GW * U) {
+        const int j = jb + wg;
+        const int nv = min(U, (cnt - j + GW - 1) / GW);
+        gd.score(
+            zb, [&](int u) { return __shfl(tk, min(j + u * GW, cnt - 1)); },
+            [&](int u) { return j0 + j + u * GW; }, nv);
+      }
+      tk = tk_next;
     }
   }
 }
@@ -2438,10 +2402,10 @@ bool supported_hidden_size(int d) {
 hipError_t launch_units(const StepArgs& a, hipStream_t s) {
   if (a.tab.sdir && a.tab.fmt == ZGR_FMT_SPARSE)
     hipLaunchKernelGGL(k_units<true>, dim3(kSlices), dim3(1024), 0, s, a.row_in, a.M, a.tab,
-                       a.nlegal, a.unit_start, a.seg_base, a.seg_lon, a.umeta, a.ucap, a.err);
+                       a.nlegal, a.unit_start, a.seg_base, a.seg_first, a.umeta, a.ucap, a.err);
   else
     hipLaunchKernelGGL(k_units<false>, dim3(1), dim3(1024), 0, s, a.row_in, a.M, a.tab, a.nlegal,
-                       a.unit_start, a.seg_base, a.seg_lon, a.umeta, a.ucap, a.err);
+                       a.unit_start, a.seg_base, a.seg_first, a.umeta, a.ucap, a.err);
   return hipGetLastError();
 }
 
