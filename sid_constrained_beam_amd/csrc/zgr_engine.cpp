@@ -238,20 +238,34 @@ bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
 // the LDS key array (a part whose keys do not fit recomputes them from the
 // scores in each pass, which costs more than more parts: measured on the
 // dense-early catalog's second step); the parts' best K keys must fit the
-// merge's LDS.
+// merge's LDS.  When those parts would take more than four rounds of blocks
+// at two per compute unit, slot-indexed steps use big parts instead (the
+// merge-sized key array, one block per compute unit): each part's fixed cost
+// (the request's rows, the log-sum-exp reads of its beams) then repeats far
+// less often.
 constexpr double kSmallRequest = 6144.0;
 constexpr double kPartCandidates = 2048.0;
 constexpr double kPartMaxCandidates = 0.9 * kKeyCapHost;
-int32_t request_parts(const zgr_plan* p, const StepArgs& a) {
+constexpr double kBigPartMaxCandidates = 0.9 * kMergeCapHost;
+int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool* big) {
+  *big = false;
   const HostTable& h = p->idx->host[a.t - 1];
   double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
   if (a.tab.fmt == kFmtAll) mean_n = p->V;
   const double est_c = a.k_in * std::min<double>(mean_n, a.tab.stride);
   if (est_c <= kSmallRequest) return 1;
+  const int merge_cap = kMergeCapHost / std::max(1, a.K);
   const int p_occ = std::max(1, 2 * p->n_cu / std::max(1, a.B));
   int P = std::min((int)std::ceil(est_c / kPartCandidates), p_occ);
   P = std::max(P, (int)std::ceil(est_c / kPartMaxCandidates));
-  P = std::min({P, kMaxParts, kMergeCapHost / std::max(1, a.K)});
+  if (!a.z_token && (double)a.B * P > 4.0 * 2 * p->n_cu) {
+    const int Pb = (int)std::ceil(est_c / kBigPartMaxCandidates);
+    if (Pb <= std::min(kMaxParts, merge_cap)) {
+      *big = true;
+      return std::max(2, Pb);
+    }
+  }
+  P = std::min({P, kMaxParts, merge_cap});
   return std::max(1, P);
 }
 
@@ -279,7 +293,7 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     }
     zmode = unc ? 1 : 0;
     a.z_token = zmode == 0;
-    a.parts = request_parts(p, a);
+    a.parts = request_parts(p, a, &a.big_parts);
     e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
     if (e != hipSuccess) return hip_fail(e, "request step launch");
     if (a.parts > 1) {
@@ -344,7 +358,8 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     zmode = 1;
   }
   a.z_token = zmode == 0;
-  a.parts = request_parts(p, a);
+  a.parts = request_parts(p, a, &a.big_parts);
+  if (zmode != 1) a.big_parts = false;  // big parts are slot-indexed only
   e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
   if (e != hipSuccess) return hip_fail(e, "request step launch");
   if (a.parts > 1) {

@@ -107,6 +107,7 @@ struct StepArgs {
   bool plain_z;         // full projection writes token-indexed rows even on dense steps
   bool z_token;         // the request kernel reads token-indexed score rows (zmode 0)
   int32_t parts;        // blocks per request in the request kernel (1 = no merge)
+  bool big_parts;       // slot-indexed parts with the merge-sized key array (one block per CU)
   uint64_t* part_keys;  // [B * parts][K] best keys of each part
   int32_t* part_cnt;    // [B * parts]
   float2* part_ms;      // [B * parts] single-beam parts: (max, sum of exp) of their range

@@ -902,7 +902,9 @@ __device__ __forceinline__ int dist_bin(uint32_t d) {
 // computed by the request kernel itself (selective projection of a light
 // sparse step: gather-dot in the block, no separate launches); kZParts is the
 // merge of a request split over several blocks.
-enum ZMode { kZToken = 0, kZSlot = 1, kZScore = 2, kZParts = 3 };
+// kZSlotBig: kZSlot with the merge-sized key array (one block per CU), for
+// requests so large that small parts would repeat their fixed cost too often.
+enum ZMode { kZToken = 0, kZSlot = 1, kZScore = 2, kZParts = 3, kZSlotBig = 4 };
 
 // Combine two (max, sum of exp(x - max)) partials; lanes that saw nothing hold
 // (-inf, 0).  Symmetric, so both butterfly partners get identical bits.
@@ -964,7 +966,8 @@ void k_request_step(
   constexpr int NT = kSelThreads;
   constexpr bool TOKEN_IDX = (MODE == kZToken);
   constexpr bool MERGE = (MODE == kZParts);
-  __shared__ uint64_t keys[MERGE ? kMergeCap : kKeyCap];
+  constexpr int KEYCAP = (MERGE || MODE == kZSlotBig) ? kMergeCap : kKeyCap;
+  __shared__ uint64_t keys[KEYCAP];
   // sel (the selection) and dhist (the distance histogram, then the boundary
   // keys) from phase 4 on; before that the log-sum-exp pass keeps its unit
   // partials and the unit prefix over the beams here
@@ -1040,13 +1043,17 @@ void k_request_step(
   // reduced by GL lanes with UL loads each per pass; GL follows the
   // request's mean legal count (1 lane for the one or two legal tokens of a
   // late step, 16 for rows of hundreds) and SEG = GL * UL * 2^s is the
-  // smallest that keeps any part's units within kUnitCap.  Both depend only
-  // on the request, so every part reduces a beam the same way.
+  // smallest that keeps any part's units within kUnitCap.  A part touches
+  // its own ceil(Cq / P) candidates plus at most two beams' worth (S each)
+  // beyond them, so its units are at most that over SEG plus one per beam.
+  // Both depend only on the request, so every part reduces a beam the same
+  // way.
   constexpr int UL = 8;
   const int mean_n = Cq / max(1, k_in);
   const int GL = mean_n >= 64 ? 16 : (mean_n >= 8 ? 4 : 1);
+  const int64_t touch = ((int64_t)Cq + P - 1) / P + 2 * (int64_t)S;
   int SEG = GL * UL;
-  while ((Cq + SEG - 1) / SEG + k_in > kUnitCap) SEG *= 2;
+  while ((touch + SEG - 1) / SEG + k_in + 1 > kUnitCap) SEG *= 2;
   if (!MERGE && !zkey) {  // uniform; split single-beam parts reduce only their own range
     int Uq;
     const int uex = block_excl_scan<NT>((cnt + SEG - 1) / SEG, sh, &Uq);
@@ -1077,7 +1084,7 @@ void k_request_step(
   const int bl_lo = C > 0 ? bl_lo_sh : 0;
   const int bl_hi = C > 0 ? bl_hi_sh : -1;
   const int e0 = C > 0 ? cpre[bl_lo] : 0, e1 = C > 0 ? cpre[bl_hi + 1] : 0;
-  bool store = C <= kKeyCap;
+  bool store = C <= KEYCAP;
   auto code_of = [&](int b, int slot) { return (uint32_t)b * S + (uint32_t)slot; };
 
   //    (kZScore) selective projection inside the block: U2 candidates per
@@ -2472,6 +2479,14 @@ hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s) {
     else
       hipLaunchKernelGGL((k_request_step<kZToken, ZGR_F32, 64, false>), grid, dim3(kSelThreads), 0, s,
                          ZGR_STEP_ARGS);
+    e = hipGetLastError();
+  } else if (a.big_parts) {
+    if (a.tab.next)
+      hipLaunchKernelGGL((k_request_step<kZSlotBig, ZGR_F32, 64, true>), grid, dim3(kSelThreads), 0, s,
+                         ZGR_STEP_ARGS);
+    else
+      hipLaunchKernelGGL((k_request_step<kZSlotBig, ZGR_F32, 64, false>), grid, dim3(kSelThreads), 0,
+                         s, ZGR_STEP_ARGS);
     e = hipGetLastError();
   } else {
     if (a.tab.next)
