@@ -57,12 +57,10 @@ struct zgr_plan {
   std::vector<void*> allocations;
   float* z = nullptr;
   int64_t z_elems = 0;
-  int32_t* nlegal = nullptr;
   int32_t* unit_start = nullptr;
-  int32_t* seg_base = nullptr;
-  int32_t* seg_first = nullptr;
+  int32_t* ctot = nullptr;
   int4* umeta = nullptr;
-  int64_t ucap = 0;
+  int64_t chunk_cap = 0;
   float* lse = nullptr;
   uint64_t* part_keys = nullptr;
   int32_t* part_cnt = nullptr;
@@ -159,12 +157,10 @@ StepArgs make_args(zgr_plan* p, int32_t t, const void* hidden, const int32_t* ro
   a.prefix_in = prefix_in;
   a.prefix_out = prefix_out;
   a.z = p->z;
-  a.nlegal = p->nlegal;
   a.unit_start = p->unit_start;
-  a.seg_base = p->seg_base;
-  a.seg_first = p->seg_first;
+  a.ctot = p->ctot;
   a.umeta = p->umeta;
-  a.ucap = p->ucap;
+  a.chunk_cap = p->chunk_cap;
   a.lse = p->lse;
   a.parts = 1;
   a.part_keys = p->part_keys;
@@ -350,6 +346,9 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
   } else {
     a.ldz = a.tab.stride;
     if (!dense) {  // dense rows all have the same tiles: no unit scan needed
+      if ((a.M + 1023) / 1024 > kMaxUnitChunksHost)
+        return fail(ZGR_E_SHAPE, "selective projection of a sparse step: more than " +
+                                     std::to_string(1024 * kMaxUnitChunksHost) + " beams");
       e = prof_launch(p, ZGR_KERNEL_UNITS, t, s, [&] { return launch_units(a, s); });
       if (e != hipSuccess) return hip_fail(e, "unit count launch");
     }
@@ -548,16 +547,15 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   };
   A((void**)&p->z, (size_t)zmax * 4);
   // unit scans: one row per codebook slice when a sparse table is sliced
-  A((void**)&p->nlegal, (size_t)kSlices * MK * 4);
-  A((void**)&p->unit_start, (size_t)kSlices * (MK + 1) * 4);
-  A((void**)&p->seg_base, (size_t)kSlices * MK * 4);
-  A((void**)&p->seg_first, (size_t)kSlices * MK * 4);
-  // unit places of one slice of a sparse step
+  A((void**)&p->unit_start, (size_t)(MK + 1) * 4);
+  // sparse projection: unit totals and places per slice and 1,024-beam chunk
+  const int64_t nq_max = (MK + 1023) / 1024;
+  A((void**)&p->ctot, (size_t)kSlices * nq_max * 4);
   for (int l = 0; l < idx->L; ++l)
     if (idx->host[l].fmt == ZGR_FMT_SPARSE)
-      p->ucap = std::max<int64_t>(
-          p->ucap, MK * slice_units_per_beam(idx->host[l].stride, idx->V, idx->dev[l].sdir != nullptr));
-  if (p->ucap > 0) A((void**)&p->umeta, (size_t)kSlices * p->ucap * 16);
+      p->chunk_cap = std::max<int64_t>(
+          p->chunk_cap, 1024 * slice_units_per_beam(idx->host[l].stride, idx->V, idx->dev[l].sdir != nullptr));
+  if (p->chunk_cap > 0) A((void**)&p->umeta, (size_t)kSlices * nq_max * p->chunk_cap * 16);
   A((void**)&p->lse, (size_t)MK * 4);
   A((void**)&p->part_keys, (size_t)B * kMaxParts * K * 8);
   A((void**)&p->part_cnt, (size_t)B * kMaxParts * 4);
@@ -883,13 +881,12 @@ extern "C" int32_t zgr_step_noalloc(const zgr_index* idx, const void* W_t, int32
   const size_t o_pms = take((size_t)B * kMaxParts * 8);
   const size_t o_pkeys = take((size_t)B * kMaxParts * K * 8);
   const int64_t nsl = (h.fmt == ZGR_FMT_SPARSE && !h.sdir.empty()) ? kSlices : 1;
-  const size_t o_nlegal = take((size_t)(nsl * M) * 4);
-  const size_t o_units = take((size_t)(nsl * (M + 1)) * 4);
-  const size_t o_segb = take((size_t)(nsl * M) * 4);
-  const size_t o_segl = take((size_t)(nsl * M) * 4);
-  const int64_t ucap =
-      h.fmt == ZGR_FMT_SPARSE ? M * slice_units_per_beam(h.stride, idx->V, !h.sdir.empty()) : 0;
-  const size_t o_umeta = take((size_t)(nsl * ucap) * 16);
+  const size_t o_units = take((size_t)(M + 1) * 4);
+  const int64_t nq = (M + 1023) / 1024;
+  const size_t o_ctot = take((size_t)(nsl * nq) * 4);
+  const int64_t chunk_cap =
+      h.fmt == ZGR_FMT_SPARSE ? 1024 * slice_units_per_beam(h.stride, idx->V, !h.sdir.empty()) : 0;
+  const size_t o_umeta = take((size_t)(nsl * nq * chunk_cap) * 16);
   const size_t o_lse = take((size_t)M * 4);
   const size_t o_z = take((size_t)M * ldz_max * 4);
   if (off > kNoAllocScratchBytes)
@@ -932,12 +929,10 @@ extern "C" int32_t zgr_step_noalloc(const zgr_index* idx, const void* W_t, int32
   a.cum_out = cum_out;
   a.slot_dbg = slot_dbg;
   a.z = (float*)(base + o_z);
-  a.nlegal = (int32_t*)(base + o_nlegal);
   a.unit_start = (int32_t*)(base + o_units);
-  a.seg_base = (int32_t*)(base + o_segb);
-  a.seg_first = (int32_t*)(base + o_segl);
+  a.ctot = (int32_t*)(base + o_ctot);
   a.umeta = (int4*)(base + o_umeta);
-  a.ucap = ucap;
+  a.chunk_cap = chunk_cap;
   a.lse = (float*)(base + o_lse);
   a.parts = 1;
   a.part_keys = (uint64_t*)(base + o_pkeys);

@@ -96,12 +96,11 @@ struct StepArgs {
   // scratch
   float* z;             // score buffer
   int64_t ldz;          // its row stride
-  int32_t* nlegal;      // [slices][M] legal count of each beam's run (sparse steps)
-  int32_t* unit_start;  // [slices][M + 1] unit prefix over the beams (sparse steps)
-  int32_t* seg_base;    // sparse: [slices][M] first entry of each beam's run
-  int32_t* seg_first;   // sparse: [slices][M] first slot of each beam's run
-  int4* umeta;          // sparse: [slices][ucap] (beam, first entry, first slot, size) per unit
-  int64_t ucap;         // units per slice that umeta holds
+  int32_t* unit_start;  // [M + 1] candidate prefix over the beams (naive baseline)
+  int32_t* ctot;        // sparse projection: [slices][chunks] units of each 1,024-beam chunk
+  int4* umeta;          // sparse projection: [slices][chunks][chunk_cap] unit places
+                        // (beam, first entry, first slot, size)
+  int64_t chunk_cap;    // unit places one chunk of one slice can hold
   float* lse;           // [M] per-beam log-sum-exp over legal tokens
   float* lse_ext;       // [M] or null: normaliser given to the request kernel (score-first)
   bool plain_z;         // full projection writes token-indexed rows even on dense steps
@@ -156,6 +155,8 @@ hipError_t launch_decode_final(const int32_t* row, const float* cum, const int32
 // Tile of tokens handled by one work unit on dense steps, and of candidates on sparse steps.
 constexpr int kDenseTile = 1024;
 constexpr int kSparseTile = 64;
+// Beam chunks (1,024 beams each) a sparse projection can take: M <= 1024 times this.
+constexpr int kMaxUnitChunksHost = 2048;
 // Units a beam can have in one slice of a sparse table: its run there holds
 // at most S_t tokens, and with a slice directory at most ceil(V / kSlices).
 inline int64_t slice_units_per_beam(int32_t stride, int32_t V, bool sliced) {

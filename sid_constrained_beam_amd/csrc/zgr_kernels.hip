@@ -13,20 +13,23 @@
 // read in place: no compacted candidate list and no temporary matrix.
 //
 // Kernels of a step:
-//   k_units            sparse steps, per beam: legal count n_b and its number
-//                      of work units; an exclusive scan over the M beams (not
-//                      over candidates: slot addresses never depend on other
-//                      beams).
-//   k_score_selective  persistent grid over (beam, tile) units: each unit
-//                      reads the beam's legal tokens (sparse: tok[row_ptr[r]+j],
-//                      a contiguous range of units per block; dense: set bits
-//                      of a 1024-token tile of the row's bitmap, tiles split
-//                      over the XCDs so each XCD's L2 holds its tiles' weight
-//                      rows) and computes z = W_t[token] . h_beam with the
-//                      weight row read in place by a group of lanes (16-byte
-//                      loads), h kept in registers, a lane-group shuffle
-//                      reduction, z stored at the slot (sparse: rank j; dense:
-//                      the token's legal rank).
+//   k_units            sparse steps, per beam: its run of legal tokens (the
+//                      row, or its tokens in one codebook eighth when the
+//                      table has a slice directory) and the run's work units;
+//                      an exclusive scan per 1,024-beam chunk (not over
+//                      candidates: slot addresses never depend on other
+//                      beams) and each unit's place.
+//   k_score_sparse     persistent grid over a sparse step's units, a slice per
+//                      XCD when sliced: each wave scores its units' candidates,
+//                      z = W_t[token] . h_beam with the weight row read in
+//                      place by a group of lanes (16-byte loads), h kept in
+//                      registers, a lane-group shuffle reduction, z stored at
+//                      the slot (the token's rank in the row).
+//   k_score_selective  the same on dense rows: persistent grid over (beam,
+//                      tile) pairs, the set bits of a 1024-token tile of the
+//                      row's bitmap, tiles split over the XCDs so each XCD's L2
+//                      holds its tiles' weight rows; z stored at the token's
+//                      legal rank.
 //   k_gemm_nt          full projection Z = H . W_t^T on MFMA (fp32, bf16, f16
 //                      inputs; fp32 accumulate), Z row = beam, column = token;
 //   k_gemm_small       the same product for few beams (first step): 16x16 MFMA.
@@ -321,133 +324,53 @@ __device__ __forceinline__ DWord dense_word(const DevTable& tab, int64_t r, int 
 
 // ---------------------------------------------------------------- k_units
 
-constexpr int kUnitsCache = 16384;
-
 // Before the selective projection of a sparse step: every beam's run of
 // legal tokens (the whole row, or with a slice directory its tokens in one
-// eighth of the codebook), the run's units of up to kSparseTile candidates,
-// the exclusive scan of the units over the M beams into unit_start[0..M]
-// (unit_start[M] = total), and each unit's place (beam, first entry of the
-// token list, first slot, size) in umeta, so the projection reads a unit's
-// place with one load.  A sliced table runs kSlices blocks, block x taking
-// slice x into its own rows of nlegal, unit_start, seg_base, seg_first and
-// umeta; otherwise one block.  The counts are read coalesced with
-// kUnitsInFlight beams' row lookups in flight per thread; the scan runs over
-// contiguous chunks per thread.
-constexpr int kUnitsInFlight = 8;
+// eighth of the codebook) and the run's units of up to kSparseTile
+// candidates.  Block (chunk q, slice x) takes beams [1024 q, 1024 q + 1024)
+// of slice x, one per thread: it scans its beams' units, writes the chunk's
+// unit total to ctot[x][q] and each unit's place (beam, first entry of the
+// token list, first slot, size) to umeta[x][q][unit], so the projection reads
+// a unit's place with one load and no block scans more than 1,024 beams.
+// Blocks are numbered q * slices + x.
 template <bool SLICED>
 __global__ __launch_bounds__(1024) void k_units(const int32_t* __restrict__ row_in, int32_t M,
-                                                DevTable tab, int32_t* __restrict__ nlegal,
-                                                int32_t* __restrict__ unit_start,
-                                                int32_t* __restrict__ seg_base,
-                                                int32_t* __restrict__ seg_first,
-                                                int4* __restrict__ umeta, int64_t ucap,
+                                                DevTable tab, int32_t* __restrict__ ctot,
+                                                int4* __restrict__ umeta, int64_t chunk_cap,
                                                 int32_t* __restrict__ err) {
-  const int x = SLICED ? (int)blockIdx.x : 0;
-  nlegal += (int64_t)x * M;
-  unit_start += (int64_t)x * (M + 1);
-  seg_base += (int64_t)x * M;
-  seg_first += (int64_t)x * M;
-  umeta += (int64_t)x * ucap;
-  __shared__ int ucache[kUnitsCache];
+  constexpr int NSL = SLICED ? kSlices : 1;
+  const int x = (int)blockIdx.x % NSL, q = (int)blockIdx.x / NSL;
+  const int nq = (M + 1023) / 1024;
   __shared__ int sh[16];
-  constexpr int R = kUnitsInFlight;
-  auto units_of_n = [](int n) { return (n + kSparseTile - 1) / kSparseTile; };
-  // entry i of a row's slice directory (eight uint16 in one 16-byte word)
-  auto dir_entry = [](const uint4& d, int i) {
-    const uint32_t w = i < 2 ? d.x : (i < 4 ? d.y : (i < 6 ? d.z : d.w));
-    return (int)((i & 1) ? (w >> 16) : (w & 0xFFFFu));
-  };
-  // this thread's beams' runs, kept for the unit places when every beam fits
-  // one pass (M <= 1024 R)
-  int keep_sb[R], keep_first[R], keep_n[R];
-  for (int c = threadIdx.x; c < M; c += 1024 * R) {
-    int r[R], lo[R], hi[R];
-    uint4 dir[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) r[u] = row_in[min(c + u * 1024, M - 1)];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int rr = (r[u] >= 0 && r[u] < tab.rows) ? r[u] : 0;
-      lo[u] = tab.row_ptr[rr];
-      hi[u] = tab.row_ptr[rr + 1];
-      if constexpr (SLICED) dir[u] = *reinterpret_cast<const uint4*>(tab.sdir + (int64_t)rr * kSlices);
+  const int b = q * 1024 + (int)threadIdx.x;
+  int n = 0, first = 0, sb = 0;
+  if (b < M) {
+    const int r = row_in[b];
+    const bool live = r >= 0 && r < tab.rows;
+    if (r >= tab.rows && x == 0) atomicOr(err, 1);
+    const int rr = live ? r : 0;
+    const int lo = tab.row_ptr[rr], hi = tab.row_ptr[rr + 1];
+    n = live ? hi - lo : 0;
+    if constexpr (SLICED) {
+      // the row's run of slice x: entries [first, end) of the row (entry i of
+      // the directory: the row's tokens below the end of slice i)
+      const uint4 d = *reinterpret_cast<const uint4*>(tab.sdir + (int64_t)rr * kSlices);
+      const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+      auto entry = [&](int i) { return (int)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu)); };
+      first = (live && x > 0) ? entry(x - 1) : 0;
+      const int end = (x + 1 < kSlices) ? entry(x) : n;
+      n = live ? end - first : 0;
     }
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int b = c + u * 1024;
-      if (b < M) {
-        if (r[u] >= tab.rows && x == 0) atomicOr(err, 1);
-        const bool live = r[u] >= 0 && r[u] < tab.rows;
-        int n = live ? hi[u] - lo[u] : 0;
-        int first = 0;
-        if constexpr (SLICED) {
-          // the row's run of slice x: entries [first, end) of the row
-          first = (live && x > 0) ? dir_entry(dir[u], x - 1) : 0;
-          const int end = (x + 1 < kSlices) ? dir_entry(dir[u], x) : n;
-          n = live ? end - first : 0;
-        }
-        keep_sb[u] = lo[u] + first;
-        keep_first[u] = first;
-        keep_n[u] = n;
-        seg_base[b] = keep_sb[u];
-        seg_first[b] = first;
-        nlegal[b] = n;
-        if (b < kUnitsCache) ucache[b] = units_of_n(n);
-      }
-    }
+    sb = lo + first;
   }
-  // The scan runs over chunks of kUnitsCache beams held in LDS (the first
-  // chunk was filled above; later ones are refilled from nlegal, coalesced):
-  // each thread sums a contiguous piece, the block scans the sums, each thread
-  // turns its piece into prefixes in place, and the chunk is written out
-  // coalesced.  carry is the units of the chunks before.
-  int carry = 0;
-  for (int c0 = 0; c0 < M; c0 += kUnitsCache) {
-    const int n = min(kUnitsCache, M - c0);
-    __syncthreads();  // pass 1 (or the previous chunk's write-out) is done with ucache
-    if (c0 > 0) {
-      for (int i = threadIdx.x; i < n; i += 1024) ucache[i] = units_of_n(nlegal[c0 + i]);
-      __syncthreads();
-    }
-    const int per = (n + 1023) / 1024;
-    const int b0 = min(n, (int)threadIdx.x * per), b1 = min(n, b0 + per);
-    int mine = 0;
-    for (int b = b0; b < b1; ++b) mine += ucache[b];
-    int total;
-    int run = carry + block_excl_scan<1024>(mine, sh, &total);
-    for (int b = b0; b < b1; ++b) {
-      const int u = ucache[b];
-      ucache[b] = run;
-      run += u;
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 1024) unit_start[c0 + i] = ucache[i];
-    carry += total;
-  }
-  if (threadIdx.x == 0) unit_start[M] = carry;
-  // each unit's place: (beam, first entry, first slot, size)
-  auto put = [&](int b, int s0, int s1, int sb, int first, int n) {
-    for (int k = 0; k < s1 - s0; ++k)
-      umeta[s0 + k] = make_int4(b, sb + k * kSparseTile, first + k * kSparseTile,
-                                min(kSparseTile, n - k * kSparseTile));
-  };
-  if (M <= 1024 * R && M <= kUnitsCache) {
-    // one pass and one chunk: the prefixes are still in LDS and this
-    // thread's runs in registers
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int b = threadIdx.x + u * 1024;
-      if (b < M)
-        put(b, ucache[b], b + 1 < M ? ucache[b + 1] : carry, keep_sb[u], keep_first[u], keep_n[u]);
-    }
-  } else {
-    // this block's own stores are read back (block scope)
-    __threadfence_block();
-    __syncthreads();
-    for (int b = threadIdx.x; b < M; b += 1024)
-      put(b, unit_start[b], unit_start[b + 1], seg_base[b], seg_first[b], nlegal[b]);
-  }
+  const int units = (n + kSparseTile - 1) / kSparseTile;
+  int tot;
+  const int s0 = block_excl_scan<1024>(units, sh, &tot);
+  if (threadIdx.x == 0) ctot[x * nq + q] = tot;
+  int4* um = umeta + ((int64_t)x * nq + q) * chunk_cap;
+  for (int k = 0; k < units; ++k)
+    um[s0 + k] = make_int4(b, sb + k * kSparseTile, first + k * kSparseTile,
+                           min(kSparseTile, n - k * kSparseTile));
 }
 
 // ---------------------------------------------------------------- k_score_selective
@@ -573,11 +496,15 @@ struct GatherDot {
 // whose weight rows then stay in the XCD's own L2 (the grid is a multiple of
 // kSlices).  A kernel of its own, so its register count (and so its
 // occupancy) is not the dense path's.
+// Beam chunks of the unit kernel a sparse projection can take (its LDS
+// prefix of chunk totals): M <= 1024 kMaxUnitChunks beams.
+constexpr int kMaxUnitChunks = kMaxUnitChunksHost;
+
 template <int DT, int D>
 __global__ __launch_bounds__(kThreads) void k_score_sparse(
-    const int32_t* __restrict__ unit_start, const int4* __restrict__ umeta, int64_t ucap,
-    int32_t M, DevTable tab, const int32_t* __restrict__ row_in, const void* __restrict__ hidden,
-    const void* __restrict__ W, float* __restrict__ z, int64_t ldz) {
+    const int32_t* __restrict__ ctot, const int4* __restrict__ umeta, int64_t chunk_cap,
+    int32_t M, DevTable tab, const void* __restrict__ hidden, const void* __restrict__ W,
+    float* __restrict__ z, int64_t ldz) {
   using GD = GatherDot<DT, D>;
   constexpr int G = GD::G, U = GD::U;
   constexpr int NW = kThreads / 64, GW = 64 / G;  // waves per block, lane groups per wave
@@ -588,21 +515,47 @@ __global__ __launch_bounds__(kThreads) void k_score_sparse(
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x / 64, wg = (threadIdx.x % 64) / G;
   // slice x of the blocks' residues mod nsl (one slice, whole rows, without
-  // a directory)
+  // a directory); the slice's units are numbered over its beam chunks in
+  // order, from the chunks' totals (prefix in LDS, by wave 0)
+  __shared__ int cpre[kMaxUnitChunks + 1];
   const int nsl = tab.sdir != nullptr ? kSlices : 1;
   const int x = (int)blockIdx.x % nsl;
   const int lb = (int)blockIdx.x / nsl, nb = (int)gridDim.x / nsl;
-  const int total = unit_start[(int64_t)x * (M + 1) + M];
+  const int nq = (M + 1023) / 1024;
+  if (wv == 0) {
+    int carry = 0;
+    for (int i0 = 0; i0 < nq; i0 += 64) {
+      const int v = i0 + lane < nq ? ctot[x * nq + i0 + lane] : 0;
+      const int incl = wave_incl_scan(v);
+      if (i0 + lane < nq) cpre[i0 + lane] = carry + incl - v;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) cpre[nq] = carry;
+  }
+  __syncthreads();
+  const int total = cpre[nq];
   const int chunk = (total + nb - 1) / nb;
   const int u0 = lb * chunk, u1 = min(total, u0 + chunk);
-  const int4* um = umeta + (int64_t)x * ucap;
+  const int4* um = umeta + (int64_t)x * nq * chunk_cap;
+  // unit u of the slice: chunk q (the last with cpre[q] <= u), its unit u - cpre[q]
+  auto place_of = [&](int u) {
+    int lo = 0, hi = nq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cpre[mid] <= u)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    return (int64_t)lo * chunk_cap + (u - cpre[lo]);
+  };
   // each wave takes every NW-th unit of the block's range on its own (no
   // block barrier); lane i holds the place of the wave's i-th unit of a
   // round, and the next unit's tokens load while a unit is scored, so a
   // unit waits only on its weight rows
   for (int ub = u0 + wv; ub < u1; ub += NW * 64) {
     const int ui = ub + lane * NW;
-    const int4 m = ui < u1 ? um[ui] : make_int4(0, 0, 0, 0);
+    const int4 m = ui < u1 ? um[place_of(ui)] : make_int4(0, 0, 0, 0);
     const int nr = min(64, (u1 - ub + NW - 1) / NW);
     int tk;
     {
@@ -2308,8 +2261,8 @@ hipError_t launch_sel_typed(const StepArgs& a, hipStream_t s) {
     // a sliced table needs a grid that is a multiple of kSlices
     int grid = a.n_cu * per_cu;
     if (a.tab.sdir) grid = std::max(kSlices, grid - grid % kSlices);
-    hipLaunchKernelGGL((k_score_sparse<DT, D>), dim3(grid), dim3(kThreads), 0, s, a.unit_start,
-                       a.umeta, a.ucap, a.M, a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
+    hipLaunchKernelGGL((k_score_sparse<DT, D>), dim3(grid), dim3(kThreads), 0, s, a.ctot, a.umeta,
+                       a.chunk_cap, a.M, a.tab, a.hidden, a.W, a.z, a.ldz);
   } else if (a.tab.next) {
     static const int per_cu =
         std::min(kSelMaxBlocksPerCu, resident_blocks_per_cu(k_score_selective<DT, D, true>, kThreads));
@@ -2407,12 +2360,13 @@ bool supported_hidden_size(int d) {
 }
 
 hipError_t launch_units(const StepArgs& a, hipStream_t s) {
+  const int nq = (a.M + 1023) / 1024;
   if (a.tab.sdir && a.tab.fmt == ZGR_FMT_SPARSE)
-    hipLaunchKernelGGL(k_units<true>, dim3(kSlices), dim3(1024), 0, s, a.row_in, a.M, a.tab,
-                       a.nlegal, a.unit_start, a.seg_base, a.seg_first, a.umeta, a.ucap, a.err);
+    hipLaunchKernelGGL(k_units<true>, dim3(nq * kSlices), dim3(1024), 0, s, a.row_in, a.M, a.tab,
+                       a.ctot, a.umeta, a.chunk_cap, a.err);
   else
-    hipLaunchKernelGGL(k_units<false>, dim3(1), dim3(1024), 0, s, a.row_in, a.M, a.tab, a.nlegal,
-                       a.unit_start, a.seg_base, a.seg_first, a.umeta, a.ucap, a.err);
+    hipLaunchKernelGGL(k_units<false>, dim3(nq), dim3(1024), 0, s, a.row_in, a.M, a.tab, a.ctot,
+                       a.umeta, a.chunk_cap, a.err);
   return hipGetLastError();
 }
 
