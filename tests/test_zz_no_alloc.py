@@ -14,13 +14,17 @@ from workload import CONFIGS
 pytestmark = pytest.mark.gpu
 
 CFG = CONFIGS["n1e6_v2048"].scaled(N=100_000, B=4, K=32)
+# the same catalog with sparse steps 2-3 carrying a slice directory (the
+# sliced projection's work lists live in the static array too)
+CFG_SLICED = CFG.scaled(fmt=["D", "S", "S"])
 _setup = {}
 
 
-def setup():
-    if "s" not in _setup:
-        _setup["s"] = gu.Setup(CFG)
-    return _setup["s"]
+def setup(sliced=False):
+    key = "sliced" if sliced else "s"
+    if key not in _setup:
+        _setup[key] = gu.Setup(CFG_SLICED, slices="always") if sliced else gu.Setup(CFG)
+    return _setup[key]
 
 
 def step_inputs(s, t, requests, k_in):
@@ -54,16 +58,19 @@ def outputs(B, K, M, S):
                 dbg=torch.empty(M * S, dtype=torch.float32, device="cuda"))
 
 
+@pytest.mark.parametrize("sliced", [False, True])
 @pytest.mark.parametrize("proj", ["selective", "full"])
-def test_noalloc_step_matches_plan_step(proj):
+def test_noalloc_step_matches_plan_step(proj, sliced):
     import torch
-    s = setup()
+    s = setup(sliced)
+    if sliced:
+        assert s.stats[1]["slice_dir"] == 1 and s.stats[2]["slice_dir"] == 1
     cfg = s.cfg
     K = cfg.K
     # call 1: step 2, four requests of K beams; call 2: step 3, two requests of K / 2 beams
     for t, requests, k_in in ((2, [0, 1, 2, 3], K), (3, [1, 3], K // 2)):
         B = len(requests)
-        print(f"[noalloc] {proj} step {t} B={B} k_in={k_in}", flush=True)
+        print(f"[noalloc] {proj} sliced={sliced} step {t} B={B} k_in={k_in}", flush=True)
         inp = step_inputs(s, t, requests, k_in)
         S = s.stats[t - 1]["stride"]
         plan = zgr.zgr_plan_warmup(s.index, s.W_dev, cfg.dtype, cfg.d, B, K, None, 0, [proj] * cfg.L)
@@ -78,7 +85,7 @@ def test_noalloc_step_matches_plan_step(proj):
                              got["cum"], got["dbg"], err)
         torch.cuda.synchronize()
         for k in ref:
-            assert torch.equal(ref[k], got[k]), (proj, t, k)
+            assert torch.equal(ref[k], got[k]), (proj, sliced, t, k)
         assert int(err.item()) == 0
         assert int((got["parent"] >= 0).sum().item()) > 0
         plan.free()
