@@ -1203,6 +1203,54 @@ void k_request_step(
           else
             final_lse(bl, float_of_ord(bmo[bl - bl_lo]), 1.f);
         }
+    } else if (!TOKEN_IDX && MODE != kZScore && GL == 16 && S <= 4 * 64 * UL) {
+      // rows of 64 or more legal tokens on average and at most 2,048 each
+      // (the table's slot stride): one wave per beam, at most four passes
+      // (longer rows go to the units below, which split a beam).  Lane
+      // i reads the beam's scores i, i + 64, ... in passes of 8 (contiguous
+      // per load), each pass reduced to (max, sum of exp) without branches
+      // and joined in order, then the wave's lanes in a fixed butterfly: the
+      // same value in every part that touches the beam.  The part's own
+      // candidates also go to keys[].
+      for (int b = bl_lo + wave; b <= bl_hi; b += kSelWaves) {  // uniform over the wave
+        const int n_b = cpre[b + 1] - cpre[b];
+        if (n_b == 0) continue;
+        const float* zb = z + (int64_t)(b0 + b) * ldz;
+        float m = -INFINITY, sm = 0.f;
+        for (int jb = 0; jb < n_b; jb += 64 * UL) {
+          float zv[UL];
+#pragma unroll
+          for (int i = 0; i < UL; ++i) {
+            const int j = jb + i * 64 + lane;
+            zv[i] = j < n_b ? zb[j] : -INFINITY;
+          }
+          float pm = zv[0];
+#pragma unroll
+          for (int i = 1; i < UL; ++i) pm = fmaxf(pm, zv[i]);
+          float ps = 0.f;
+          if (pm != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < UL; ++i) ps += __expf(zv[i] - pm);
+          }
+          lse_combine(m, sm, pm, ps);
+#pragma unroll
+          for (int i = 0; i < UL; ++i) {
+            const int j = jb + i * 64 + lane;
+            const int f = cpre[b] + j;
+            if (store && j < n_b && f >= f0 && f < f1) {
+              // sparse rows: slot = legal rank; dense rows (rank-indexed
+              // scores): the code goes in after this pass
+              const uint32_t code = dense ? 0u : code_of(b, j);
+              keys[f - f0] = ((uint64_t)__float_as_uint(zv[i]) << 32) | code;
+            }
+          }
+        }
+        xor_down<32>([&](auto o) {
+          constexpr int X = decltype(o)::value;
+          lse_combine(m, sm, xor_lane<X>(m), xor_lane<X>(sm));
+        });
+        if (lane == 0) final_lse(b, m, sm);
+      }
     } else {
       // unit u of the part (u_lo + u is the request's unit) to a 16-lane
       // group; the group's lanes read the unit's scores at a stride of 16
