@@ -834,6 +834,8 @@ constexpr int kMergeCap = kMergeCapHost;  // the parts' best keys a merge holds 
 // selection's LDS (before the selection needs it)
 constexpr int kUnitCap = 1400;
 constexpr int kMaxK = 1024;
+// candidates of a wave-sized log-sum-exp unit (four passes of eight per lane)
+constexpr int kWaveUnit = 4 * 8 * 64;
 
 // Distance histogram: 64 exact bins for distances below 64 ulps, then 64
 // sub-bins per octave (monotone in the distance; 1728 bins used).
@@ -1005,7 +1007,12 @@ void k_request_step(
   const int mean_n = Cq / max(1, k_in);
   const int GL = mean_n >= 64 ? 16 : (mean_n >= 8 ? 4 : 1);
   const int64_t touch = ((int64_t)Cq + P - 1) / P + 2 * (int64_t)S;
-  int SEG = GL * UL;
+  // scores at their slots, rows of 64 or more on average that either fit one
+  // wave-sized unit (the slot stride is at most 2,048) or hold 256 or more on
+  // average: wave-sized units of 2,048 candidates, one wave each (below)
+  const bool wave_units =
+      !TOKEN_IDX && MODE != kZScore && GL == 16 && ((int)S <= kWaveUnit || mean_n >= 256);
+  int SEG = wave_units ? kWaveUnit : GL * UL;
   while ((touch + SEG - 1) / SEG + k_in + 1 > kUnitCap) SEG *= 2;
   if (!MERGE && !zkey) {  // uniform; split single-beam parts reduce only their own range
     int Uq;
@@ -1203,26 +1210,43 @@ void k_request_step(
           else
             final_lse(bl, float_of_ord(bmo[bl - bl_lo]), 1.f);
         }
-    } else if (!TOKEN_IDX && MODE != kZScore && GL == 16 && S <= 4 * 64 * UL) {
-      // rows of 64 or more legal tokens on average and at most 2,048 each
-      // (the table's slot stride): one wave per beam, at most four passes
-      // (longer rows go to the units below, which split a beam).  Lane
-      // i reads the beam's scores i, i + 64, ... in passes of 8 (contiguous
-      // per load), each pass reduced to (max, sum of exp) without branches
-      // and joined in order, then the wave's lanes in a fixed butterfly: the
-      // same value in every part that touches the beam.  The part's own
+    } else if (wave_units) {
+      // rows of 64 or more legal tokens on average: wave-sized units, SEG
+      // candidates from each beam's first (SEG is the request's), one wave
+      // each.  Lane i reads the unit's scores i, i + 64, ... in passes of 8
+      // (contiguous per load), each pass reduced to (max, sum of exp) without
+      // branches and joined in order, then the wave's lanes in a fixed
+      // butterfly; a beam of several units is joined below in unit order:
+      // the same value in every part that touches the beam.  The part's own
       // candidates also go to keys[].
-      for (int b = bl_lo + wave; b <= bl_hi; b += kSelWaves) {  // uniform over the wave
+      // (when every row fits one unit, the waves walk the beams directly)
+      const int u_lo = C > 0 ? upre[bl_lo] : 0, u_hi = C > 0 ? upre[bl_hi + 1] : 0;
+      const bool one_unit = (int)S <= SEG;
+      const int w_hi = one_unit ? (C > 0 ? bl_hi + 1 : 0) : u_hi;
+      for (int u = (one_unit ? bl_lo : u_lo) + wave; u < w_hi; u += kSelWaves) {  // uniform over the wave
+        int b = u;
+        if (!one_unit) {
+          int lo = bl_lo, hi = bl_hi + 1;  // the unit's beam: last b with upre[b] <= u
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (upre[mid] <= u)
+              lo = mid;
+            else
+              hi = mid;
+          }
+          b = lo;
+        }
         const int n_b = cpre[b + 1] - cpre[b];
-        if (n_b == 0) continue;
+        if (n_b == 0) continue;  // a dead beam (direct walk only)
+        const int j0 = one_unit ? 0 : (u - upre[b]) * SEG, j1 = min(n_b, j0 + SEG);
         const float* zb = z + (int64_t)(b0 + b) * ldz;
         float m = -INFINITY, sm = 0.f;
-        for (int jb = 0; jb < n_b; jb += 64 * UL) {
+        for (int jb = j0; jb < j1; jb += 64 * UL) {
           float zv[UL];
 #pragma unroll
           for (int i = 0; i < UL; ++i) {
             const int j = jb + i * 64 + lane;
-            zv[i] = j < n_b ? zb[j] : -INFINITY;
+            zv[i] = j < j1 ? zb[j] : -INFINITY;
           }
           float pm = zv[0];
 #pragma unroll
@@ -1237,13 +1261,36 @@ void k_request_step(
           for (int i = 0; i < UL; ++i) {
             const int j = jb + i * 64 + lane;
             const int f = cpre[b] + j;
-            if (store && j < n_b && f >= f0 && f < f1) {
+            if (store && j < j1 && f >= f0 && f < f1) {
               // sparse rows: slot = legal rank; dense rows (rank-indexed
               // scores): the code goes in after this pass
               const uint32_t code = dense ? 0u : code_of(b, j);
               keys[f - f0] = ((uint64_t)__float_as_uint(zv[i]) << 32) | code;
             }
           }
+        }
+        xor_down<32>([&](auto o) {
+          constexpr int X = decltype(o)::value;
+          lse_combine(m, sm, xor_lane<X>(m), xor_lane<X>(sm));
+        });
+        if (lane == 0) {
+          if (one_unit || upre[b + 1] - upre[b] == 1) {
+            final_lse(b, m, sm);
+          } else {
+            upart[u - u_lo] = make_float2(m, sm);
+            multi_sh = 1;
+          }
+        }
+      }
+      __syncthreads();
+      // beams of several units: one wave joins the unit partials in order
+      for (int b = bl_lo + wave; multi_sh && b <= bl_hi; b += kSelWaves) {
+        const int nu = upre[b + 1] - upre[b];
+        if (nu < 2) continue;  // uniform over the wave
+        float m = -INFINITY, sm = 0.f;
+        for (int i = lane; i < nu; i += 64) {
+          const float2 pq = upart[upre[b] - u_lo + i];
+          lse_combine(m, sm, pq.x, pq.y);
         }
         xor_down<32>([&](auto o) {
           constexpr int X = decltype(o)::value;
