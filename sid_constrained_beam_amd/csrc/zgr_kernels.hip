@@ -1121,8 +1121,9 @@ void k_request_step(
     atomicMax(&omax_sh, ord_of(bcum[b] + (m - l)));
   };
   if constexpr (!MERGE) {
-    if (zkey && !(TOKEN_IDX && dense)) {
-      // this part's own range only, coalesced, with its keys' scores
+    if ((zkey || (k_in == 1 && P == 1)) && !(TOKEN_IDX && dense)) {
+      // this part's own range only, coalesced, with its keys' scores (a
+      // single-beam request in one part: its whole row, by every thread)
       float m = -INFINITY, s = 0.f;
       const float* zb = z + (int64_t)b0 * ldz;
       for (int i0 = threadIdx.x; i0 < C; i0 += NT * U) {
@@ -1173,8 +1174,12 @@ void k_request_step(
       if (threadIdx.x == 0) {
         float mm = pm[0], ss = ps[0];
         for (int w = 1; w < kSelWaves; ++w) lse_combine(mm, ss, pm[w], ps[w]);
-        zms_sh = make_float2(mm, ss);
-        omax_sh = ord_of(mm);
+        if (zkey) {
+          zms_sh = make_float2(mm, ss);
+          omax_sh = ord_of(mm);
+        } else if (C > 0) {
+          final_lse(0, mm, ss);
+        }
       }
     } else if (TOKEN_IDX && dense) {
       // token-indexed rows of a dense table (the score-first comparison; its
