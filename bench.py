@@ -547,8 +547,10 @@ def index_bytes_report(names):
     per-step tables as built, and the same tables in other encodings, from
     the built index's per-step rows (R_t) and entries (nnz_t):
       as_built          formats as chosen (dense: bitmap + rank directory;
-                        sparse: sorted tokens, the position is the next row)
-      bitmap_only       dense rows without the rank directory
+                        sparse: sorted tokens, the position is the next row,
+                        plus the slice directory where the build adds one)
+      bitmap_only       dense rows without the rank directory, sparse rows
+                        without the slice directory
       dense_next_matrix dense rows as an int32 next-row matrix [R_t][V]
       all_sparse / all_dense_bitmap   one format for every step
       explicit_successor  every step as sorted tokens plus an explicit int32
