@@ -483,10 +483,12 @@ def modes_bench(args):
 
 
 def projections_bench(args):
-    """Per-step latency of the three ways to score a step on the same recorded
+    """Per-step latency of the ways to score a step on the same recorded
     inputs: the full projection (MFMA over the whole codebook), the padded-slot
-    selective projection (weight rows read in place), and the naive compaction
-    baseline (compact candidate list sized on the host + temporary matrix).
+    selective projection (weight rows read in place), the naive compaction
+    baseline (compact candidate list sized on the host + temporary matrix) and
+    the LDS-staged comparison (dense steps: weight-row tiles staged in LDS and
+    shared by a block's beams; sparse steps run the selective projection).
     Each step is timed as issued (eager, HIP events on the stream), request
     kernel included, since the naive path cannot be captured (it reads its
     list size back)."""
@@ -527,11 +529,13 @@ def projections_bench(args):
                                                                    for i, x in enumerate(per_step)))
     cand = [int(st["n"].sum()) for st in w.steps]
     ratios = {}
-    for a_, b_ in (("naive", "full"), ("naive", "selective"), ("full", "selective")):
+    for a_, b_ in (("naive", "full"), ("naive", "selective"), ("full", "selective"),
+                   ("staged", "selective")):
         if a_ in res and b_ in res:
             ratios[f"{a_}_over_{b_}"] = [round(x / y, 3) for x, y in zip(res[a_], res[b_])]
     print(json.dumps({
-        "metric": "per-step latency by projection (us): full, padded-slot selective, naive compaction",
+        "metric": "per-step latency by projection (us): full, padded-slot selective, naive "
+                  "compaction, LDS-staged",
         "value": res["selective"], "unit": "us", "higher_is_better": False, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: L={cfg.L}, V={cfg.V}, N={cfg.N}, d={cfg.d}, "
@@ -669,7 +673,7 @@ def main():
                     help="time the index rebuild pipeline of this workload's catalog instead")
     ap.add_argument("--rebuild-reps", type=int, default=3)
     ap.add_argument("--projections", action="store_true",
-                    help="time full / selective / naive-compaction scoring per step instead")
+                    help="time full / selective / naive-compaction / staged scoring per step instead")
     ap.add_argument("--batch", type=int, default=0, help="override the workload's batch")
     ap.add_argument("--proj-kinds", default="full,selective,naive",
                     help="with --projections: comma list of the projections to time")

@@ -81,6 +81,12 @@ extern "C" {
                                  through a compact candidate list (sized on the host from a
                                  device count, so the step synchronises its stream) and a
                                  temporary [candidates x d] matrix of copied weight rows */
+#define ZGR_PROJ_STAGED 4     /* comparison, never picked by the planner: on dense steps the
+                                 weight rows of a codebook tile are staged in LDS once and
+                                 scored from there for every beam of a block (beams' hidden
+                                 vectors held in registers); f32 with d >= 256 and bf16 with
+                                 d >= 512 only, other dense steps and every sparse step run
+                                 the selective projection */
 
 typedef struct zgr_index zgr_index;
 typedef struct zgr_plan zgr_plan;
@@ -272,9 +278,9 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
 int32_t zgr_plan_choice(const zgr_plan* plan, int32_t t, int32_t* proj, float* us_full,
                         float* us_sel);
 
-/* Re-freeze step t's projection (ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE or the
- * ZGR_PROJ_NAIVE baseline), e.g. to resume a plan exported by zgr_plan_choice
- * without a new warm-up. */
+/* Re-freeze step t's projection (ZGR_PROJ_FULL, ZGR_PROJ_SELECTIVE or one of
+ * the comparisons ZGR_PROJ_NAIVE and ZGR_PROJ_STAGED), e.g. to resume a plan
+ * exported by zgr_plan_choice without a new warm-up. */
 int32_t zgr_plan_set_choice(zgr_plan* plan, int32_t t, int32_t proj);
 
 /*

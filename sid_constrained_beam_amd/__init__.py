@@ -37,8 +37,9 @@ DTYPE_CODES = {"f32": ZGR_F32, "bf16": ZGR_BF16, "f16": ZGR_F16}
 FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR_FMT_SPARSE,
              "N": ZGR_FMT_DENSE_NEXT}
 ZGR_PROJ_NAIVE = 3
+ZGR_PROJ_STAGED = 4
 PROJ_CODES = {None: ZGR_PROJ_AUTO, "auto": ZGR_PROJ_AUTO, "full": ZGR_PROJ_FULL,
-              "selective": ZGR_PROJ_SELECTIVE, "naive": ZGR_PROJ_NAIVE}
+              "selective": ZGR_PROJ_SELECTIVE, "naive": ZGR_PROJ_NAIVE, "staged": ZGR_PROJ_STAGED}
 
 _P = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64

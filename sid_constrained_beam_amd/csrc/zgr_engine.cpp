@@ -352,7 +352,10 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
       e = prof_launch(p, ZGR_KERNEL_UNITS, t, s, [&] { return launch_units(a, s); });
       if (e != hipSuccess) return hip_fail(e, "unit count launch");
     }
-    e = prof_launch(p, ZGR_KERNEL_SELECTIVE, t, s, [&] { return launch_selective_score(a, s); });
+    const bool staged = proj == ZGR_PROJ_STAGED && dense;
+    e = prof_launch(p, ZGR_KERNEL_SELECTIVE, t, s, [&] {
+      return staged ? launch_staged_score(a, s) : launch_selective_score(a, s);
+    });
     if (e != hipSuccess) return hip_fail(e, "selective score launch");
     zmode = 1;
   }
@@ -499,8 +502,8 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
   if (n_warmup < 0) return fail(ZGR_E_ARG, "zgr_plan_warmup: n_warmup must be >= 0");
   for (int l = 0; l < idx->L; ++l) {
     if (!W_dev[l]) return fail(ZGR_E_ARG, "zgr_plan_warmup: null W_t");
-    if (force && (force[l] < ZGR_PROJ_AUTO || force[l] > ZGR_PROJ_NAIVE))
-      return fail(ZGR_E_ARG, "zgr_plan_warmup: force[t] must be AUTO, FULL, SELECTIVE or NAIVE");
+    if (force && (force[l] < ZGR_PROJ_AUTO || force[l] > ZGR_PROJ_STAGED))
+      return fail(ZGR_E_ARG, "zgr_plan_warmup: force[t] must be AUTO, FULL, SELECTIVE, NAIVE or STAGED");
     // the slot code beam_rank * S_t + slot must fit 32 bits
     if ((int64_t)K * std::max<int32_t>(1, idx->host[l].stride) >= (int64_t)UINT32_MAX)
       return fail(ZGR_E_SHAPE, "zgr_plan_warmup: K * slot stride too large");
@@ -662,8 +665,9 @@ int32_t zgr_plan_choice(const zgr_plan* p, int32_t t, int32_t* proj, float* us_f
 int32_t zgr_plan_set_choice(zgr_plan* p, int32_t t, int32_t proj) {
   if (!p) return fail(ZGR_E_ARG, "zgr_plan_set_choice: null plan");
   if (t < 1 || t > p->L) return fail(ZGR_E_ARG, "zgr_plan_set_choice: t out of range");
-  if (proj != ZGR_PROJ_FULL && proj != ZGR_PROJ_SELECTIVE && proj != ZGR_PROJ_NAIVE)
-    return fail(ZGR_E_ARG, "zgr_plan_set_choice: proj must be FULL, SELECTIVE or NAIVE");
+  if (proj != ZGR_PROJ_FULL && proj != ZGR_PROJ_SELECTIVE && proj != ZGR_PROJ_NAIVE &&
+      proj != ZGR_PROJ_STAGED)
+    return fail(ZGR_E_ARG, "zgr_plan_set_choice: proj must be FULL, SELECTIVE, NAIVE or STAGED");
   p->choice[t - 1] = proj;
   return ZGR_OK;
 }

@@ -116,6 +116,9 @@ struct StepArgs {
 
 hipError_t launch_units(const StepArgs& a, hipStream_t s);
 hipError_t launch_selective_score(const StepArgs& a, hipStream_t s);
+// Dense steps: the LDS-staged comparison kernel where its shape applies, else
+// the selective projection.
+hipError_t launch_staged_score(const StepArgs& a, hipStream_t s);
 hipError_t launch_full_projection(const StepArgs& a, hipStream_t s);
 // Which full-projection kernel, tile and epilogue a step shape gets (host
 // logic only; the launcher and zgr_full_projection_variant share it).

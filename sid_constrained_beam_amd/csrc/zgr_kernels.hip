@@ -30,6 +30,8 @@
 //                      row's bitmap, tiles split over the XCDs so each XCD's L2
 //                      holds its tiles' weight rows; z stored at the token's
 //                      legal rank.
+//   k_score_staged     comparison on dense rows: weight-row tiles staged in LDS
+//                      once per group of beams held in registers.
 //   k_gemm_nt          full projection Z = H . W_t^T on MFMA (fp32, bf16, f16
 //                      inputs; fp32 accumulate), Z row = beam, column = token;
 //   k_gemm_small       the same product for few beams (first step): 16x16 MFMA.
@@ -707,6 +709,215 @@ __global__ __launch_bounds__(kThreads) void k_score_selective(
       }
     }
     if (!by_xcd) break;  // the flat range covered every tile
+  }
+}
+
+// LDS-staged projection of a dense step (a comparison, chosen only when a
+// plan is told to): the weight rows are staged in LDS and shared by the
+// beams of a block.  A block (kStageThreads threads, one per CU) takes work
+// items (a group of BG beams, a codebook slice): the blocks of XCD x (blocks
+// are dealt to the 8 XCDs in turn) take slice x, an eighth of the row's
+// bitmap words, so an XCD reads only its slice's weight rows and its blocks
+// stream them in the same order.  Each wave keeps BW beams' hidden vectors in
+// registers (lane l holds 16-byte chunks l, 64 + l, ... of each) and their
+// bitmap words of a 64-word part of the slice in LDS.  The slice's rows are
+// read TT at a time, a contiguous run of W_t, in coalesced 16-byte loads by
+// the whole block (three tiles in flight in registers, three LDS buffers, one
+// barrier per tile), and every legal (beam, token) pair of the tile is scored
+// from LDS: a round takes the next legal token of each of the wave's beams,
+// and one reduction sums the round's BW dot products.  A weight row then
+// leaves L2 once per work item instead of once per legal pair: the traffic
+// drops by the expected number of the block's beams that have the token
+// legal (BG times the row density), at the price of a block barrier per tile
+// and registers that allow two waves per SIMD.
+constexpr int kStageThreads = 512;
+constexpr int kStageTileBytes = 32 * 1024;  // one LDS buffer (three per block)
+constexpr int kStageOut = 256;              // scores a wave holds before it stores them
+
+template <int DT, int D>
+struct StagedShape {
+  static constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
+  static constexpr int RB = D * ES;      // bytes per weight row
+  static constexpr int NV = RB / 1024;   // 16-byte chunks of a row per lane
+  static constexpr int BW0 = 32 / (NV > 0 ? NV : 1);
+  static constexpr int BW = pow2_floor(BW0 > 8 ? 8 : (BW0 < 1 ? 1 : BW0));  // beams per wave
+  static constexpr int TT0 = kStageTileBytes / RB;
+  static constexpr int TT = TT0 > 32 ? 32 : TT0;                 // tokens per tile
+  static constexpr int TB = TT * RB;                             // bytes per tile
+  static constexpr int LPT = TB / (16 * kStageThreads);          // 16-byte loads per thread
+  static constexpr int NWV = kStageThreads / 64;
+  static constexpr int BG = NWV * BW;  // beams per work item
+  // f16 inputs would widen the hidden shares to f32 (twice the registers)
+  static constexpr bool OK =
+      DT != ZGR_F16 && RB % 1024 == 0 && LPT >= 1 && TB % (16 * kStageThreads) == 0;
+};
+
+template <int DT, int D, bool NX>
+__global__ __launch_bounds__(kStageThreads) void k_score_staged(int32_t M, DevTable tab,
+                                                                const int32_t* __restrict__ row_in,
+                                                                const void* __restrict__ hidden,
+                                                                const void* __restrict__ W,
+                                                                float* __restrict__ z, int64_t ldz) {
+  using SS = StagedShape<DT, D>;
+  static_assert(SS::OK, "staged projection shape");
+  constexpr int NV = SS::NV, BW = SS::BW, TT = SS::TT, LPT = SS::LPT, BG = SS::BG;
+  constexpr int RC = SS::RB / 16;  // 16-byte chunks per row
+  constexpr int GL = 64 / BW;      // lanes per beam after the reduction
+  __shared__ uint4 stage[3][SS::TB / 16];
+  // Each wave's scores wait in LDS (value, slot * BW + beam) and go to z in
+  // batches, so no global store is in flight while the tile loads are: the
+  // loads' wait then covers only the older tile.
+  __shared__ float ov[SS::NWV][kStageOut];
+  __shared__ int od[SS::NWV][kStageOut];
+  __shared__ uint32_t wsh[SS::NWV][BW][64];
+  __shared__ int rsh[SS::NWV][BW][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nx = (gridDim.x & 7) == 0 ? 8 : 1;
+  const int x = (int)blockIdx.x % nx;
+  const int sw = (tab.words + nx - 1) / nx;  // words per slice
+  const int ws0 = x * sw, ws1 = min(tab.words, ws0 + sw);
+  const int ngroups = (M + BG - 1) / BG;
+  for (int g = (int)blockIdx.x / nx; g < ngroups; g += (int)gridDim.x / nx) {
+    const int b0 = g * BG + wv * BW;  // the wave's first beam
+    // rows in one load (lane i: beam b0 + i), hidden vectors beside them
+    const int rl = (lane < BW && b0 + lane < M) ? row_in[b0 + lane] : -1;
+    uint4 h[BW][NV];
+#pragma unroll
+    for (int i = 0; i < BW; ++i) {
+      const char* hb = (const char*)hidden + (int64_t)min(b0 + i, M - 1) * SS::RB;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) h[i][c] = *(const uint4*)(hb + (int64_t)(c * 64 + lane) * 16);
+    }
+    int rq[BW];
+#pragma unroll
+    for (int i = 0; i < BW; ++i) {
+      const int r = __builtin_amdgcn_readlane(rl, i);
+      rq[i] = (r >= 0 && r < tab.rows) ? r : -1;  // the request kernel reports bad rows
+    }
+    float* zw = z + (int64_t)b0 * ldz;
+    int cnt = 0;  // scores waiting in the wave's LDS buffer
+    auto flush = [&]() {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int j = lane; j < cnt; j += 64) {
+        const int d = od[wv][j];
+        zw[(int64_t)(d % BW) * ldz + d / BW] = ov[wv][j];
+      }
+      // the stores complete here, so no store is outstanding behind a tile's
+      // loads when the pipeline waits for them (vmcnt 0; expcnt, lgkmcnt not waited)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      cnt = 0;
+    };
+    for (int sw0 = ws0; sw0 < ws1; sw0 += 64) {
+      const int nwd = min(64, ws1 - sw0);
+      // the beams' bitmap words of this part (lane w: word sw0 + w) and
+      // their ranks, kept in the wave's LDS (registers hold the hidden shares)
+#pragma unroll
+      for (int i = 0; i < BW; ++i) {
+        const DWord d = (rq[i] >= 0 && lane < nwd) ? dense_word<NX>(tab, rq[i], sw0 + lane) : DWord{0u, 0};
+        wsh[wv][i][lane] = d.bits;
+        rsh[wv][i][lane] = d.rank;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int v0 = sw0 * 32;
+      const int ntile = (nwd * 32 + TT - 1) / TT;
+      // every thread issues all its loads (a chunk past row V - 1 reads the
+      // last chunk of W_t instead; those rows are never scored), so the
+      // compiler's wait for a tile counts only the loads issued after it
+      struct Tile {
+        uint4 v[LPT];
+      };
+      auto load_tile = [&](int k) {
+        const int t0 = min(v0 + k * TT, tab.V - 1);
+        const int lastc = min(TT, tab.V - t0) * RC - 1;  // last chunk of rows below V
+        const uint4* src = (const uint4*)W + (int64_t)t0 * RC;
+        Tile r;
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) r.v[j] = src[min(j * kStageThreads + (int)threadIdx.x, lastc)];
+        return r;
+      };
+      auto store_tile = [&](int sb, const Tile& r) {
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) stage[sb][j * kStageThreads + threadIdx.x] = r.v[j];
+      };
+      auto compute = [&](int k, int sb) {
+        const int tw = (k * TT) >> 5, off = (k * TT) & 31;
+        uint32_t tb[BW];
+        int tr[BW];
+#pragma unroll
+        for (int i = 0; i < BW; ++i) {
+          const uint32_t wb = (uint32_t)__builtin_amdgcn_readfirstlane((int)wsh[wv][i][tw]);
+          const int wr = __builtin_amdgcn_readfirstlane(rsh[wv][i][tw]);
+          tb[i] = TT == 32 ? wb : (wb >> off) & ((1u << (TT & 31)) - 1u);
+          tr[i] = wr + __popc(wb & ((1u << off) - 1u));
+        }
+        const uint4* st = stage[sb];
+        for (;;) {
+          uint32_t any = 0;
+#pragma unroll
+          for (int i = 0; i < BW; ++i) any |= tb[i];
+          if (!any) break;
+          if (cnt + BW > kStageOut) flush();
+          float acc[BW];
+          int dst = 0;
+          bool put = false;
+#pragma unroll
+          for (int i = 0; i < BW; ++i) {
+            acc[i] = 0.f;
+            if (tb[i]) {
+              const int t = __builtin_ctz(tb[i]);
+              tb[i] &= tb[i] - 1u;
+              const uint4* row = st + t * RC;
+#pragma unroll
+              for (int c = 0; c < NV; ++c) acc[i] = GatherDot<DT, D>::dot16(row[c * 64 + lane], h[i][c], acc[i]);
+              if (lane == i * GL) {
+                dst = tr[i] * BW + i;
+                put = true;
+              }
+              ++tr[i];
+            }
+          }
+          // lane i * GL ends with beam i's sum
+          const float v = group_sum_multi<64, BW>(acc, lane);
+          const uint64_t pm = __ballot(put);
+          if (put) {
+            const int j = cnt + __popcll(pm & ((1ull << lane) - 1ull));
+            ov[wv][j] = v;
+            od[wv][j] = dst;
+          }
+          cnt += __popcll(pm);
+        }
+      };
+      // three tiles in flight in registers, three LDS buffers, one barrier
+      // per tile; loads past the last tile read clamped rows, so every
+      // iteration issues the same loads
+      Tile r0 = load_tile(0), r1 = load_tile(1), r2 = load_tile(2);
+      store_tile(0, r0);
+      __syncthreads();
+      for (int k = 0; k < ntile; k += 3) {
+        // buffer 0 holds tile k; r1, r2 tiles k + 1, k + 2 (in flight)
+        r0 = load_tile(k + 3);
+        compute(k, 0);
+        store_tile(1, r1);
+        __syncthreads();
+        if (k + 1 >= ntile) break;
+        r1 = load_tile(k + 4);
+        compute(k + 1, 1);
+        store_tile(2, r2);
+        __syncthreads();
+        if (k + 2 >= ntile) break;
+        r2 = load_tile(k + 5);
+        compute(k + 2, 2);
+        store_tile(0, r0);
+        __syncthreads();
+      }
+    }
+    flush();
   }
 }
 
@@ -2352,6 +2563,25 @@ constexpr int kSelMaxBlocksPerCu = 5;
 // decides below that).
 constexpr int kSparseMaxBlocksPerCu = 8;
 
+// The staged comparison on a dense step where its shape applies (true when
+// it launched).
+template <int DT, int D>
+bool launch_staged(const StepArgs& a, hipStream_t s) {
+  using SS = StagedShape<DT, D>;
+  if constexpr (!SS::OK) {
+    return false;
+  } else {
+    if (a.tab.fmt == ZGR_FMT_SPARSE) return false;
+    if (a.tab.next)
+      hipLaunchKernelGGL((k_score_staged<DT, D, true>), dim3(a.n_cu), dim3(kStageThreads), 0, s, a.M,
+                         a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
+    else
+      hipLaunchKernelGGL((k_score_staged<DT, D, false>), dim3(a.n_cu), dim3(kStageThreads), 0, s, a.M,
+                         a.tab, a.row_in, a.hidden, a.W, a.z, a.ldz);
+    return true;
+  }
+}
+
 template <int DT, int D>
 hipError_t launch_sel_typed(const StepArgs& a, hipStream_t s) {
   const int32_t tt = dense_tile_tokens(D, DT);
@@ -2377,17 +2607,23 @@ hipError_t launch_sel_typed(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, int D, bool STAGED>
+hipError_t launch_sel_or_staged(const StepArgs& a, hipStream_t s) {
+  if (STAGED && launch_staged<DT, D>(a, s)) return hipGetLastError();
+  return launch_sel_typed<DT, D>(a, s);
+}
+
+template <int DT, bool STAGED = false>
 hipError_t launch_sel_d(const StepArgs& a, hipStream_t s) {
   switch (a.d) {
-    case 64: return launch_sel_typed<DT, 64>(a, s);
-    case 128: return launch_sel_typed<DT, 128>(a, s);
-    case 256: return launch_sel_typed<DT, 256>(a, s);
-    case 512: return launch_sel_typed<DT, 512>(a, s);
-    case 768: return launch_sel_typed<DT, 768>(a, s);
-    case 1024: return launch_sel_typed<DT, 1024>(a, s);
-    case 2048: return launch_sel_typed<DT, 2048>(a, s);
-    case 4096: return launch_sel_typed<DT, 4096>(a, s);
+    case 64: return launch_sel_or_staged<DT, 64, STAGED>(a, s);
+    case 128: return launch_sel_or_staged<DT, 128, STAGED>(a, s);
+    case 256: return launch_sel_or_staged<DT, 256, STAGED>(a, s);
+    case 512: return launch_sel_or_staged<DT, 512, STAGED>(a, s);
+    case 768: return launch_sel_or_staged<DT, 768, STAGED>(a, s);
+    case 1024: return launch_sel_or_staged<DT, 1024, STAGED>(a, s);
+    case 2048: return launch_sel_or_staged<DT, 2048, STAGED>(a, s);
+    case 4096: return launch_sel_or_staged<DT, 4096, STAGED>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -2475,6 +2711,15 @@ hipError_t launch_selective_score(const StepArgs& a, hipStream_t s) {
     case ZGR_F32: return launch_sel_d<ZGR_F32>(a, s);
     case ZGR_BF16: return launch_sel_d<ZGR_BF16>(a, s);
     case ZGR_F16: return launch_sel_d<ZGR_F16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_staged_score(const StepArgs& a, hipStream_t s) {
+  switch (a.dtype) {
+    case ZGR_F32: return launch_sel_d<ZGR_F32, true>(a, s);
+    case ZGR_BF16: return launch_sel_d<ZGR_BF16, true>(a, s);
+    case ZGR_F16: return launch_sel_d<ZGR_F16, true>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

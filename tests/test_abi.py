@@ -152,5 +152,6 @@ def test_step_noalloc_argument_errors():
     assert call(args(k_in=5)) == zgr.ZGR_E_ARG
     assert call(args(proj=zgr.ZGR_PROJ_AUTO)) == zgr.ZGR_E_ARG
     assert call(args(proj=zgr.ZGR_PROJ_NAIVE)) == zgr.ZGR_E_ARG
+    assert call(args(proj=zgr.ZGR_PROJ_STAGED)) == zgr.ZGR_E_ARG
     assert call(args()) == zgr.ZGR_E_STATE  # the index is not on a device
     idx.free()

@@ -49,7 +49,7 @@ def oracle_inputs(s, requests, t):
     return prefixes, cum
 
 
-@pytest.mark.parametrize("proj", ["selective", "full", "naive"])
+@pytest.mark.parametrize("proj", ["selective", "full", "naive", "staged"])
 @pytest.mark.parametrize("name", list(CASES))
 def test_step_parity_teacher_forced(name, proj):
     s = setup_of(name)
@@ -286,7 +286,7 @@ def test_naive_baseline_matches_padded_slots():
     assert np.allclose(outs["selective"][1][ok], outs["naive"][1][ok], atol=1e-4, rtol=0)
 
 
-@pytest.mark.parametrize("proj", ["selective", "full"])
+@pytest.mark.parametrize("proj", ["selective", "full", "staged"])
 @pytest.mark.parametrize("name", list(NEXT_CASES))
 def test_next_row_matrix_encoding(name, proj):
     """Dense steps stored as an int32 next-row matrix instead of the bitmap:
