@@ -2021,7 +2021,8 @@ constexpr int kLdsRow = kTileKBytes + 16;  // padded row pitch in bytes
 
 // C[m][n] = sum_k A[m][k] * B[n][k]: A = hidden [M][D], B = W_t [N][D], both
 // k-contiguous.  BM x BN block tile, 4 waves in 2x2 each owning (BM/2)x(BN/2)
-// as MFMA 32x32 blocks, 128-byte k-slices staged through LDS with a register
+// (8 waves in 2x4 for 16-bit 128x128 tiles, see gemm_threads) as MFMA 32x32
+// blocks, 128-byte k-slices staged through LDS with a register
 // prefetch of the next slice.
 // compact != 0 (dense table): only legal columns are written, at their legal
 // rank within the beam's row (rank directory + popcount below the column);
@@ -2068,8 +2069,13 @@ struct GemmOrder {
   }
 };
 
+// Threads of a GEMM block: 16-bit 128x128 tiles run 8 waves (2 x 4, 64x32
+// each), which hide more of the k loop's load latency (the 1e7-item
+// V = 4,096 step 2: 34.7 -> 31.0 us); fp32 and 64x64 tiles keep 4 (2 x 2).
+constexpr int gemm_threads(int dt, int bm) { return (bm == 128 && dt != ZGR_F32) ? 512 : kThreads; }
+
 template <int DT, int BM, int BN, bool NX, bool SP>
-__global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A,
+__global__ __launch_bounds__(gemm_threads(DT, BM)) void k_gemm_nt(const void* __restrict__ A,
                                                       const void* __restrict__ Bm,
                                                       float* __restrict__ C, int32_t M, int32_t N,
                                                       int32_t D, int64_t ldc, int32_t compact,
@@ -2077,8 +2083,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
                                                       const int32_t* __restrict__ row_in) {
   constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
   constexpr int TK = kTileKBytes / ES;  // k elements per slice
-  constexpr int WM = BM / 2, WN = BN / 2, IB = WM / 32, JB = WN / 32;
-  constexpr int NA = BM * 8 / kThreads, NB = BN * 8 / kThreads;  // 16-byte chunks per thread
+  constexpr int NT = gemm_threads(DT, BM);
+  constexpr int NWX = NT / 128;  // waves along N (two along M)
+  constexpr int WM = BM / 2, WN = BN / NWX, IB = WM / 32, JB = WN / 32;
+  constexpr int NA = BM * 8 / NT, NB = BN * 8 / NT;  // 16-byte chunks per thread
   constexpr int TW = BN / 32;                                     // bitmap words per tile row
   constexpr int STAGE = (BM + BN) * kLdsRow;
   constexpr int CTILE = SP ? BM * (BN + 1) * 4 : 0;  // staged output tile (sparse epilogue)
@@ -2094,14 +2102,14 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   if (tm < 0) return;  // padding block (before any barrier)
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWX, wn = wave % NWX;
   const char* Ab = (const char*)A;
   const char* Bb = (const char*)Bm;
   const int64_t rowbytes = (int64_t)D * ES;
   // compact epilogue: the tile rows' bitmap words and ranks are loaded into
   // registers now (thread i < BM owns tile row i) and reach LDS only after
   // the k loop, so their two dependent loads overlap the product
-  static_assert(BM <= kThreads, "one tile row per thread");
+  static_assert(BM <= NT, "one tile row per thread");
   DWord pdw[TW];
 #pragma unroll
   for (int k = 0; k < TW; ++k) pdw[k] = DWord{0u, 0};
@@ -2144,13 +2152,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
   const char* pb[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int c = threadIdx.x + i * kThreads;
+    const int c = threadIdx.x + i * NT;
     const int gm = m0 + (c >> 3);
     pa[i] = gm < M ? Ab + (int64_t)gm * rowbytes + (c & 7) * 16 : nullptr;
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int c = threadIdx.x + i * kThreads;
+    const int c = threadIdx.x + i * NT;
     const int gn = n0 + (c >> 3);
     pb[i] = gn < N ? Bb + (int64_t)gn * rowbytes + (c & 7) * 16 : nullptr;
   }
@@ -2173,12 +2181,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nt(const void* __restrict__ A
     char* Bs = As + BM * kLdsRow;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const int c = threadIdx.x + i * kThreads;
+      const int c = threadIdx.x + i * NT;
       *(uint4*)(As + (c >> 3) * kLdsRow + (c & 7) * 16) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int c = threadIdx.x + i * kThreads;
+      const int c = threadIdx.x + i * NT;
       *(uint4*)(Bs + (c >> 3) * kLdsRow + (c & 7) * 16) = rb[i];
     }
   };
@@ -2662,7 +2670,7 @@ hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
   const int compact = g.epilogue;  // ZGR_EPI_PLAIN / DENSE / SLOT = 0 / 1 / 2
 #define ZGR_GEMM(BM_, BN_, SP_)                                                                    \
   hipLaunchKernelGGL((k_gemm_nt<DT, BM_, BN_, NX, SP_>), dim3(GemmOrder(a.M, V, BM_, BN_).blocks()), \
-                     dim3(kThreads), 0, s,                                                          \
+                     dim3(gemm_threads(DT, BM_)), 0, s,                                                          \
                      a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in)
   if (g.kernel == ZGR_GEMM_TILED && g.tile_m == 128) {
     if (compact == ZGR_EPI_SLOT)
