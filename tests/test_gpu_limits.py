@@ -35,6 +35,13 @@ LIMITS = {
     "hidden_4096_bf16": cfg_of("hidden_4096_bf16", 3, 512, 20_000, 4096, 16, 2, "bf16"),
     "hidden_768_f16": cfg_of("hidden_768_f16", 3, 1024, 50_000, 768, 24, 3, "f16"),
     "batch_300": cfg_of("batch_300", 3, 128, 5_000, 64, 8, 300, "f32"),
+    # 16-bit full projections on 128x128 tiles (8-wave blocks) with ragged edges: M = 32 * 125
+    # beams and V not a multiple of the tile (nor of 32) at steps 2 and 3
+    # (step 2 dense: legal-rank epilogue; step 3 sparse: slot epilogue)
+    "ragged_tiles_bf16": cfg_of("ragged_tiles_bf16", 3, 2000, 300_000, 512, 125, 32, "bf16",
+                                fmt=["D", "D", "S"]),
+    "ragged_tiles_f16": cfg_of("ragged_tiles_f16", 3, 2100, 200_000, 256, 125, 32, "f16",
+                               fmt=["D", "D", "S"]),
 }
 
 _setups = {}
@@ -156,3 +163,12 @@ def test_limit_configs_are_extreme():
     assert setup_of("beam_1024").cfg.K == 1024
     d8 = setup_of("depth_8")
     assert d8.cfg.L == 8
+    # the ragged cases reach the 16-bit 128x128 tiles at steps 2 and 3, with partial edge tiles
+    for name in ("ragged_tiles_bf16", "ragged_tiles_f16"):
+        s = setup_of(name)
+        M = s.cfg.B * s.cfg.K
+        assert M % 128 and s.cfg.V % 128 and s.cfg.V % 32
+        for t in (2, 3):
+            var = zgr.zgr_full_projection_variant(M, s.cfg.V, s.cfg.dtype, s.stats[t - 1]["fmt"],
+                                                  "filter_first")
+            assert var[1:3] == (128, 128), (name, t, var)
