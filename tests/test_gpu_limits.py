@@ -54,7 +54,7 @@ def setup_of(name):
     return _setups[name]
 
 
-@pytest.mark.parametrize("proj", ["selective", "full"])
+@pytest.mark.parametrize("proj", ["selective", "full", "staged"])
 @pytest.mark.parametrize("name", list(LIMITS))
 def test_limit_decode(name, proj):
     import torch
