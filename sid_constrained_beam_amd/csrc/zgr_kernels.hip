@@ -1595,20 +1595,34 @@ void k_request_step(
         }
       }
       __syncthreads();
-      // beams of several units: one wave joins the unit partials in order
-      for (int b = bl_lo + wave; multi_sh && b <= bl_hi; b += kSelWaves) {
-        const int nu = upre[b + 1] - upre[b];
-        if (nu < 2) continue;  // uniform over the wave
-        float m = -INFINITY, s = 0.f;
-        for (int i = lane; i < nu; i += 64) {
-          const float2 pq = upart[upre[b] - u_lo + i];
-          lse_combine(m, s, pq.x, pq.y);
+      // beams of a few units: one thread joins their partials in order;
+      // beams of many: one wave, in a fixed butterfly
+      constexpr int kJoinSerial = 16;
+      if (multi_sh) {
+        for (int b = bl_lo + (int)threadIdx.x; b <= bl_hi; b += NT) {
+          const int nu = upre[b + 1] - upre[b];
+          if (nu < 2 || nu > kJoinSerial) continue;
+          float m = -INFINITY, s = 0.f;
+          for (int i = 0; i < nu; ++i) {
+            const float2 pq = upart[upre[b] - u_lo + i];
+            lse_combine(m, s, pq.x, pq.y);
+          }
+          final_lse(b, m, s);
         }
-        xor_down<32>([&](auto o) {
-          constexpr int X = decltype(o)::value;
-          lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
-        });
-        if (lane == 0) final_lse(b, m, s);
+        for (int b = bl_lo + wave; b <= bl_hi; b += kSelWaves) {
+          const int nu = upre[b + 1] - upre[b];
+          if (nu <= kJoinSerial) continue;  // uniform over the wave
+          float m = -INFINITY, s = 0.f;
+          for (int i = lane; i < nu; i += 64) {
+            const float2 pq = upart[upre[b] - u_lo + i];
+            lse_combine(m, s, pq.x, pq.y);
+          }
+          xor_down<32>([&](auto o) {
+            constexpr int X = decltype(o)::value;
+            lse_combine(m, s, xor_lane<X>(m), xor_lane<X>(s));
+          });
+          if (lane == 0) final_lse(b, m, s);
+        }
       }
     }
   }
