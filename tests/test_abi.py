@@ -101,6 +101,9 @@ def test_plan_and_step_argument_errors():
     assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 1, 2000, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_SHAPE
     bad_force = (ctypes.c_int32 * 2)(0, 5)
     assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 1, 1, cb, None, 0, bad_force, None, ctypes.byref(out)) == zgr.ZGR_E_ARG
+    # every named projection (the staged comparison included) passes the force check
+    ok_force = (ctypes.c_int32 * 2)(zgr.ZGR_PROJ_NAIVE, zgr.ZGR_PROJ_STAGED)
+    assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 1, 1, cb, None, 0, ok_force, None, ctypes.byref(out)) == zgr.ZGR_E_STATE
     # the index was built on the host only: a plan needs it on the device
     assert L.zgr_plan_warmup(idx.handle, W, 0, 64, 1, 1, cb, None, 0, None, None, ctypes.byref(out)) == zgr.ZGR_E_STATE
     assert "not on the device" in zgr.last_error()
