@@ -405,6 +405,25 @@ int32_t zgr_full_projection_variant(int32_t M, int32_t V, int32_t dtype, int32_t
                                     int32_t n_cu, int32_t* kernel, int32_t* tile_m, int32_t* tile_n,
                                     int32_t* epilogue);
 
+/* How the request kernel (normalise, select, advance) ran at step t in the
+ * plan's last zgr_step or zgr_decode.  *kind: ZGR_REQ_TOKEN (scores in
+ * token-indexed rows), ZGR_REQ_SLOT (scores at their slot or legal rank),
+ * ZGR_REQ_SCORED (light sparse step: the request kernel gathers and scores
+ * its candidates itself) or ZGR_REQ_PRUNED (dense step after the full
+ * projection, whose epilogue left every beam's legal (max, sum of exp) per
+ * 32-token word: the request normalises from those partials and reads only
+ * the scores of the K words whose best candidates rank highest, which hold
+ * its whole top K -- ZeroGR page, "why fewer scores is not faster": filter,
+ * score and select share one pass over the slots).  *parts: blocks per
+ * request (above 1 a merging dispatch follows).  Host state only; either
+ * output may be NULL.  Errors: ZGR_E_ARG (null plan, t outside [1, L]),
+ * ZGR_E_STATE (step t has not run on this plan). */
+#define ZGR_REQ_TOKEN 0
+#define ZGR_REQ_SLOT 1
+#define ZGR_REQ_SCORED 2
+#define ZGR_REQ_PRUNED 5
+int32_t zgr_plan_request_path(const zgr_plan* plan, int32_t t, int32_t* kind, int32_t* parts);
+
 /* ---- per-kernel timing ------------------------------------------------------------------ */
 
 /* Kernel classes of a step, for zgr_plan_profile_read. */

@@ -38,6 +38,7 @@ FMT_CODES = {None: ZGR_FMT_AUTO, "A": ZGR_FMT_AUTO, "D": ZGR_FMT_DENSE, "S": ZGR
              "N": ZGR_FMT_DENSE_NEXT}
 ZGR_PROJ_NAIVE = 3
 ZGR_PROJ_STAGED = 4
+ZGR_REQ_TOKEN, ZGR_REQ_SLOT, ZGR_REQ_SCORED, ZGR_REQ_PRUNED = 0, 1, 2, 5
 PROJ_CODES = {None: ZGR_PROJ_AUTO, "auto": ZGR_PROJ_AUTO, "full": ZGR_PROJ_FULL,
               "selective": ZGR_PROJ_SELECTIVE, "naive": ZGR_PROJ_NAIVE, "staged": ZGR_PROJ_STAGED}
 
@@ -123,6 +124,7 @@ def lib() -> ctypes.CDLL:
             "zgr_step": (_I32, [_P, _I32, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _P]),
             "zgr_decode": (_I32, [_P, HIDDEN_FN, _P, _I32, _P, _P, _P, _P]),
             "zgr_plan_status": (_I32, [_P, _P]),
+            "zgr_plan_request_path": (_I32, [_P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
             "zgr_plan_profile": (_I32, [_P, _I32]),
             "zgr_plan_profile_read": (_I32, [_P, _I32, _I32, ctypes.POINTER(_I64),
                                              ctypes.POINTER(ctypes.c_double)]),
@@ -418,6 +420,14 @@ def zgr_plan_choice(plan: Plan, t: int):
     proj, uf, us = _I32(), ctypes.c_float(), ctypes.c_float()
     _check(lib().zgr_plan_choice(plan.handle, t, ctypes.byref(proj), ctypes.byref(uf), ctypes.byref(us)))
     return proj.value, uf.value, us.value
+
+
+def zgr_plan_request_path(plan: Plan, t: int):
+    """(kind, parts) of the request kernel at step t in the plan's last step or decode;
+    kind is one of ZGR_REQ_TOKEN / SLOT / SCORED / PRUNED."""
+    kind, parts = _I32(), _I32()
+    _check(lib().zgr_plan_request_path(plan.handle, t, ctypes.byref(kind), ctypes.byref(parts)))
+    return kind.value, parts.value
 
 
 def zgr_plan_set_choice(plan: Plan, t: int, proj):

@@ -52,6 +52,7 @@ struct zgr_plan {
   void* naive_tmp = nullptr;
   int64_t naive_cap = 0;
   float us_full[zgr::kMaxL], us_sel[zgr::kMaxL];
+  int32_t req_kind[zgr::kMaxL] = {0}, req_parts[zgr::kMaxL] = {0};  // last run of each step
   int n_cu = 256;
   // HBM scratch
   std::vector<void*> allocations;
@@ -62,6 +63,7 @@ struct zgr_plan {
   int4* umeta = nullptr;
   int64_t chunk_cap = 0;
   float* lse = nullptr;
+  float2* zms = nullptr;  // dense full projections: legal (max, sum of exp) per 32-token word
   uint64_t* part_keys = nullptr;
   int32_t* part_cnt = nullptr;
   float2* part_ms = nullptr;
@@ -242,6 +244,7 @@ bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
 constexpr double kSmallRequest = 6144.0;
 constexpr double kPartCandidates = 2048.0;
 constexpr double kPartMaxCandidates = 0.9 * kKeyCapHost;
+constexpr double kPruneGain = 4.0;  // pruning needs this many candidates per kept-word bound
 constexpr double kBigPartMaxCandidates = 0.9 * kMergeCapHost;
 int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool* big) {
   *big = false;
@@ -263,6 +266,35 @@ int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool* big) {
   }
   P = std::min({P, kMaxParts, merge_cap});
   return std::max(1, P);
+}
+
+// A dense step under the tiled full projection can prune its requests: the
+// epilogue leaves each (beam, 32-token word) its legal (max, sum of exp), and
+// the request kernel reads only the scores of the K words whose best
+// candidates rank highest (at most 32 K candidates per request).  It pays when
+// the request holds several times that many candidates (estimated from the
+// table's mean row); each thread of the request kernel joins at most
+// kPruneWordsHost of its beam's words.
+double prune_bound(const StepArgs& a) {
+  return 32.0 * (double)std::min<int64_t>(a.K, (int64_t)a.k_in * a.tab.words);
+}
+bool prune_step(const zgr_plan* p, const StepArgs& a) {
+  if (!p->zms || a.plain_z || a.k_in < 2) return false;
+  if (a.tab.fmt != ZGR_FMT_DENSE && a.tab.fmt != ZGR_FMT_DENSE_NEXT) return false;
+  if (gemm_variant(a.M, a.tab.V, true, false, a.n_cu).kernel != ZGR_GEMM_TILED) return false;
+  int kp2 = 1;
+  while (kp2 < a.k_in) kp2 <<= 1;
+  const int G = std::max(1, std::min(64, 1024 / kp2));
+  if ((a.tab.words + G - 1) / G > kPruneWordsHost) return false;
+  const HostTable& h = p->idx->host[a.t - 1];
+  const double mean_n = (double)h.nnz / (double)std::max<int64_t>(1, h.rows);
+  return a.k_in * std::min<double>(mean_n, a.tab.stride) >= kPruneGain * prune_bound(a);
+}
+
+// Blocks per pruned request: the fewest whose shares of the kept words'
+// candidates fit the merge-sized LDS key array (one block for K <= 448).
+int32_t prune_parts(const StepArgs& a) {
+  return std::max(1, (int)std::ceil(prune_bound(a) / kMergeCapHost));
 }
 
 // Enqueue one step with the given projection.
@@ -290,6 +322,8 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     zmode = unc ? 1 : 0;
     a.z_token = zmode == 0;
     a.parts = request_parts(p, a, &a.big_parts);
+    p->req_kind[t - 1] = zmode;
+    p->req_parts[t - 1] = a.parts;
     e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
     if (e != hipSuccess) return hip_fail(e, "request step launch");
     if (a.parts > 1) {
@@ -337,9 +371,11 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     // slot; the few-beam kernel on a sparse step writes token-indexed rows
     const bool slot = dense || full_projection_slot_layout(a);
     a.ldz = (slot && !dense) ? a.tab.stride : p->V;
+    const bool prune = prune_step(p, a);
+    a.zms = prune ? p->zms : nullptr;
     e = prof_launch(p, ZGR_KERNEL_GEMM, t, s, [&] { return launch_full_projection(a, s); });
     if (e != hipSuccess) return hip_fail(e, "full projection launch");
-    zmode = slot ? 1 : 0;
+    zmode = prune ? 5 : (slot ? 1 : 0);
   } else if (!dense && light_sparse_step(p, a)) {
     a.ldz = a.tab.stride;
     zmode = 2;
@@ -360,8 +396,10 @@ int32_t run_step(zgr_plan* p, StepArgs a, int32_t proj, hipStream_t s) {
     zmode = 1;
   }
   a.z_token = zmode == 0;
-  a.parts = request_parts(p, a, &a.big_parts);
+  a.parts = zmode == 5 ? prune_parts(a) : request_parts(p, a, &a.big_parts);
   if (zmode != 1) a.big_parts = false;  // big parts are slot-indexed only
+  p->req_kind[t - 1] = zmode;
+  p->req_parts[t - 1] = a.parts;
   e = prof_launch(p, ZGR_KERNEL_REQUEST, t, s, [&] { return launch_request_step(a, zmode, s); });
   if (e != hipSuccess) return hip_fail(e, "request step launch");
   if (a.parts > 1) {
@@ -560,6 +598,9 @@ int32_t zgr_plan_warmup(const zgr_index* idx, const void* const* W_dev, int32_t 
           p->chunk_cap, 1024 * slice_units_per_beam(idx->host[l].stride, idx->V, idx->dev[l].sdir != nullptr));
   if (p->chunk_cap > 0) A((void**)&p->umeta, (size_t)kSlices * nq_max * p->chunk_cap * 16);
   A((void**)&p->lse, (size_t)MK * 4);
+  bool any_dense = false;
+  for (int l = 0; l < idx->L; ++l) any_dense = any_dense || idx->host[l].fmt != ZGR_FMT_SPARSE;
+  if (any_dense) A((void**)&p->zms, (size_t)MK * ((idx->V + 31) / 32) * 8);
   A((void**)&p->part_keys, (size_t)B * kMaxParts * K * 8);
   A((void**)&p->part_cnt, (size_t)B * kMaxParts * 4);
   A((void**)&p->part_ms, (size_t)B * kMaxParts * 8);
@@ -775,6 +816,15 @@ int32_t zgr_full_projection_variant(int32_t M, int32_t V, int32_t dtype, int32_t
   if (tile_m) *tile_m = g.tile_m;
   if (tile_n) *tile_n = g.tile_n;
   if (epilogue) *epilogue = g.epilogue;
+  return ZGR_OK;
+}
+
+int32_t zgr_plan_request_path(const zgr_plan* p, int32_t t, int32_t* kind, int32_t* parts) {
+  if (!p) return fail(ZGR_E_ARG, "zgr_plan_request_path: null plan");
+  if (t < 1 || t > p->L) return fail(ZGR_E_ARG, "zgr_plan_request_path: t out of range");
+  if (p->req_parts[t - 1] < 1) return fail(ZGR_E_STATE, "zgr_plan_request_path: step not run yet");
+  if (kind) *kind = p->req_kind[t - 1];
+  if (parts) *parts = p->req_parts[t - 1];
   return ZGR_OK;
 }
 

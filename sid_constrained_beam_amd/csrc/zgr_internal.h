@@ -103,6 +103,8 @@ struct StepArgs {
   int64_t chunk_cap;    // unit places one chunk of one slice can hold
   float* lse;           // [M] per-beam log-sum-exp over legal tokens
   float* lse_ext;       // [M] or null: normaliser given to the request kernel (score-first)
+  float2* zms;          // [M][words] or null: the full projection's legal (max, sum of exp)
+                        // per 32-token word of a dense row, read by the pruned request kernel
   bool plain_z;         // full projection writes token-indexed rows even on dense steps
   bool z_token;         // the request kernel reads token-indexed score rows (zmode 0)
   int32_t parts;        // blocks per request in the request kernel (1 = no merge)
@@ -131,11 +133,15 @@ GemmVariant gemm_variant(int32_t M, int32_t V, bool dense, bool plain, int32_t n
 // true when the full projection of this step writes sparse rows by slot
 // (legal columns only, ldz = stride) rather than token-indexed rows (ldz = V)
 bool full_projection_slot_layout(const StepArgs& a);
-// zmode: 0 = z token-indexed, 1 = z slot-indexed, 2 = score inside the request kernel.
+// zmode: 0 = z token-indexed, 1 = z slot-indexed, 2 = score inside the request kernel,
+// 5 = dense rank-indexed rows pruned by the full projection's word partials (a.zms).
 // With a.parts > 1 each request's candidates are split over a.parts blocks, then merged.
 constexpr int kMaxParts = 64;
 constexpr int kKeyCapHost = 5120;     // candidates of a request part whose keys fit the request kernel's LDS
 constexpr int kMergeCapHost = 14336;  // part keys (parts x K) the merge holds in LDS
+// word partials one thread of a pruned request joins: its beam's words split
+// over min(64, 1024 / k_in rounded up to a power of two) threads
+constexpr int kPruneWordsHost = 8;
 hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s);
 // after launch_request_step with a.parts > 1: the per-request merge of the parts
 hipError_t launch_request_merge(const StepArgs& a, hipStream_t s);

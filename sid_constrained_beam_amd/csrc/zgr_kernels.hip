@@ -1047,6 +1047,8 @@ constexpr int kUnitCap = 1400;
 constexpr int kMaxK = 1024;
 // candidates of a wave-sized log-sum-exp unit (four passes of eight per lane)
 constexpr int kWaveUnit = 4 * 8 * 64;
+// word partials a thread of a pruned request joins (its beam's share of them)
+constexpr int kPruneWords = kPruneWordsHost;
 
 // Distance histogram: 64 exact bins for distances below 64 ulps, then 64
 // sub-bins per octave (monotone in the distance; 1728 bins used).
@@ -1070,7 +1072,11 @@ __device__ __forceinline__ int dist_bin(uint32_t d) {
 // merge of a request split over several blocks.
 // kZSlotBig: kZSlot with the merge-sized key array (one block per CU), for
 // requests so large that small parts would repeat their fixed cost too often.
-enum ZMode { kZToken = 0, kZSlot = 1, kZScore = 2, kZParts = 3, kZSlotBig = 4 };
+// kZPrune: dense rank-indexed rows after the full projection, whose epilogue
+// left each (beam, 32-token word) its legal (max, sum of exp): the request
+// reads only the scores of the K words whose best candidates rank highest
+// (merge-sized key array, so a request of K <= 448 stays in one block).
+enum ZMode { kZToken = 0, kZSlot = 1, kZScore = 2, kZParts = 3, kZSlotBig = 4, kZPrune = 5 };
 
 // Combine two (max, sum of exp(x - max)) partials; lanes that saw nothing hold
 // (-inf, 0).  Symmetric, so both butterfly partners get identical bits.
@@ -1080,6 +1086,38 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
   const float e2 = (m2 == mn) ? 1.f : __expf(m2 - mn);
   s = s * e1 + s2 * e2;
   m = mn;
+}
+
+// Join of two (max, sum of exp) pairs with one exponential: the pair with the
+// larger max keeps its sum, the other's is scaled by exp(-|difference|); two
+// empty pairs (max -inf) give (-inf, 0).
+__device__ __forceinline__ void ms_join(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  const float e = __expf(-fabsf(m - m2));
+  s = (mn == -INFINITY) ? 0.f : ((m >= m2) ? fmaf(s2, e, s) : fmaf(s, e, s2));
+  m = mn;
+}
+
+// N pairs per lane, reduced over lanes by halving: at lane offset O a lane
+// keeps the half of its pairs that its partner does not (the upper half where
+// lane & O is set) and joins its partner's copy of that half.  Offsets run
+// 1, 2, 4, ... (exchanges within a 16-lane row are DPP moves), so after
+// log2(N) stages lane l holds pair rev(l mod N) (its low log2(N) bits
+// reversed), reduced over the lanes that differ from it in those bits.
+template <int N, int O>
+__device__ __forceinline__ void ms_halve(float (&m)[16], float (&s)[16], int l) {
+  if constexpr (N > 1) {
+    const bool hi = (l & O) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float sm = hi ? m[i] : m[i + N / 2], ss = hi ? s[i] : s[i + N / 2];
+      float km = hi ? m[i + N / 2] : m[i], ks = hi ? s[i + N / 2] : s[i];
+      ms_join(km, ks, xor_lane<O>(sm), xor_lane<O>(ss));
+      m[i] = km;
+      s[i] = ks;
+    }
+    ms_halve<N / 2, O * 2>(m, s, l);
+  }
 }
 
 // One block per part of a request, the step after scoring.  A request's
@@ -1128,11 +1166,12 @@ void k_request_step(
     int32_t* __restrict__ token_out, int32_t* __restrict__ row_out, float* __restrict__ cum_out,
     const int32_t* __restrict__ prefix_in, int32_t* __restrict__ prefix_out,
     float* __restrict__ slot_dbg, const float* __restrict__ lse_ext, int32_t ztok,
-    int32_t* __restrict__ err) {
+    const float2* __restrict__ zms, int32_t* __restrict__ err) {
   constexpr int NT = kSelThreads;
   constexpr bool TOKEN_IDX = (MODE == kZToken);
   constexpr bool MERGE = (MODE == kZParts);
-  constexpr int KEYCAP = (MERGE || MODE == kZSlotBig) ? kMergeCap : kKeyCap;
+  constexpr bool PRUNE = (MODE == kZPrune);
+  constexpr int KEYCAP = (MERGE || MODE == kZSlotBig || PRUNE) ? kMergeCap : kKeyCap;
   __shared__ uint64_t keys[KEYCAP];
   // sel (the selection) and dhist (the distance histogram, then the boundary
   // keys) from phase 4 on; before that the log-sum-exp pass keeps its unit
@@ -1201,8 +1240,8 @@ void k_request_step(
   if ((int)threadIdx.x < k_in) cpre[threadIdx.x] = exc;
   // 2. this part's candidates [f0, f1) and the beams they fall on
   //    [bl_lo, bl_hi]: the beams holding f0 and f1 - 1 say so themselves
-  const int f0 = MERGE ? 0 : (int)((int64_t)Cq * part / P);
-  const int f1 = MERGE ? 0 : (int)((int64_t)Cq * (part + 1) / P);
+  int f0 = MERGE ? 0 : (int)((int64_t)Cq * part / P);
+  int f1 = MERGE ? 0 : (int)((int64_t)Cq * (part + 1) / P);
   if (cnt > 0 && exc <= f0 && f0 < exc + cnt) bl_lo_sh = threadIdx.x;
   if (cnt > 0 && exc <= f1 - 1 && f1 - 1 < exc + cnt) bl_hi_sh = threadIdx.x;
   // units of the log-sum-exp pass: SEG candidates from each beam's first,
@@ -1225,7 +1264,7 @@ void k_request_step(
       !TOKEN_IDX && MODE != kZScore && GL == 16 && ((int)S <= kWaveUnit || mean_n >= 256);
   int SEG = wave_units ? kWaveUnit : GL * UL;
   while ((touch + SEG - 1) / SEG + k_in + 1 > kUnitCap) SEG *= 2;
-  if (!MERGE && !zkey) {  // uniform; split single-beam parts reduce only their own range
+  if (!MERGE && !zkey && !PRUNE) {  // uniform; split single-beam parts reduce only their own range
     int Uq;
     const int uex = block_excl_scan<NT>((cnt + SEG - 1) / SEG, sh, &Uq);
     if ((int)threadIdx.x < k_in) upre[threadIdx.x] = uex;
@@ -1314,7 +1353,7 @@ void k_request_step(
   // step needs no long serial walks.  The first round's bitmap words are
   // loaded now so that phase 3 hides their latency.
   const int nbl = bl_hi - bl_lo + 1;  // beams this part touches (0 when C = 0)
-  const bool code_pass = !MERGE && dense && store && !TOKEN_IDX;
+  const bool code_pass = !MERGE && !PRUNE && dense && store && !TOKEN_IDX;
   const int pairs = nbl * tab.words;
   int LPW = 1;
   while (LPW < 32 && pairs * LPW * 2 <= NT) LPW *= 2;
@@ -1331,7 +1370,7 @@ void k_request_step(
     // best candidate of the beam (cand is monotone in z within a beam)
     atomicMax(&omax_sh, ord_of(bcum[b] + (m - l)));
   };
-  if constexpr (!MERGE) {
+  if constexpr (!MERGE && !PRUNE) {
     if ((zkey || (k_in == 1 && P == 1)) && !(TOKEN_IDX && dense)) {
       // this part's own range only, coalesced, with its keys' scores (a
       // single-beam request in one part: its whole row, by every thread)
@@ -1626,6 +1665,139 @@ void k_request_step(
       }
     }
   }
+  if constexpr (PRUNE) {
+    // Word-level pruning.  The full projection's epilogue left zms[beam][w]
+    // = the legal (max, sum of exp) of the 32-token word w of the beam's row.
+    //  a. a beam's log-sum-exp joins its words' partials: G threads per beam,
+    //     each over PW consecutive words in order, then a fixed butterfly
+    //  b. a word's best candidate is cum + (max - lse), the same arithmetic as
+    //     its key below; the word's key takes the word's first code, so words
+    //     order exactly as their best candidates' keys do
+    //  c. the K-th largest word key (radix select): the words at or above it
+    //     hold the request's whole top K, since a candidate in any other word
+    //     lies below K better candidates (the best of each kept word)
+    //  d. the kept words in (beam, word) order, their legal counts and a flat
+    //     prefix; this part takes its share [f0, f1) of that list
+    //  e. and loads those scores only
+    const int NWD = tab.words;
+    int kp2 = 1;
+    while (kp2 < k_in) kp2 <<= 1;
+    const int G = min(64, NT / kp2);
+    const int PW = (NWD + G - 1) / G;  // at most kPruneWords (checked by the host)
+    const int pb = (int)threadIdx.x / G, pg = (int)threadIdx.x - pb * G;
+    const bool plive = pb < k_in && brow[min(pb, k_in - 1)] >= 0;
+    float wmax[kPruneWords];
+    float m = -INFINITY, sm = 0.f;
+    {
+      float2 pq[kPruneWords];
+      const float2* zp = zms + (int64_t)(b0 + min(pb, k_in - 1)) * NWD;
+#pragma unroll
+      for (int u = 0; u < kPruneWords; ++u) {
+        const int w = pg * PW + u;
+        pq[u] = (plive && u < PW && w < NWD) ? zp[w] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kPruneWords; ++u) {
+        wmax[u] = pq[u].x;
+        lse_combine(m, sm, pq[u].x, pq[u].y);
+      }
+    }
+    xor_down_width(G, [&](auto o) {
+      constexpr int X = decltype(o)::value;
+      lse_combine(m, sm, xor_lane<X>(m), xor_lane<X>(sm));
+    });
+    const bool pcand = plive && cpre[pb + 1] > cpre[pb];
+    if (pcand && pg == 0) final_lse(pb, m, sm);
+    __syncthreads();
+    const float pl = pcand ? blse[pb] : 0.f, pc = pcand ? bcum[pb] : 0.f;
+    uint64_t wkey[kPruneWords];  // 0: an empty word
+    int nonempty = 0;
+#pragma unroll
+    for (int u = 0; u < kPruneWords; ++u) {
+      const bool ok = wmax[u] != -INFINITY;  // only real words of live beams
+      wkey[u] = ok ? make_key(pc + (wmax[u] - pl), code_of(pb, (pg * PW + u) << 5)) : 0ull;
+      nonempty += ok ? 1 : 0;
+    }
+    int ne_total;
+    (void)block_excl_scan<NT>(nonempty, sh, &ne_total);
+    const bool keep_all = ne_total <= K;  // uniform
+    RadixSel rs{0, 0, K};
+    if (!keep_all) {
+      for (int shift = 56; shift >= 0; shift -= 8) {
+        if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPruneWords; ++u)
+          if (wkey[u] != 0ull && (wkey[u] & rs.mask) == rs.prefix) atomicAdd(&hist[(wkey[u] >> shift) & 0xFF], 1);
+        __syncthreads();
+        if (radix_narrow<NT>(rs, shift, hist, sh)) break;
+      }
+    }
+    auto kept = [&](uint64_t k) { return k != 0ull && (keep_all || (k & rs.mask) >= rs.prefix); };
+    int nkeep = 0;
+#pragma unroll
+    for (int u = 0; u < kPruneWords; ++u) nkeep += kept(wkey[u]) ? 1 : 0;
+    int NU;
+    int kpos = block_excl_scan<NT>(nkeep, sh, &NU);  // NU <= K: the keys are distinct
+    int* uinfo = reinterpret_cast<int*>(selhist);  // [kMaxK] beam << 16 | word
+    uint32_t* ubits = reinterpret_cast<uint32_t*>(uinfo + kMaxK);
+    int* urank = reinterpret_cast<int*>(ubits + kMaxK);
+    int* ucum = urank + kMaxK;
+#pragma unroll
+    for (int u = 0; u < kPruneWords; ++u)
+      if (kept(wkey[u])) {
+        if (kpos < kMaxK) uinfo[kpos] = (pb << 16) | (pg * PW + u);
+        ++kpos;
+      }
+    NU = min(NU, kMaxK);
+    __syncthreads();
+    int ucnt = 0;
+    if ((int)threadIdx.x < NU) {
+      const int info = uinfo[threadIdx.x];
+      const DWord dw = dense_word<NX>(tab, brow[info >> 16], info & 0xFFFF);
+      ubits[threadIdx.x] = dw.bits;
+      urank[threadIdx.x] = dw.rank;
+      ucnt = __popc(dw.bits);
+    }
+    int Cp;
+    const int uex = block_excl_scan<NT>(ucnt, sh, &Cp);
+    if ((int)threadIdx.x < NU) ucum[threadIdx.x] = uex;
+    f0 = (int)((int64_t)Cp * part / P);
+    f1 = (int)((int64_t)Cp * (part + 1) / P);
+    if (f1 - f0 > KEYCAP) {  // the host sizes P so that this cannot happen
+      if (threadIdx.x == 0) atomicOr(err, 1);
+      f1 = f0 + KEYCAP;
+    }
+    C = f1 - f0;
+    store = true;
+    __syncthreads();
+    // four threads per kept word, eight bit positions each: their eight loads
+    // go out together, clamped to the word's candidates (always in bounds)
+    for (int i2 = threadIdx.x; i2 < NU * 4; i2 += NT) {
+      const int u = i2 >> 2, lo = (i2 & 3) * 8;
+      const int fb = ucum[u];
+      const uint32_t bits = ubits[u];
+      const int nc = __popc(bits);
+      if (fb + nc <= f0 || fb >= f1) continue;
+      const int info = uinfo[u];
+      const int bl = info >> 16, w = info & 0xFFFF;
+      const float* zb = z + (int64_t)(b0 + bl) * ldz + urank[u];
+      const int k0 = __popc(bits & ((1u << lo) - 1u));
+      float zv[8];
+      int kk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kk[i] = k0 + __popc((bits >> lo) & ((1u << i) - 1u));
+        zv[i] = zb[min(kk[i], nc - 1)];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int f = fb + kk[i];
+        if (((bits >> (lo + i)) & 1u) && f >= f0 && f < f1)
+          keys[f - f0] = ((uint64_t)__float_as_uint(zv[i]) << 32) | code_of(bl, (w << 5) + lo + i);
+      }
+    }
+  }
   __syncthreads();
   if (code_pass) {
     // a bit's legal rank is the word's count before it plus the set bits below
@@ -1677,7 +1849,8 @@ void k_request_step(
     for (int b = wave; b < k_in; b += kSelWaves) {
       const int r = brow[b];
       const int n = cpre[b + 1] - cpre[b];
-      const bool mine = MERGE || ((n > 0) ? (cpre[b] >= f0 && cpre[b] < f1) : (b % P == part));
+      const bool mine =
+          MERGE || (PRUNE ? b % P == part : ((n > 0) ? (cpre[b] >= f0 && cpre[b] < f1) : (b % P == part)));
       if (!mine) continue;
       float* dbg = slot_dbg + (int64_t)(b0 + b) * S;
       const float* zb = z + (int64_t)(b0 + b) * ldz;
@@ -2094,7 +2267,8 @@ __global__ __launch_bounds__(gemm_threads(DT, BM)) void k_gemm_nt(const void* __
                                                       float* __restrict__ C, int32_t M, int32_t N,
                                                       int32_t D, int64_t ldc, int32_t compact,
                                                       DevTable tab,
-                                                      const int32_t* __restrict__ row_in) {
+                                                      const int32_t* __restrict__ row_in,
+                                                      float2* __restrict__ zms) {
   constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
   constexpr int TK = kTileKBytes / ES;  // k elements per slice
   constexpr int NT = gemm_threads(DT, BM);
@@ -2346,6 +2520,11 @@ __global__ __launch_bounds__(gemm_threads(DT, BM)) void k_gemm_nt(const void* __
   // 32-bit offset from the lane's first row (rows of the tile differ by a
   // constant times ldc; the compact rows have ldc = V <= 65536, so the
   // offsets stay below 2^31).
+  // With zms, each row also gets the legal (max, sum of exp) of each 32-column
+  // bitmap word: a 32x32 block's 16 rows per lane half are reduced over the
+  // half's 32 lanes (four halving exchanges within 16-lane rows, then one
+  // across them), after which lanes i and i + 16 of the half hold the pair of
+  // row rev(i).
   const int ldc32 = (int)ldc;
   const uint32_t below = (1u << l32) - 1u;
   float* cw = C + (int64_t)(m0 + wm * WM + 4 * half) * ldc;
@@ -2354,12 +2533,25 @@ __global__ __launch_bounds__(gemm_threads(DT, BM)) void k_gemm_nt(const void* __
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
       const int kw = (wn * WN + j * 32) >> 5;  // the block's 32 columns are one bitmap word
+      float pm[16], ps[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int ro = i * 32 + 8 * (v >> 2) + (v & 3);  // row within the lane's rows
         const int2 wr = tword[(wm * WM + 4 * half + ro) * TW + kw];
         const uint32_t x = (uint32_t)wr.x;
-        if ((x >> l32) & 1u) cw[ro * ldc32 + wr.y + (int)__popc(x & below)] = acc[i][j][v];
+        const bool legal = (x >> l32) & 1u;
+        if (legal) cw[ro * ldc32 + wr.y + (int)__popc(x & below)] = acc[i][j][v];
+        pm[v] = legal ? acc[i][j][v] : -INFINITY;
+        ps[v] = legal ? 1.f : 0.f;
+      }
+      if (zms) {  // uniform
+        ms_halve<16, 1>(pm, ps, l32);
+        ms_join(pm[0], ps[0], xor_lane<16>(pm[0]), xor_lane<16>(ps[0]));
+        const int v = ((l32 & 1) << 3) | ((l32 & 2) << 1) | ((l32 & 4) >> 1) | ((l32 & 8) >> 3);
+        const int row = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+        const int wd = (n0 >> 5) + kw;
+        if (l32 < 16 && row < M && wd < tab.words)
+          zms[(int64_t)row * tab.words + wd] = make_float2(pm[0], ps[0]);
       }
     }
 }
@@ -2685,7 +2877,8 @@ hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
 #define ZGR_GEMM(BM_, BN_, SP_)                                                                    \
   hipLaunchKernelGGL((k_gemm_nt<DT, BM_, BN_, NX, SP_>), dim3(GemmOrder(a.M, V, BM_, BN_).blocks()), \
                      dim3(gemm_threads(DT, BM_)), 0, s,                                                          \
-                     a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in)
+                     a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in,                     \
+                     compact == ZGR_EPI_DENSE ? a.zms : nullptr)
   if (g.kernel == ZGR_GEMM_TILED && g.tile_m == 128) {
     if (compact == ZGR_EPI_SLOT)
       ZGR_GEMM(128, 128, true);
@@ -2785,7 +2978,7 @@ hipError_t launch_full_projection(const StepArgs& a, hipStream_t s) {
 #define ZGR_STEP_ARGS                                                                            \
   a.tab, a.t, a.L, a.k_in, a.K, a.row_in, a.cum_in, a.hidden, a.W, a.z, a.ldz, a.parts,            \
       a.part_keys, a.part_cnt, a.part_ms, a.parent_out, a.token_out, a.row_out, a.cum_out, a.prefix_in,       \
-      a.prefix_out, a.slot_dbg, a.lse_ext, (int32_t)a.z_token, a.err
+      a.prefix_out, a.slot_dbg, a.lse_ext, (int32_t)a.z_token, a.zms, a.err
 
 template <int DT, int D>
 hipError_t launch_scored_step(const StepArgs& a, hipStream_t s) {
@@ -2825,6 +3018,14 @@ hipError_t launch_request_step(const StepArgs& a, int zmode, hipStream_t s) {
                          ZGR_STEP_ARGS);
     else
       hipLaunchKernelGGL((k_request_step<kZToken, ZGR_F32, 64, false>), grid, dim3(kSelThreads), 0, s,
+                         ZGR_STEP_ARGS);
+    e = hipGetLastError();
+  } else if (zmode == kZPrune) {
+    if (a.tab.next)
+      hipLaunchKernelGGL((k_request_step<kZPrune, ZGR_F32, 64, true>), grid, dim3(kSelThreads), 0, s,
+                         ZGR_STEP_ARGS);
+    else
+      hipLaunchKernelGGL((k_request_step<kZPrune, ZGR_F32, 64, false>), grid, dim3(kSelThreads), 0, s,
                          ZGR_STEP_ARGS);
     e = hipGetLastError();
   } else if (a.big_parts) {

@@ -65,6 +65,8 @@ GEMM_CASES = [
     ("v2048_t2_unc", "n1e7_v2048", {}, 2, "unconstrained"),
     # the same with the dense steps stored as the int32 next-row matrix
     ("v2048_t2_next", "n1e7_v2048", {"fmt": "NNSS"}, 2, "filter_first"),
+    # 1e7 items, V = 4096: dense step 2 without word pruning (64 words per beam thread group)
+    ("v4096_t2_dense", "n1e7_v4096", {}, 2, "filter_first"),
     # 1e7 items, V = 16384: sparse steps 2-3 by slot; score-first first step
     ("v16384_t3_slot", "n1e7_v16384", {}, 3, "filter_first"),
     ("v16384_t1_sf", "n1e7_v16384", {}, 1, "score_first"),

@@ -115,6 +115,7 @@ def test_plan_and_step_argument_errors():
     assert L.zgr_plan_status(None, None) == zgr.ZGR_E_ARG
     assert L.zgr_plan_set_mode(None, 0) == zgr.ZGR_E_ARG
     assert L.zgr_plan_mode(None, None) == zgr.ZGR_E_ARG
+    assert L.zgr_plan_request_path(None, 1, None, None) == zgr.ZGR_E_ARG
     L.zgr_plan_free(None)
 
 

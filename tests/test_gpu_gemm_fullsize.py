@@ -22,6 +22,12 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 N_CU = 256
 
+# Steps whose request kernel must take the word-pruned path (dense rows after
+# the tiled full projection, many candidates per kept-word bound), and one
+# dense full step that must not (V = 4096: too many words per thread).
+PRUNED = {("v2048_t2_dense", 2), ("v2048_t2_next", 2), ("dense_t2_next", 2), ("dense_t3_slot", 2)}
+NOT_PRUNED = {("v4096_t2_dense", 2)}
+
 
 def log(*a):
     print(*a, flush=True)
@@ -59,10 +65,15 @@ def test_full_projection_at_size(label, name, over, t_last, mode):
         var = zgr.zgr_full_projection_variant(M, cfg.V, cfg.dtype, fmt, mode, N_CU)
         out = gu.run_gpu_step(s, plan, t, prefixes, cum, B, K, list(range(B)), with_dbg=sample,
                               mode=mode)
+        kind, parts = zgr.zgr_plan_request_path(plan, t)
+        if (label, t) in PRUNED:
+            assert kind == zgr.ZGR_REQ_PRUNED, (label, t, kind)
+        if (label, t) in NOT_PRUNED:
+            assert kind == zgr.ZGR_REQ_SLOT, (label, t, kind)
         diag = {}
         amb = gu.check_step(s, t, prefixes, cum, out, B, K, tol, requests=sample, mode=mode,
                             diag=diag)
-        log(f"[{label}] step {t} M={M} kernel {var}: ambiguous {amb}/{len(sample)}, max |dlogp| "
+        log(f"[{label}] step {t} M={M} kernel {var} request {kind}x{parts}: ambiguous {amb}/{len(sample)}, max |dlogp| "
             f"{diag['max_dlogp']:.3g}, max |dscore| {diag['max_dscore']:.3g} (tol {tol:g}); "
             f"tight band {diag['tight_band_max']:.3g}: {diag.get('tight_exact', 0)} exact, "
             f"{diag.get('tight_ambiguous', 0)} ambiguous ({time.time() - t0:.1f}s)")

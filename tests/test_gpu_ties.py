@@ -30,6 +30,10 @@ CASES = {
     "v16_l3_f32": (16, 3, 40, 3, 64, "f32"),
     "v16_l3_bf16": (16, 3, 40, 3, 64, "bf16"),
     "v64_l3_f32": (64, 3, 64, 2, 64, "f32"),
+    # 64 requests of 64 beams over 256 tokens: the dense second step takes the
+    # tiled full projection and its word-pruned selection, where all 512 word
+    # keys of a request tie on the score and the radix select runs to the codes
+    "v256_l2_f32_b64": (256, 2, 64, 64, 64, "f32"),
 }
 
 
@@ -54,6 +58,8 @@ def test_exact_ties_follow_beam_then_slot(name, proj, fmt):
     sc_t = torch.empty(B * K, dtype=torch.float32, device="cuda")
     sid_t = torch.empty(B * K * L, dtype=torch.int32, device="cuda")
     zgr.zgr_decode(plan, s.hidden_source(0), K, item_t, sid_t, sc_t)
+    if name == "v256_l2_f32_b64" and proj == "full" and fmt == "D":
+        assert zgr.zgr_plan_request_path(plan, 2)[0] == zgr.ZGR_REQ_PRUNED
     items = item_t.cpu().numpy().reshape(B, K)
     sids = sid_t.cpu().numpy().reshape(B, K, L)
     scores = sc_t.cpu().numpy().reshape(B, K)
