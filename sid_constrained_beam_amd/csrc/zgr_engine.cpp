@@ -244,7 +244,7 @@ bool light_sparse_step(const zgr_plan* p, const StepArgs& a) {
 constexpr double kSmallRequest = 6144.0;
 constexpr double kPartCandidates = 2048.0;
 constexpr double kPartMaxCandidates = 0.9 * kKeyCapHost;
-constexpr double kPruneGain = 4.0;  // pruning needs this many candidates per kept-word bound
+constexpr double kPruneGain = 2.0;  // pruning needs this many candidates per kept-word bound
 constexpr double kBigPartMaxCandidates = 0.9 * kMergeCapHost;
 int32_t request_parts(const zgr_plan* p, const StepArgs& a, bool* big) {
   *big = false;
@@ -279,9 +279,11 @@ double prune_bound(const StepArgs& a) {
   return 32.0 * (double)std::min<int64_t>(a.K, (int64_t)a.k_in * a.tab.words);
 }
 bool prune_step(const zgr_plan* p, const StepArgs& a) {
-  if (!p->zms || a.plain_z || a.k_in < 2) return false;
+  if (!p->zms || a.plain_z) return false;
   if (a.tab.fmt != ZGR_FMT_DENSE && a.tab.fmt != ZGR_FMT_DENSE_NEXT) return false;
-  if (gemm_variant(a.M, a.tab.V, true, false, a.n_cu).kernel != ZGR_GEMM_TILED) return false;
+  // a single-beam request split over blocks ranks its keys by the score alone
+  // (the merge forms the cumulative scores), which the pruned path does not
+  if (a.k_in == 1 && prune_bound(a) > kMergeCapHost) return false;
   int kp2 = 1;
   while (kp2 < a.k_in) kp2 <<= 1;
   const int G = std::max(1, std::min(64, 1024 / kp2));

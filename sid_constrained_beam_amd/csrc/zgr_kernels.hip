@@ -1104,8 +1104,8 @@ __device__ __forceinline__ void ms_join(float& m, float& s, float m2, float s2) 
 // 1, 2, 4, ... (exchanges within a 16-lane row are DPP moves), so after
 // log2(N) stages lane l holds pair rev(l mod N) (its low log2(N) bits
 // reversed), reduced over the lanes that differ from it in those bits.
-template <int N, int O>
-__device__ __forceinline__ void ms_halve(float (&m)[16], float (&s)[16], int l) {
+template <int A, int N, int O>
+__device__ __forceinline__ void ms_halve(float (&m)[A], float (&s)[A], int l) {
   if constexpr (N > 1) {
     const bool hi = (l & O) != 0;
 #pragma unroll
@@ -1116,7 +1116,7 @@ __device__ __forceinline__ void ms_halve(float (&m)[16], float (&s)[16], int l) 
       m[i] = km;
       s[i] = ks;
     }
-    ms_halve<N / 2, O * 2>(m, s, l);
+    ms_halve<A, N / 2, O * 2>(m, s, l);
   }
 }
 
@@ -1721,16 +1721,41 @@ void k_request_step(
     int ne_total;
     (void)block_excl_scan<NT>(nonempty, sh, &ne_total);
     const bool keep_all = ne_total <= K;  // uniform
+    // radix select, 8 bits per pass from the top, two barriers per pass: the
+    // counts, then wave 0 scans the 256 digits (four per lane, descending),
+    // publishes the digit holding the need-th largest and clears the bins
     RadixSel rs{0, 0, K};
     if (!keep_all) {
+      __shared__ int rp_digit, rp_above, rp_count;
+      if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+      __syncthreads();
       for (int shift = 56; shift >= 0; shift -= 8) {
-        if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-        __syncthreads();
 #pragma unroll
         for (int u = 0; u < kPruneWords; ++u)
           if (wkey[u] != 0ull && (wkey[u] & rs.mask) == rs.prefix) atomicAdd(&hist[(wkey[u] >> shift) & 0xFF], 1);
         __syncthreads();
-        if (radix_narrow<NT>(rs, shift, hist, sh)) break;
+        if (wave == 0) {
+          int c[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
+          const int tot = c[0] + c[1] + c[2] + c[3];
+          int run = wave_incl_scan(tot) - tot;  // digits above this lane's four
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (run < rs.need && run + c[i] >= rs.need) {
+              rp_digit = 255 - 4 * lane - i;
+              rp_above = run;
+              rp_count = c[i];
+            }
+            run += c[i];
+            hist[255 - 4 * lane - i] = 0;
+          }
+        }
+        __syncthreads();
+        rs.prefix |= (uint64_t)rp_digit << shift;
+        rs.mask |= (uint64_t)0xFF << shift;
+        rs.need -= rp_above;
+        if (rp_count == rs.need) break;  // uniform: every key under the prefix is kept
       }
     }
     auto kept = [&](uint64_t k) { return k != 0ull && (keep_all || (k & rs.mask) >= rs.prefix); };
@@ -2545,7 +2570,7 @@ __global__ __launch_bounds__(gemm_threads(DT, BM)) void k_gemm_nt(const void* __
         ps[v] = legal ? 1.f : 0.f;
       }
       if (zms) {  // uniform
-        ms_halve<16, 1>(pm, ps, l32);
+        ms_halve<16, 16, 1>(pm, ps, l32);
         ms_join(pm[0], ps[0], xor_lane<16>(pm[0]), xor_lane<16>(ps[0]));
         const int v = ((l32 & 1) << 3) | ((l32 & 2) << 1) | ((l32 & 4) >> 1) | ((l32 & 8) >> 3);
         const int row = m0 + wm * WM + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
@@ -2574,8 +2599,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(const void* __rest
                                                               float* __restrict__ C, int32_t M,
                                                               int32_t N, int32_t D, int64_t ldc,
                                                               int32_t compact, DevTable tab,
-                                                              const int32_t* __restrict__ row_in) {
+                                                              const int32_t* __restrict__ row_in,
+                                                              float2* __restrict__ zms) {
   __shared__ uint32_t tbits[32];
+  __shared__ float2 wms[2][32];  // zms: each column half's (max, sum of exp) per tile row
   __shared__ int trank[32];
   __shared__ f32x4 part[4][64];
   constexpr int ES = (DT == ZGR_F32) ? 4 : 2;
@@ -2632,11 +2659,42 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(const void* __rest
     trank[threadIdx.x] = pdw.rank;
   }
   __syncthreads();
-  if (ks) return;
-  const f32x4 o = part[tw][lane];
+  if (!ks) {
+    const f32x4 o = part[tw][lane];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) acc[v] += o[v];
+    for (int v = 0; v < 4; ++v) acc[v] += o[v];
+  }
   // 16x16 accumulator layout: lane -> column l16, register v -> row 4*g + v
+  if (zms) {  // uniform: a dense table's compact epilogue
+    // each tile row's legal (max, sum of exp) over the block's 32 columns
+    // (one bitmap word): a wave's 4 rows per lane group are reduced over the
+    // group's 16 lanes (halving over lane offsets 1 and 2, then offsets 4 and
+    // 8, all within a 16-lane row), lanes 0-3 of the group hold row rev(l16),
+    // and the two column halves are joined through LDS in a fixed order
+    if (!ks) {
+      const int bitq = (tw & 1) * 16 + l16;
+      float pm[4], ps[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const bool legal = (tbits[(tw >> 1) * 16 + 4 * g + v] >> bitq) & 1u;
+        pm[v] = legal ? acc[v] : -INFINITY;
+        ps[v] = legal ? 1.f : 0.f;
+      }
+      ms_halve<4, 4, 1>(pm, ps, l16);
+      ms_join(pm[0], ps[0], xor_lane<4>(pm[0]), xor_lane<4>(ps[0]));
+      ms_join(pm[0], ps[0], xor_lane<8>(pm[0]), xor_lane<8>(ps[0]));
+      const int v = ((l16 & 1) << 1) | ((l16 & 2) >> 1);
+      if (l16 < 4) wms[tw & 1][(tw >> 1) * 16 + 4 * g + v] = make_float2(pm[0], ps[0]);
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int row = tm * 32 + threadIdx.x;
+      float m = wms[0][threadIdx.x].x, sm = wms[0][threadIdx.x].y;
+      ms_join(m, sm, wms[1][threadIdx.x].x, wms[1][threadIdx.x].y);
+      if (row < M && tn < tab.words) zms[(int64_t)row * tab.words + tn] = make_float2(m, sm);
+    }
+  }
+  if (ks) return;
   if (!compact) {
     if (n < N) {
 #pragma unroll
@@ -2891,7 +2949,8 @@ hipError_t launch_proj_typed(const StepArgs& a, hipStream_t s) {
       ZGR_GEMM(64, 64, false);
   } else {
     hipLaunchKernelGGL((k_gemm_small<DT, NX>), dim3(((a.M + 31) / 32) * ((V + 31) / 32)), dim3(kSmallThreads), 0, s,
-                       a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in);
+                       a.hidden, a.W, a.z, a.M, V, a.d, a.ldz, compact, a.tab, a.row_in,
+                       compact == ZGR_EPI_DENSE ? a.zms : nullptr);
   }
 #undef ZGR_GEMM
   return hipGetLastError();
