@@ -1364,11 +1364,14 @@ void k_request_step(
   }
 
   // 3. legal-only log-sum-exp of the beams bl_lo..bl_hi over [e0, e1)
+  //    (omax_t: the best candidate of this thread's beams, cand being
+  //    monotone in z within a beam; joined over the block below with one LDS
+  //    atomic per wave, not one per beam on a single address)
+  uint32_t omax_t = 0u;
   auto final_lse = [&](int b, float m, float s) {
     const float l = lse_ext ? lse_ext[b0 + b] : m + __logf(s);
     blse[b] = l;
-    // best candidate of the beam (cand is monotone in z within a beam)
-    atomicMax(&omax_sh, ord_of(bcum[b] + (m - l)));
+    omax_t = max(omax_t, ord_of(bcum[b] + (m - l)));
   };
   if constexpr (!MERGE && !PRUNE) {
     if ((zkey || (k_in == 1 && P == 1)) && !(TOKEN_IDX && dense)) {
@@ -1822,6 +1825,11 @@ void k_request_step(
           keys[f - f0] = ((uint64_t)__float_as_uint(zv[i]) << 32) | code_of(bl, (w << 5) + lo + i);
       }
     }
+  }
+  {
+    uint32_t o = omax_t;
+    xor_down<32>([&](auto d) { o = max(o, xor_lane<decltype(d)::value>(o)); });
+    if (lane == 0 && o != 0u) atomicMax(&omax_sh, o);
   }
   __syncthreads();
   if (code_pass) {
