@@ -1730,35 +1730,64 @@ void k_request_step(
     RadixSel rs{0, 0, K};
     if (!keep_all) {
       __shared__ int rp_digit, rp_above, rp_count;
+      __shared__ uint64_t rp_prefix, rp_mask;
       if (threadIdx.x < 256) hist[threadIdx.x] = 0;
       __syncthreads();
-      for (int shift = 56; shift >= 0; shift -= 8) {
+      auto count = [&](int shift) {
 #pragma unroll
         for (int u = 0; u < kPruneWords; ++u)
           if (wkey[u] != 0ull && (wkey[u] & rs.mask) == rs.prefix) atomicAdd(&hist[(wkey[u] >> shift) & 0xFF], 1);
-        __syncthreads();
-        if (wave == 0) {
-          int c[4];
+      };
+      auto scan = [&]() {  // wave 0
+        int c[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
-          const int tot = c[0] + c[1] + c[2] + c[3];
-          int run = wave_incl_scan(tot) - tot;  // digits above this lane's four
+        for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
+        const int tot = c[0] + c[1] + c[2] + c[3];
+        int run = wave_incl_scan(tot) - tot;  // digits above this lane's four
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (run < rs.need && run + c[i] >= rs.need) {
-              rp_digit = 255 - 4 * lane - i;
-              rp_above = run;
-              rp_count = c[i];
-            }
-            run += c[i];
-            hist[255 - 4 * lane - i] = 0;
+        for (int i = 0; i < 4; ++i) {
+          if (run < rs.need && run + c[i] >= rs.need) {
+            rp_digit = 255 - 4 * lane - i;
+            rp_above = run;
+            rp_count = c[i];
           }
+          run += c[i];
+          hist[255 - 4 * lane - i] = 0;
         }
-        __syncthreads();
+      };
+      auto take = [&](int shift) {
         rs.prefix |= (uint64_t)rp_digit << shift;
         rs.mask |= (uint64_t)0xFF << shift;
         rs.need -= rp_above;
-        if (rp_count == rs.need) break;  // uniform: every key under the prefix is kept
+        return rp_count == rs.need;  // every key under the prefix is kept
+      };
+      if (kp2 * G <= 64) {
+        // every word key lives in wave 0 (a single-beam request): its passes
+        // run there alone, ordered by LDS waits instead of block barriers
+        if (wave == 0) {
+          for (int shift = 56; shift >= 0; shift -= 8) {
+            count(shift);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            scan();
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            if (take(shift)) break;  // uniform over the wave
+          }
+          if (lane == 0) {
+            rp_prefix = rs.prefix;
+            rp_mask = rs.mask;
+          }
+        }
+        __syncthreads();
+        rs.prefix = rp_prefix;
+        rs.mask = rp_mask;
+      } else {
+        for (int shift = 56; shift >= 0; shift -= 8) {
+          count(shift);
+          __syncthreads();
+          if (wave == 0) scan();
+          __syncthreads();
+          if (take(shift)) break;  // uniform
+        }
       }
     }
     auto kept = [&](uint64_t k) { return k != 0ull && (keep_all || (k & rs.mask) >= rs.prefix); };
