@@ -1253,7 +1253,8 @@ void k_request_step(
   // beyond them, so its units are at most that over SEG plus one per beam.
   // Both depend only on the request, so every part reduces a beam the same
   // way.
-  constexpr int UL = 8;
+  // (4 in the part kernels compiled for two blocks per CU: with 8 they spill)
+  constexpr int UL = (MODE == kZSlot || MODE == kZToken) ? 4 : 8;
   const int mean_n = Cq / max(1, k_in);
   const int GL = mean_n >= 64 ? 16 : (mean_n >= 8 ? 4 : 1);
   const int64_t touch = ((int64_t)Cq + P - 1) / P + 2 * (int64_t)S;
